@@ -1,0 +1,24 @@
+"""Exact tiled attention with online softmax for AMD MI355X (gfx950).
+
+The computation lives in libattn.so (hand-written HIP kernels behind the C
+ABI of include/attn.h); this package only loads it and marshals torch tensors
+into its calls.  Build the library with ``python -m exact_attention_66_amd.build``.
+"""
+from ._binding import (  # noqa: F401
+    ATTN_DTYPE_BF16,
+    ATTN_DTYPE_FP16,
+    ATTN_OK,
+    EXPORTED,
+    LIB_PATH,
+    STATUS_NAMES,
+    AttnError,
+    attn_bwd,
+    attn_bwd_workspace_bytes,
+    attn_fwd,
+    attn_last_hip_error,
+    attn_status_string,
+    backward,
+    default_scale,
+    forward,
+    load,
+)

@@ -1,0 +1,126 @@
+// C ABI of the exact-attention library: argument validation (pure host code,
+// no HIP call before every check has passed), then dispatch to the kernels.
+#include "../../include/attn.h"
+
+#include <cmath>
+#include <cstdint>
+#include <limits>
+
+#include "attn_launch.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Byte ranges [p, p+n) overlap?
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return na != 0 && nb != 0 && x < y + nb && y < x + na;
+}
+
+// Element count B*H*N*d, or -1 when any size is < 1 or the byte size of an
+// fp32 [B,H,N,d] array would overflow int64.
+int64_t checked_elems(int64_t B, int64_t H, int64_t N, int64_t d) {
+  if (B < 1 || H < 1 || N < 1 || d < 1) return -1;
+  const int64_t lim = std::numeric_limits<int64_t>::max() / 8;
+  int64_t x = B;
+  for (int64_t f : {H, N, d}) {
+    if (x > lim / f) return -1;
+    x *= f;
+  }
+  return x;
+}
+
+int check_common(int64_t B, int64_t H, int64_t N, int64_t d, float scale, int dtype) {
+  const int64_t elems = checked_elems(B, H, N, d);
+  if (elems < 0) return ATTN_ERR_BAD_SHAPE;
+  // grid sizes: B*H*ceil(N/64) work units must fit the launch limits
+  if (B * H > (int64_t)1 << 24 || N > (int64_t)1 << 24 || B * H * (N / 64) > (int64_t)INT32_MAX) return ATTN_ERR_BAD_SHAPE;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED_HEAD_DIM;
+  if (dtype != ATTN_DTYPE_BF16 && dtype != ATTN_DTYPE_FP16) return ATTN_ERR_BAD_DTYPE;
+  if (N % 64 != 0) return ATTN_ERR_UNSUPPORTED_SEQLEN;
+  if (!std::isfinite(scale) || !(scale > 0.0f)) return ATTN_ERR_BAD_SCALE;
+  return ATTN_OK;
+}
+
+int launch_status(hipError_t e) {
+  if (e == hipSuccess) return ATTN_OK;
+  g_last_hip_error = (int)e;
+  return ATTN_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+             int64_t N, int64_t d, float scale, int causal, int dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL_PTR;
+  int st = check_common(B, H, N, d, scale, dtype);
+  if (st != ATTN_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return ATTN_ERR_MISALIGNED;
+  const size_t tb = (size_t)(B * H * N * d) * 2, lb = (size_t)(B * H * N) * 4;
+  for (const void* in : {q, k, v})
+    if (overlaps(o, tb, in, tb) || overlaps(lse, lb, in, tb)) return ATTN_ERR_ALIASING;
+  if (overlaps(o, tb, lse, lb)) return ATTN_ERR_ALIASING;
+
+  attn::FwdArgs a{q, k, v, o, lse, B, H, N, d, scale, causal != 0, dtype, (hipStream_t)stream};
+  return launch_status(attn::launch_fwd(a));
+}
+
+size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d) {
+  if (checked_elems(B, H, N, d) < 0 || (d != 64 && d != 128)) return 0;
+  return attn::bwd_delta_bytes(B, H, N) + attn::bwd_dqacc_bytes(B, H, N, d);
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
+             void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal,
+             int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv) return ATTN_ERR_NULL_PTR;
+  int st = check_common(B, H, N, d, scale, dtype);
+  if (st != ATTN_OK) return st;
+  const size_t need = attn_bwd_workspace_bytes(B, H, N, d);
+  if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE_TOO_SMALL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dO) || !aligned16(lse) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return ATTN_ERR_MISALIGNED;
+  const size_t tb = (size_t)(B * H * N * d) * 2, lb = (size_t)(B * H * N) * 4;
+  struct R { const void* p; size_t n; };
+  const R ins[] = {{q, tb}, {k, tb}, {v, tb}, {o, tb}, {dO, tb}, {lse, lb}};
+  const R outs[] = {{dq, tb}, {dk, tb}, {dv, tb}, {workspace, need}};
+  for (const R& x : outs) {
+    for (const R& y : ins)
+      if (overlaps(x.p, x.n, y.p, y.n)) return ATTN_ERR_ALIASING;
+    for (const R& y : outs)
+      if (&x != &y && overlaps(x.p, x.n, y.p, y.n)) return ATTN_ERR_ALIASING;
+  }
+
+  char* ws = (char*)workspace;
+  attn::BwdArgs a{q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal != 0, dtype,
+                  (float*)ws, (float*)(ws + attn::bwd_delta_bytes(B, H, N)), (hipStream_t)stream};
+  return launch_status(attn::launch_bwd(a));
+}
+
+const char* attn_status_string(int status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_NULL_PTR: return "a required pointer is NULL";
+    case ATTN_ERR_BAD_SHAPE: return "B, H and N must be >= 1 and the sizes must not overflow";
+    case ATTN_ERR_UNSUPPORTED_HEAD_DIM: return "head dimension d must be 64 or 128";
+    case ATTN_ERR_BAD_DTYPE: return "dtype must be ATTN_DTYPE_BF16 (0) or ATTN_DTYPE_FP16 (1)";
+    case ATTN_ERR_MISALIGNED: return "pointers must be 16-byte aligned (workspace 256-byte aligned)";
+    case ATTN_ERR_UNSUPPORTED_SEQLEN: return "sequence length N must be a multiple of 64";
+    case ATTN_ERR_BAD_SCALE: return "scale must be finite and > 0";
+    case ATTN_ERR_WORKSPACE_TOO_SMALL: return "workspace is NULL or smaller than attn_bwd_workspace_bytes()";
+    case ATTN_ERR_ALIASING: return "an output overlaps an input or another output";
+    case ATTN_ERR_HIP: return "a HIP kernel launch failed (see attn_last_hip_error())";
+    default: return "unknown status";
+  }
+}
+
+int attn_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

@@ -1,0 +1,117 @@
+// Device-side building blocks shared by the forward and backward kernels:
+// 16-bit element traits, gfx950 MFMA wrappers, LDS transpose reads and
+// cross-half wavefront exchange.
+//
+// MFMA operand layouts used throughout (wave64; h = lane / 32, r = lane % 32),
+// checked on gfx950 with an in-bounds lane probe:
+//   v_mfma_f32_32x32x16_{bf16,f16}:  D[32x32] += A[32x16] * B[16x32]
+//     A: lane holds A[r][8h + i],  i = 0..7
+//     B: lane holds B[8h + i][r],  i = 0..7
+//     D: lane holds D[8*(j/4) + 4h + j%4][r],  j = 0..15
+// Because the reduction index enters A and B the same way, any fixed
+// relabelling of the 16 reduction slots is harmless as long as both operands
+// use it; the kernels relabel keys so that a score accumulator can be fed
+// back as an operand without moving data (see slot_key()).
+//
+// ds_read_b64_tr_b16 (gfx950): within each group of 16 lanes, lane j supplies
+// the address of 4 consecutive 16-bit elements; lanes 4s..4s+3 together form
+// row s (lane 4s+t gives columns 4t..4t+3) of a 4x16 block, and lane i
+// receives column i of that block (4 elements, one per row).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define ATTN_LDS __attribute__((address_space(3)))
+
+struct bf16_t {
+  typedef __bf16 T;
+  typedef __bf16 v8 __attribute__((ext_vector_type(8)));
+  typedef __bf16 v4 __attribute__((ext_vector_type(4)));
+  typedef __bf16 v2 __attribute__((ext_vector_type(2)));
+  static __device__ __forceinline__ f32x16 mfma32(v8 a, v8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ v4 tr_read(const T* lds_ptr) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((ATTN_LDS v4*)(lds_ptr));
+  }
+  static __device__ __forceinline__ float dot2(v2 a, v2 b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);
+  }
+};
+
+struct f16_t {
+  typedef _Float16 T;
+  typedef _Float16 v8 __attribute__((ext_vector_type(8)));
+  typedef _Float16 v4 __attribute__((ext_vector_type(4)));
+  typedef _Float16 v2 __attribute__((ext_vector_type(2)));
+  static __device__ __forceinline__ f32x16 mfma32(v8 a, v8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  typedef __fp16 raw4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
+  static __device__ __forceinline__ v4 tr_read(const T* lds_ptr) {
+    return __builtin_bit_cast(v4, __builtin_amdgcn_ds_read_tr16_b64_v4f16((ATTN_LDS raw4*)(lds_ptr)));
+  }
+  static __device__ __forceinline__ float dot2(v2 a, v2 b, float c) { return __builtin_amdgcn_fdot2(a, b, c, false); }
+};
+
+// Row of a 32x32 accumulator held in slot j by a lane of half h.
+__device__ __forceinline__ constexpr int acc_row(int j, int h) { return 8 * (j / 4) + 4 * h + (j % 4); }
+
+// Reduction slot relabelling: slot i (0..7) of a lane in half h inside one
+// 16-wide reduction step carries key/row 8*(i/4) + 4h + i%4 of that step.
+// This is exactly the set of rows a 32x32 accumulator keeps in slots
+// 8*kk + i, so accumulator slots 8kk..8kk+7 form the B (or A) operand of
+// reduction step kk with no data movement.
+__device__ __forceinline__ constexpr int slot_key(int i, int h) { return 8 * (i / 4) + 4 * h + (i % 4); }
+
+// max / sum of a value across the two 32-lane halves (lane l and l ^ 32).
+__device__ __forceinline__ float xhalf_max(float x) {
+  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// 8 fp32 -> 8 16-bit values (round to nearest even) packed as an MFMA operand.
+template <typename E>
+__device__ __forceinline__ typename E::v8 pack8(float a0, float a1, float a2, float a3,
+                                                float a4, float a5, float a6, float a7) {
+  typename E::v8 r;
+  r[0] = (typename E::T)a0; r[1] = (typename E::T)a1; r[2] = (typename E::T)a2; r[3] = (typename E::T)a3;
+  r[4] = (typename E::T)a4; r[5] = (typename E::T)a5; r[6] = (typename E::T)a6; r[7] = (typename E::T)a7;
+  return r;
+}
+
+// acc + sum of the 8 packed 16-bit values (exact products by 1.0, fp32 sums).
+template <typename E>
+__device__ __forceinline__ float sum8(typename E::v8 x, float acc) {
+  const typename E::v2 one = {(typename E::T)1.0f, (typename E::T)1.0f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const typename E::v2 pr = {x[2 * i], x[2 * i + 1]};
+    acc = E::dot2(pr, one, acc);
+  }
+  return acc;
+}
+
+template <typename E>
+__device__ __forceinline__ typename E::v8 concat44(typename E::v4 lo, typename E::v4 hi) {
+  typename E::v8 r;
+  r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+  r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+  return r;
+}
+
+}  // namespace attn

@@ -1,0 +1,289 @@
+// Forward pass of exact attention on gfx950: one workgroup per
+// (batch*head, block of BM queries), K/V tiles staged through LDS,
+// scores and P V on MFMA, online softmax in registers.
+//
+// Method: page "突破单卡显存极限：FlashAttention-2技术解析与实战指南" §2.1
+// (blockwise softmax with a running row max m and denominator l, rescaled by
+// exp(m_old - m_new)); page "FlashAttention-2：GPU利用率从50%干到90%"
+// improvements 1-3 (grid over batch x head x query block, most work kept on
+// the matrix units with the normalisation deferred to the end, each
+// wavefront owning its own query rows so waves never exchange softmax state).
+//
+// gfx950 mapping (not the pages' A100 tiling):
+//  * each wave owns 32*QB queries and computes S^T = K Q^T with
+//    v_mfma_f32_32x32x16, so a lane holds one query's scores for 16 keys per
+//    32-key block: the row max is in-lane plus one permlane32 swap, and the
+//    row sum needs no exchange until the epilogue;
+//  * the S^T accumulator, converted to 16-bit, is directly the B operand of
+//    O^T += V^T P^T (keys relabelled per slot_key), and V^T comes from LDS
+//    with ds_read_b64_tr_b16, so P never leaves registers;
+//  * K/V tiles are double-buffered in LDS, the next tile's global loads are
+//    issued before the current tile's math;
+//  * exponentials use exp2 with scale*log2(e) folded into one FMA, and the
+//    O rescale is skipped while the running max grows by less than 2^8
+//    (exact: the same stale max is used for O, l and lse);
+//  * causal launches order work units heaviest query block first.
+#include "attn_device.h"
+#include "attn_launch.h"
+
+namespace attn {
+
+namespace {
+
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kLog2e = 1.44269504088896340736f;
+// Rescale O only when the running max grows by more than this (log2 units).
+constexpr float kRescaleSlack = 8.0f;
+
+template <typename E, int D, bool CAUSAL, int QB, int NW, int BN>
+__global__ __launch_bounds__(NW * 64) void fwd_kernel(const typename E::T* __restrict__ Q,
+                                                      const typename E::T* __restrict__ K,
+                                                      const typename E::T* __restrict__ V,
+                                                      typename E::T* __restrict__ O,
+                                                      float* __restrict__ LSE, int BH, int N, int nqb,
+                                                      float scale_log2) {
+  using T = typename E::T;
+  using v8 = typename E::v8;
+  using v4 = typename E::v4;
+  constexpr int BM = NW * 32 * QB;   // queries per workgroup
+  constexpr int KS = D / 16;         // reduction steps over d for S
+  constexpr int DB = D / 32;         // 32-wide d blocks of O^T
+  constexpr int KB = BN / 32;        // 32-key blocks per tile
+  constexpr int LD = D + 8;          // padded LDS row, in elements
+  constexpr int NT = NW * 64;
+  constexpr int CPT = BN * D / 8 / NT;  // 16-byte chunks per thread per tensor
+  static_assert(CPT >= 1 && (BN * D / 8) % NT == 0, "tile must split evenly over threads");
+
+  __shared__ __attribute__((aligned(16))) T lds_k[2][BN * LD];
+  __shared__ __attribute__((aligned(16))) T lds_v[2][BN * LD];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int h = lane >> 5;
+  const int r = lane & 31;
+
+  int qblk, bh;
+  if (CAUSAL) {  // heaviest query blocks first, across all heads
+    qblk = nqb - 1 - (int)(blockIdx.x / BH);
+    bh = (int)(blockIdx.x % BH);
+  } else {
+    bh = (int)(blockIdx.x / nqb);
+    qblk = (int)(blockIdx.x % nqb);
+  }
+  const int q0 = qblk * BM;
+  const int qw0 = q0 + w * 32 * QB;
+  const bool wave_valid = qw0 < N;
+  const size_t head = (size_t)bh * (size_t)N * D;
+  const T* Qh = Q + head;
+  const T* Kh = K + head;
+  const T* Vh = V + head;
+
+  // Q fragments, B operand of S^T = K Q^T: lane holds Q[q = qw0+32qb+r][16ks + 8h .. +7].
+  v8 qf[QB][KS];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int q = min(qw0 + qb * 32 + r, N - 1);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[qb][ks] = *(const v8*)(Qh + (size_t)q * D + ks * 16 + 8 * h);
+  }
+
+  f32x16 oacc[QB][DB];
+  // m_run: running max (log2 units, may trail the true max by < kRescaleSlack);
+  // l_run: sum of the fp32 exponentials (gives lse); lr_run: sum of the same
+  // exponentials after rounding to 16 bits, i.e. of the weights the P V
+  // product really used, so that O is normalised by exactly its own weights.
+  float m_run[QB], l_run[QB], lr_run[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m_run[qb] = -__builtin_inff();
+    l_run[qb] = 0.f;
+    lr_run[qb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) oacc[qb][db] = f32x16{};
+  }
+
+  const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
+  const int ntiles = (kv_end + BN - 1) / BN;
+  const int q_last = qw0 + 32 * QB - 1;
+
+  v8 kreg[CPT], vreg[CPT];
+  auto gload = [&](int t) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int idx = tid + c * NT;
+      const int row = idx / (D / 8);
+      const int col = (idx % (D / 8)) * 8;
+      const int key = min(t * BN + row, N - 1);
+      kreg[c] = *(const v8*)(Kh + (size_t)key * D + col);
+      vreg[c] = *(const v8*)(Vh + (size_t)key * D + col);
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int idx = tid + c * NT;
+      const int row = idx / (D / 8);
+      const int col = (idx % (D / 8)) * 8;
+      *(v8*)(&lds_k[buf][row * LD + col]) = kreg[c];
+      *(v8*)(&lds_v[buf][row * LD + col]) = vreg[c];
+    }
+  };
+
+  gload(0);
+  lstore(0);
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < ntiles) gload(t + 1);
+    const int k0 = t * BN;
+    const bool active = wave_valid && (!CAUSAL || k0 <= q_last);
+    if (active) {
+      const T* kl = lds_k[buf];
+      const T* vl = lds_v[buf];
+      // ---- S^T = K Q^T
+      f32x16 s[KB][QB];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) s[kb][qb] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          const v8 kf = *(const v8*)(kl + (kb * 32 + r) * LD + ks * 16 + 8 * h);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) s[kb][qb] = E::mfma32(kf, qf[qb][ks], s[kb][qb]);
+        }
+      }
+      // ---- causal mask (key > query -> -inf) on tiles that reach past the wave's first query
+      if (CAUSAL && k0 + BN - 1 > qw0) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+              const int key = k0 + kb * 32 + acc_row(j, h);
+              const int q = qw0 + qb * 32 + r;
+              if (key > q) s[kb][qb][j] = -__builtin_inff();
+            }
+      }
+      // ---- online softmax (log2 domain); P is rounded to 16 bits here and
+      // kept packed as the B operand of the P V product
+      v8 pf[KB][2][QB];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        float mx = -__builtin_inff();
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[kb][qb][j]);
+        mx = xhalf_max(mx);
+        const float mt = mx * scale_log2;
+        const bool need = mt > m_run[qb] + kRescaleSlack;
+        if (__builtin_amdgcn_ballot_w64(need) != 0) {
+          const float mn = fmaxf(m_run[qb], mt);
+          const float alpha = fast_exp2(m_run[qb] - mn);
+          l_run[qb] *= alpha;
+          lr_run[qb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) oacc[qb][db] *= alpha;
+          m_run[qb] = mn;
+        }
+        const float neg_m = -m_run[qb];
+        float ls = 0.f, lr = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk) {
+            float p[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              p[i] = fast_exp2(fmaf(s[kb][qb][8 * kk + i], scale_log2, neg_m));
+              ls += p[i];
+            }
+            pf[kb][kk][qb] = pack8<E>(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
+            lr = sum8<E>(pf[kb][kk][qb], lr);
+          }
+        l_run[qb] += ls;
+        lr_run[qb] += lr;
+      }
+      // ---- O^T += V^T P^T
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const int vrow = kb * 32 + kk * 16 + 4 * h + ((lane & 15) >> 2);
+          const int vcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const v4 lo = E::tr_read(vl + vrow * LD + db * 32 + vcol);
+            const v4 hi = E::tr_read(vl + (vrow + 8) * LD + db * 32 + vcol);
+            const v8 vf = concat44<E>(lo, hi);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = E::mfma32(vf, pf[kb][kk][qb], oacc[qb][db]);
+          }
+        }
+      }
+    }
+    if (t + 1 < ntiles) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (!wave_valid) return;
+  // ---- epilogue: O = acc / l, lse = (m + log2 l) ln 2
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const float l = xhalf_sum(l_run[qb]);
+    const float inv = 1.0f / xhalf_sum(lr_run[qb]);
+    const int q = qw0 + qb * 32 + r;
+    T* orow = O + head + (size_t)q * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int jg = 0; jg < 4; ++jg) {
+        v4 ov;
+        ov[0] = (T)(oacc[qb][db][4 * jg + 0] * inv);
+        ov[1] = (T)(oacc[qb][db][4 * jg + 1] * inv);
+        ov[2] = (T)(oacc[qb][db][4 * jg + 2] * inv);
+        ov[3] = (T)(oacc[qb][db][4 * jg + 3] * inv);
+        *(v4*)(orow + db * 32 + 8 * jg + 4 * h) = ov;
+      }
+    if (h == 0) LSE[(size_t)bh * N + q] = (m_run[qb] + __builtin_amdgcn_logf(l)) * kLn2;
+  }
+}
+
+template <typename E, int D, bool CAUSAL, int QB, int NW, int BN>
+hipError_t launch_fwd_cfg(const FwdArgs& a) {
+  constexpr int BM = NW * 32 * QB;
+  const int BH = (int)(a.B * a.H);
+  const int N = (int)a.N;
+  const int nqb = (N + BM - 1) / BM;
+  dim3 grid((unsigned)(nqb * BH)), block(NW * 64);
+  const float scale_log2 = a.scale * kLog2e;
+  const typename E::T* q = (const typename E::T*)a.q;
+  const typename E::T* k = (const typename E::T*)a.k;
+  const typename E::T* v = (const typename E::T*)a.v;
+  typename E::T* o = (typename E::T*)a.o;
+  float* lse = a.lse;
+  void* args[] = {(void*)&q, (void*)&k, (void*)&v, (void*)&o, (void*)&lse,
+                  (void*)&BH, (void*)&N, (void*)&nqb, (void*)&scale_log2};
+  return hipLaunchKernel((const void*)fwd_kernel<E, D, CAUSAL, QB, NW, BN>, grid, block, args, 0, a.stream);
+}
+
+template <typename E, int D>
+hipError_t launch_fwd_d(const FwdArgs& a) {
+  if (a.causal) return launch_fwd_cfg<E, D, true, 1, 4, 64>(a);
+  return launch_fwd_cfg<E, D, false, 1, 4, 64>(a);
+}
+
+}  // namespace
+
+hipError_t launch_fwd(const FwdArgs& a) {
+  if (a.dtype == 0) return a.d == 64 ? launch_fwd_d<bf16_t, 64>(a) : launch_fwd_d<bf16_t, 128>(a);
+  return a.d == 64 ? launch_fwd_d<f16_t, 64>(a) : launch_fwd_d<f16_t, 128>(a);
+}
+
+}  // namespace attn

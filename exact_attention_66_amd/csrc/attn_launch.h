@@ -1,0 +1,52 @@
+// Internal launch interface between the C ABI (attn_api.cpp) and the kernel
+// translation units.  Arguments are already validated when these run.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace attn {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int64_t B, H, N, d;
+  float scale;
+  bool causal;
+  int dtype;  // 0 bf16, 1 fp16
+  hipStream_t stream;
+};
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dO;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  int64_t B, H, N, d;
+  float scale;
+  bool causal;
+  int dtype;
+  float* delta;   // [B,H,N] fp32 scratch: D_i = dO_i . O_i
+  float* dq_acc;  // [B,H,N,d] fp32 scratch: dQ accumulator
+  hipStream_t stream;
+};
+
+hipError_t launch_fwd(const FwdArgs& a);
+hipError_t launch_bwd(const BwdArgs& a);
+
+// Workspace split used by attn_bwd: delta first, then the dQ accumulator,
+// each starting on a 256-byte boundary.
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+inline size_t bwd_delta_bytes(int64_t B, int64_t H, int64_t N) { return align256((size_t)(B * H * N) * 4); }
+inline size_t bwd_dqacc_bytes(int64_t B, int64_t H, int64_t N, int64_t d) { return align256((size_t)(B * H * N * d) * 4); }
+
+}  // namespace attn

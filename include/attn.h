@@ -1,0 +1,124 @@
+/*
+ * attn.h - C ABI of the exact-attention library for AMD MI355X (gfx950).
+ *
+ * Exact scaled-dot-product attention, forward and backward, computed in
+ * tiles with an online softmax so that the N x N score matrix never reaches
+ * device memory.
+ *
+ *   Forward  O = softmax(scale * Q K^T  [causal mask]) V,  lse = per-row log-sum-exp.
+ *   Backward dQ, dK, dV from Q, K, V, O, dO and lse, recomputing the scores.
+ *
+ * The operation is the attention of page "FlashAttention技术解析 如何让GPT训练
+ * 速度提升5-9倍" §2.1 (plain softmax(QK^T / sqrt(d_k)) V, and the tiled form
+ * that never stores the score matrix), with the softmax_scale and causal
+ * arguments of page "Flash Attention V2 大模型时代的算力救星" §4.2; the
+ * blockwise softmax follows page "突破单卡显存极限：FlashAttention-2技术解析与
+ * 实战指南" §2.1, and the backward pass keeps only the softmax normalisation
+ * statistic and recomputes the scores (page "Flash Attention V2 …" §3.2).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Layout:    Q, K, V, O, dO, dQ, dK, dV are contiguous [B, H, N, d] arrays of
+ *            16-bit floats (dtype ATTN_DTYPE_BF16 or ATTN_DTYPE_FP16);
+ *            lse is a contiguous [B, H, N] array of fp32 holding natural-log
+ *            m + ln(sum exp(s - m)) per query row.
+ * Causal:    nonzero = query i sees keys j <= i (top-left, diagonal kept).
+ * Scale:     fp32 multiplier of Q K^T; must be finite and > 0
+ *            (1/sqrt(d) is the usual value).
+ * Pointers:  device pointers (hipMalloc / torch CUDA tensors) on the current
+ *            device, each 16-byte aligned.  The caller owns all memory; the
+ *            library allocates nothing and keeps no state between calls.
+ * Sizes:     B, H, N >= 1; d in {64, 128}; N a multiple of 64.
+ * Streams:   work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *            stream) and the call returns without synchronising.
+ * Errors:    every check runs before any HIP call; on a nonzero return no
+ *            output has been written and nothing has been enqueued.  Faults
+ *            inside a kernel surface at the caller's next synchronisation.
+ * Threads:   calls are re-entrant; calls on different streams may overlap.
+ */
+#ifndef EXACT_ATTENTION_ATTN_H
+#define EXACT_ATTENTION_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum attn_dtype {
+  ATTN_DTYPE_BF16 = 0,
+  ATTN_DTYPE_FP16 = 1,
+};
+
+enum attn_status {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL_PTR = 1,              /* a required pointer is NULL */
+  ATTN_ERR_BAD_SHAPE = 2,             /* B, H or N < 1, or the sizes overflow int64 */
+  ATTN_ERR_UNSUPPORTED_HEAD_DIM = 3,  /* d not in {64, 128} */
+  ATTN_ERR_BAD_DTYPE = 4,             /* dtype not an attn_dtype value */
+  ATTN_ERR_MISALIGNED = 5,            /* a pointer is not 16-byte aligned */
+  ATTN_ERR_UNSUPPORTED_SEQLEN = 6,    /* N not a multiple of 64 */
+  ATTN_ERR_BAD_SCALE = 7,             /* scale NaN, infinite or <= 0 */
+  ATTN_ERR_WORKSPACE_TOO_SMALL = 8,   /* workspace NULL or below attn_bwd_workspace_bytes() */
+  ATTN_ERR_ALIASING = 9,              /* an output overlaps an input or another output */
+  ATTN_ERR_HIP = 10,                  /* a kernel launch failed; see attn_last_hip_error() */
+};
+
+/*
+ * attn_fwd - forward pass.
+ *   q, k, v  [B,H,N,d] inputs (read only).
+ *   o        [B,H,N,d] output, same dtype: softmax(scale Q K^T) V, rounded to
+ *            nearest-even from fp32.
+ *   lse      [B,H,N] fp32 output: natural-log log-sum-exp of each row of the
+ *            (masked, scaled) scores; the only statistic the backward needs.
+ * o and lse must not overlap q, k, v or each other.
+ * Returns ATTN_OK or an attn_status error code.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal,
+             int dtype, void* stream);
+
+/*
+ * attn_bwd_workspace_bytes - size of the scratch buffer attn_bwd needs:
+ * one fp32 per query row (D_i = dO_i . O_i) plus an fp32 [B,H,N,d] dQ
+ * accumulator, rounded up to 256 bytes.  It grows as O(B*H*N*d), never with
+ * N^2 (the memory bound of page "突破单卡显存极限…" §2.2).  Returns 0 when the
+ * sizes are invalid (B, H, N < 1, d not in {64,128}, or overflow).
+ */
+size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d);
+
+/*
+ * attn_bwd - backward pass for the loss gradient dO = dL/dO.
+ *   q, k, v, o, lse  exactly the inputs and outputs of the matching attn_fwd
+ *                    call (same scale, causal and dtype).
+ *   dO       [B,H,N,d] upstream gradient.
+ *   dq, dk, dv [B,H,N,d] outputs (dtype), rounded to nearest-even.
+ *   workspace  device buffer of at least attn_bwd_workspace_bytes(B,H,N,d)
+ *              bytes, 256-byte aligned; overwritten, contents undefined
+ *              afterwards.  Concurrent calls need distinct workspaces.
+ * dq, dk, dv and workspace must not overlap any input or each other.
+ * dK and dV are accumulated per key block without atomics and are bitwise
+ * reproducible; dQ is summed across key blocks with fp32 atomics, so its last
+ * bits may vary from run to run.
+ * Returns ATTN_OK or an attn_status error code.
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o,
+             const void* dO, const float* lse, void* dq, void* dk, void* dv,
+             int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal,
+             int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/* attn_status_string - static, NUL-terminated description of a status code. */
+const char* attn_status_string(int status);
+
+/*
+ * attn_last_hip_error - the hipError_t value of the most recent failed launch
+ * on the calling thread (0 if none), valid after ATTN_ERR_HIP.
+ */
+int attn_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXACT_ATTENTION_ATTN_H */

@@ -1,0 +1,112 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/attn.h declares, and rejects bad arguments before any HIP call.
+
+All calls here carry arguments that fail validation, so no kernel is ever
+launched; the pointers are fake, 16-byte-aligned host integers.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_attention_66_amd as ea
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+OK, NULL, SHAPE, HEADDIM, DTYPE, ALIGN, SEQ, SCALE, WS, ALIAS = 0, 1, 2, 3, 4, 5, 6, 7, 8, 9
+
+# fake device pointers, far apart so that tensors of the sizes used never overlap
+P = [0x10000000 * (i + 1) for i in range(12)]
+
+
+def _declared_functions():
+    with open(HEADER) as f:
+        text = f.read()
+    return re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(attn_\w+)\s*\(", text, flags=re.M)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return ea.load()
+
+
+def test_library_exports_every_declared_function(lib):
+    names = _declared_functions()
+    assert set(names) == set(ea.EXPORTED), names
+    for n in names:
+        assert hasattr(lib, n), n
+        assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
+
+
+def test_status_strings(lib):
+    for code, name in ea.STATUS_NAMES.items():
+        s = ea.attn_status_string(code)
+        assert s and s != "unknown status", (code, name)
+    assert ea.attn_status_string(12345) == "unknown status"
+    assert ea.attn_last_hip_error() == 0
+
+
+def test_workspace_bytes():
+    # delta [B,H,N] fp32 + dQ accumulator [B,H,N,d] fp32, each padded to 256 bytes
+    assert ea.attn_bwd_workspace_bytes(1, 1, 64, 64) == 256 + 64 * 64 * 4
+    assert ea.attn_bwd_workspace_bytes(4, 32, 4096, 128) == 4 * 32 * 4096 * 4 + 4 * 32 * 4096 * 128 * 4
+    n = 32768
+    assert ea.attn_bwd_workspace_bytes(1, 16, n, 128) < 16 * n * 130 * 4 + 512  # O(N d), never N^2
+    for bad in [(0, 1, 64, 64), (1, 0, 64, 64), (1, 1, 0, 64), (1, 1, 64, 96), (1, 1, 64, -1),
+                (1 << 40, 1 << 20, 1 << 20, 128)]:
+        assert ea.attn_bwd_workspace_bytes(*bad) == 0, bad
+
+
+def fwd(lib, q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=1, H=2, N=128, d=64, scale=0.125, causal=1, dtype=0):
+    return lib.attn_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, None)
+
+
+def bwd(lib, q=P[0], k=P[1], v=P[2], o=P[3], dO=P[4], lse=P[5], dq=P[6], dk=P[7], dv=P[8], B=1, H=2, N=128,
+        d=64, scale=0.125, causal=1, dtype=0, ws=P[9], ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = lib.attn_bwd_workspace_bytes(B, H, N, d) if d in (64, 128) and min(B, H, N) > 0 else 1 << 20
+    return lib.attn_bwd(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal, dtype, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "o", "lse"])
+def test_fwd_null(lib, which):
+    assert fwd(lib, **{which: None}) == NULL
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), SHAPE), (dict(H=-1), SHAPE), (dict(N=0), SHAPE), (dict(B=1 << 40, H=1 << 20), SHAPE),
+    (dict(d=96), HEADDIM), (dict(d=256), HEADDIM), (dict(d=32), HEADDIM),
+    (dict(dtype=2), DTYPE), (dict(dtype=-1), DTYPE),
+    (dict(N=100), SEQ), (dict(N=65), SEQ),
+    (dict(scale=float("nan")), SCALE), (dict(scale=float("inf")), SCALE), (dict(scale=0.0), SCALE),
+    (dict(scale=-0.1), SCALE),
+    (dict(q=P[0] + 8), ALIGN), (dict(lse=P[4] + 4), ALIGN), (dict(o=P[3] + 2), ALIGN),
+    (dict(o=P[0]), ALIAS), (dict(lse=P[1] + 64), ALIAS), (dict(lse=P[3] + 16), ALIAS),
+])
+def test_fwd_rejects(lib, kw, code):
+    assert fwd(lib, **kw) == code
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "o", "dO", "lse", "dq", "dk", "dv"])
+def test_bwd_null(lib, which):
+    assert bwd(lib, **{which: None}) == NULL
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), SHAPE), (dict(d=80), HEADDIM), (dict(dtype=7), DTYPE), (dict(N=96), SEQ),
+    (dict(scale=float("-inf")), SCALE),
+    (dict(ws=None), WS), (dict(ws_bytes=100), WS),
+    (dict(dq=P[6] + 8), ALIGN), (dict(ws=P[9] + 16), ALIGN),
+    (dict(dq=P[0]), ALIAS), (dict(dk=P[6]), ALIAS), (dict(ws=P[8]), ALIAS), (dict(dv=P[5]), ALIAS),
+])
+def test_bwd_rejects(lib, kw, code):
+    assert bwd(lib, **kw) == code
+
+
+def test_python_binding_rejects_noncontiguous():
+    import torch
+    q = torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16).transpose(2, 3)
+    with pytest.raises(ValueError):
+        ea._binding._ptr(q)
