@@ -1,0 +1,144 @@
+"""Backward parity of the HIP kernels against the fp64 oracle (runs on the GPU).
+
+The GPU forward output (O, lse) feeds the GPU backward exactly as in
+training; the oracle computes its gradients from the same rounded inputs.
+Small shapes are compared over every head; the full workload sizes over
+whole sampled heads (the oracle evaluates one head at a time), plus
+invariants that hold at any size on every head.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from parity import GRAD_REL_FRO, check_grad, f64, log, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(ea, x, scale, causal):
+    q, k, v, do = (x[n].cuda() for n in ("q", "k", "v", "do"))
+    o, lse = ea.forward(q, k, v, scale=scale, causal=causal)
+    dq, dk, dv = ea.backward(q, k, v, o, lse, do, scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    return (q, k, v, do, o, lse), (dq, dk, dv)
+
+
+SMALL = [
+    (1, 2, 64, 64, "bf16", False),
+    (1, 2, 64, 128, "bf16", True),
+    (2, 3, 192, 64, "bf16", True),       # key blocks of 128 with a ragged last block
+    (1, 2, 320, 128, "bf16", True),
+    (1, 2, 320, 64, "fp16", False),
+    (2, 2, 512, 128, "fp16", True),
+    (1, 1, 1024, 128, "bf16", False),
+    (1, 2, 1088, 64, "fp16", True),
+]
+
+
+@pytest.mark.parametrize("B,H,N,d,dt,causal", SMALL)
+def test_backward_small_all_elements(B, H, N, d, dt, causal):
+    ea = require_gpu()
+    w = workloads.Workload("small", B, H, N, d, dt, causal, True, seed=9000 + N + d + 10 * B + H)
+    log(f"backward small {w}")
+    x = workloads.make_inputs(w)
+    _, grads = _run(ea, x, w.scale, causal)
+    ref = oracle.backward(*(workloads.to_f64_numpy(x[n]) for n in ("q", "k", "v", "do")), w.scale, causal)
+    for name, g, gr in zip(("dQ", "dK", "dV"), grads, ref):
+        check_grad(f64(g), gr, name)
+
+
+def _invariants(dk, dv, do, what):
+    """Rows of dS sum to 0, so sum_j dK_j = 0; rows of P sum to 1, so
+    sum_j dV_j = sum_i dO_i.  Checked per head, relative to the head's
+    Frobenius norm (each of the N summed values carries its own rounding)."""
+    sk = dk.double().sum(dim=2).norm(dim=-1)
+    nk = dk.double().norm(dim=(2, 3))
+    assert bool((sk <= 2e-2 * nk).all()), f"{what}: |sum_j dK_j| / |dK| = {(sk / nk).max().item():.3e}"
+    sv = (dv.double().sum(dim=2) - do.double().sum(dim=2)).norm(dim=-1)
+    nv = dv.double().norm(dim=(2, 3))
+    assert bool((sv <= 2e-2 * nv).all()), f"{what}: |sum dV - sum dO| / |dV| = {(sv / nv).max().item():.3e}"
+
+
+@pytest.mark.parametrize("name", [n for n, w in workloads.WORKLOADS.items() if w.backward])
+def test_backward_full_size_sampled_heads(name):
+    ea = require_gpu()
+    w = workloads.WORKLOADS[name]
+    log(f"backward full size {w.name}")
+    x = workloads.make_inputs(w)
+    (q, k, v, do, o, lse), (dq, dk, dv) = _run(ea, x, w.scale, w.causal)
+    for t in (dq, dk, dv):
+        assert torch.isfinite(t).all().item()
+    _invariants(dk, dv, do, w.name)
+    heads = [(0, 0), (w.B - 1, w.H - 1)] if w.N >= 16384 else sorted({(0, 0), (w.B // 2, w.H // 3), (w.B - 1, w.H - 1)})
+    rb = 2048 if w.N > 4096 else None
+    for b, h in heads:
+        log(f"  oracle head ({b},{h})")
+        ref = oracle.backward_head(*(workloads.to_f64_numpy(x[n][b, h]) for n in ("q", "k", "v", "do")),
+                                   w.scale, w.causal, row_block=rb)
+        for gname, g, gr in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref):
+            check_grad(f64(g[b, h]), gr, f"{gname}[{b},{h}]")
+
+
+def test_backward_dk_dv_deterministic():
+    ea = require_gpu()
+    w = workloads.Workload("det", 2, 4, 1024, 128, "bf16", True, True, seed=9100)
+    x = workloads.make_inputs(w)
+    _, (dq1, dk1, dv1) = _run(ea, x, w.scale, True)
+    _, (dq2, dk2, dv2) = _run(ea, x, w.scale, True)
+    assert torch.equal(dk1, dk2) and torch.equal(dv1, dv2)
+    # dQ is summed with fp32 atomics: equal up to the last bits
+    assert (dq1.float() - dq2.float()).abs().max().item() <= 1e-2 * dq1.float().abs().max().item()
+
+
+def test_backward_writes_every_output_element():
+    ea = require_gpu()
+    w = workloads.Workload("nan", 1, 3, 448, 64, "fp16", True, True, seed=9200)
+    x = workloads.make_inputs(w)
+    q, k, v, do = (x[n].cuda() for n in ("q", "k", "v", "do"))
+    o, lse = ea.forward(q, k, v, scale=w.scale, causal=True)
+    dq, dk, dv = (torch.full_like(q, float("nan")) for _ in range(3))
+    ws = torch.full((ea.attn_bwd_workspace_bytes(1, 3, 448, 64),), 255, dtype=torch.uint8, device="cuda")
+    ea.attn_bwd(q, k, v, o, do, lse, dq, dk, dv, w.scale, True, ws)
+    torch.cuda.synchronize()
+    assert torch.isfinite(dq).all().item() and torch.isfinite(dk).all().item() and torch.isfinite(dv).all().item()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_special_inputs(causal):
+    """Identical keys give dQ = 0; identical values give dQ = dK = 0; a
+    peaky (x4 / x2) input exercises large lse values."""
+    ea = require_gpu()
+    B, H, N, d = 1, 2, 256, 128
+    w = workloads.Workload("special", B, H, N, d, "bf16", causal, True, seed=9300)
+    x = workloads.make_inputs(w)
+    same_k = dict(x, k=x["k"][:, :, :1].expand(-1, -1, N, -1).contiguous())
+    _, (dq, dk, dv) = _run(ea, same_k, w.scale, causal)
+    assert dq.float().abs().max().item() <= 1e-2 * (1 + dk.float().abs().max().item())
+    same_v = dict(x, v=x["v"][:, :, :1].expand(-1, -1, N, -1).contiguous())
+    _, (dq, dk, dv) = _run(ea, same_v, w.scale, causal)
+    assert dq.float().abs().max().item() <= 1e-2 and dk.float().abs().max().item() <= 1e-2
+    peaky = dict(x, q=(x["q"].float() * 4).to(torch.bfloat16), k=(x["k"].float() * 2).to(torch.bfloat16))
+    _, grads = _run(ea, peaky, w.scale, causal)
+    ref = oracle.backward(*(workloads.to_f64_numpy(peaky[n]) for n in ("q", "k", "v", "do")), w.scale, causal)
+    for name, g, gr in zip(("dQ", "dK", "dV"), grads, ref):
+        check_grad(f64(g), gr, f"peaky {name}")
+
+
+def test_backward_workspace_reuse_and_side_stream():
+    ea = require_gpu()
+    w = workloads.Workload("ws", 1, 2, 512, 64, "bf16", True, True, seed=9400)
+    x = workloads.make_inputs(w)
+    ws = torch.empty(ea.attn_bwd_workspace_bytes(1, 2, 512, 64), dtype=torch.uint8, device="cuda")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        q, k, v, do = (x[n].cuda() for n in ("q", "k", "v", "do"))
+        o, lse = ea.forward(q, k, v, scale=w.scale, causal=True)
+        g1 = ea.backward(q, k, v, o, lse, do, scale=w.scale, causal=True, workspace=ws)
+        g2 = ea.backward(q, k, v, o, lse, do, scale=w.scale, causal=True, workspace=ws)
+    s.synchronize()
+    assert torch.equal(g1[1], g2[1]) and torch.equal(g1[2], g2[2])
+    ref = oracle.backward(*(workloads.to_f64_numpy(x[n]) for n in ("q", "k", "v", "do")), w.scale, True)
+    for name, g, gr in zip(("dQ", "dK", "dV"), g2, ref):
+        check_grad(f64(g), gr, name)
