@@ -9,6 +9,7 @@ from ._binding import (  # noqa: F401
     ATTN_DTYPE_FP16,
     ATTN_OK,
     EXPORTED,
+    KERNEL_KINDS,
     LIB_PATH,
     STATUS_NAMES,
     AttnError,
@@ -16,6 +17,8 @@ from ._binding import (  # noqa: F401
     attn_bwd_workspace_bytes,
     attn_fwd,
     attn_last_hip_error,
+    attn_profile_start,
+    attn_profile_stop,
     attn_status_string,
     backward,
     default_scale,

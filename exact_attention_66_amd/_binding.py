@@ -24,7 +24,10 @@ STATUS_NAMES = {
     4: "ATTN_ERR_BAD_DTYPE", 5: "ATTN_ERR_MISALIGNED", 6: "ATTN_ERR_UNSUPPORTED_SEQLEN",
     7: "ATTN_ERR_BAD_SCALE", 8: "ATTN_ERR_WORKSPACE_TOO_SMALL", 9: "ATTN_ERR_ALIASING", 10: "ATTN_ERR_HIP",
 }
-EXPORTED = ["attn_fwd", "attn_bwd_workspace_bytes", "attn_bwd", "attn_status_string", "attn_last_hip_error"]
+EXPORTED = ["attn_fwd", "attn_bwd_workspace_bytes", "attn_bwd", "attn_profile_start", "attn_profile_stop",
+            "attn_status_string", "attn_last_hip_error"]
+# attn_kernel_kind values
+KERNEL_KINDS = ["fwd", "bwd_pre", "bwd_main", "bwd_dq_cast"]
 
 _lib = None
 
@@ -55,6 +58,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_bwd_workspace_bytes.restype = sz
     lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, f32, i32, i32, vp, sz, vp]
     lib.attn_bwd.restype = i32
+    lib.attn_profile_start.argtypes = []
+    lib.attn_profile_start.restype = i32
+    lib.attn_profile_stop.argtypes = [ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double)]
+    lib.attn_profile_stop.restype = i32
     lib.attn_status_string.argtypes = [i32]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_last_hip_error.argtypes = []
@@ -69,6 +76,23 @@ def attn_status_string(status: int) -> str:
 
 def attn_last_hip_error() -> int:
     return int(load().attn_last_hip_error())
+
+
+def attn_profile_start() -> None:
+    st = load().attn_profile_start()
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_profile_start")
+
+
+def attn_profile_stop() -> dict:
+    """Close the profiling window: {kernel: (launches, total_ms)} per kernel kind."""
+    n = len(KERNEL_KINDS)
+    counts = (ctypes.c_int64 * n)()
+    total = (ctypes.c_double * n)()
+    st = load().attn_profile_stop(counts, total)
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_profile_stop")
+    return {k: (int(counts[i]), float(total[i])) for i, k in enumerate(KERNEL_KINDS)}
 
 
 def attn_bwd_workspace_bytes(B: int, H: int, N: int, d: int) -> int:

@@ -327,8 +327,8 @@ hipError_t launch_bwd_cfg(const BwdArgs& a) {
   {
     constexpr int RPB = 256 / (D / 8);
     void* args[] = {(void*)&o, (void*)&dO, (void*)&delta, (void*)&dqa, (void*)&rows};
-    hipError_t e = hipLaunchKernel((const void*)bwd_pre<E, D>, dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256),
-                                   args, 0, a.stream);
+    hipError_t e = launch_kernel((const void*)bwd_pre<E, D>, dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256),
+                                 args, a.stream, 1);
     if (e != hipSuccess) return e;
   }
   {
@@ -336,15 +336,15 @@ hipError_t launch_bwd_cfg(const BwdArgs& a) {
     void* args[] = {(void*)&q, (void*)&k, (void*)&v, (void*)&dO, (void*)&lse, (void*)&delta, (void*)&dk,
                     (void*)&dv, (void*)&dqa, (void*)&BH, (void*)&N, (void*)&nkb, (void*)&scale,
                     (void*)&scale_log2};
-    hipError_t e = hipLaunchKernel((const void*)bwd_main<E, D, CAUSAL, NW, BMQ>, dim3((unsigned)(nkb * BH)),
-                                   dim3(NW * 64), args, 0, a.stream);
+    hipError_t e = launch_kernel((const void*)bwd_main<E, D, CAUSAL, NW, BMQ>, dim3((unsigned)(nkb * BH)),
+                                 dim3(NW * 64), args, a.stream, 2);
     if (e != hipSuccess) return e;
   }
   {
     int64_t n8 = rows * D / 8;
     void* args[] = {(void*)&dqa, (void*)&dq, (void*)&n8, (void*)&scale};
-    return hipLaunchKernel((const void*)bwd_dq_cast<E>, dim3((unsigned)((n8 + 255) / 256)), dim3(256), args, 0,
-                           a.stream);
+    return launch_kernel((const void*)bwd_dq_cast<E>, dim3((unsigned)((n8 + 255) / 256)), dim3(256), args,
+                         a.stream, 3);
   }
 }
 

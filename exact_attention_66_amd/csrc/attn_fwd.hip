@@ -270,7 +270,7 @@ hipError_t launch_fwd_cfg(const FwdArgs& a) {
   float* lse = a.lse;
   void* args[] = {(void*)&q, (void*)&k, (void*)&v, (void*)&o, (void*)&lse,
                   (void*)&BH, (void*)&N, (void*)&nqb, (void*)&scale_log2};
-  return hipLaunchKernel((const void*)fwd_kernel<E, D, CAUSAL, QB, NW, BN>, grid, block, args, 0, a.stream);
+  return launch_kernel((const void*)fwd_kernel<E, D, CAUSAL, QB, NW, BN>, grid, block, args, a.stream, 0);
 }
 
 template <typename E, int D>

@@ -40,6 +40,10 @@ struct BwdArgs {
   hipStream_t stream;
 };
 
+// hipLaunchKernel, or an event-timed launch while a profiling window is open;
+// kind is an attn_kernel_kind value.
+hipError_t launch_kernel(const void* fn, dim3 grid, dim3 block, void** args, hipStream_t stream, int kind);
+
 hipError_t launch_fwd(const FwdArgs& a);
 hipError_t launch_bwd(const BwdArgs& a);
 

@@ -1,0 +1,91 @@
+// Opt-in kernel timing: while a profiling window is open, every kernel the
+// library launches is bracketed by a HIP event pair taken by the launch
+// itself (hipExtLaunchKernel), so the durations are those of the kernels on
+// the stream they run on.  Closed by default; the launch path then calls
+// hipLaunchKernel directly and keeps no state.
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <mutex>
+#include <vector>
+
+#include "../../include/attn.h"
+#include "attn_launch.h"
+
+namespace attn {
+
+namespace {
+
+struct Rec {
+  int kind;
+  hipEvent_t start, stop;
+};
+
+std::atomic<bool> g_on{false};
+std::mutex g_mu;
+std::vector<Rec> g_recs;
+
+}  // namespace
+
+hipError_t launch_kernel(const void* fn, dim3 grid, dim3 block, void** args, hipStream_t stream, int kind) {
+  if (!g_on.load(std::memory_order_acquire)) return hipLaunchKernel(fn, grid, block, args, 0, stream);
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  hipError_t e = hipEventCreate(&e0);
+  if (e == hipSuccess) e = hipEventCreate(&e1);
+  if (e != hipSuccess) {
+    if (e0) (void)hipEventDestroy(e0);
+    return e;
+  }
+  e = hipExtLaunchKernel(fn, grid, block, args, 0, stream, e0, e1, 0);
+  if (e != hipSuccess) {
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    return e;
+  }
+  std::lock_guard<std::mutex> lk(g_mu);
+  g_recs.push_back({kind, e0, e1});
+  return hipSuccess;
+}
+
+}  // namespace attn
+
+extern "C" {
+
+int attn_profile_start(void) {
+  std::lock_guard<std::mutex> lk(attn::g_mu);
+  for (auto& r : attn::g_recs) {
+    (void)hipEventDestroy(r.start);
+    (void)hipEventDestroy(r.stop);
+  }
+  attn::g_recs.clear();
+  attn::g_on.store(true, std::memory_order_release);
+  return ATTN_OK;
+}
+
+int attn_profile_stop(int64_t counts[ATTN_KERNEL_KINDS], double total_ms[ATTN_KERNEL_KINDS]) {
+  attn::g_on.store(false, std::memory_order_release);
+  std::lock_guard<std::mutex> lk(attn::g_mu);
+  int status = ATTN_OK;
+  for (int i = 0; i < ATTN_KERNEL_KINDS; ++i) {
+    if (counts) counts[i] = 0;
+    if (total_ms) total_ms[i] = 0.0;
+  }
+  for (auto& r : attn::g_recs) {
+    float ms = 0.f;
+    hipError_t e = hipEventSynchronize(r.stop);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.start, r.stop);
+    if (e != hipSuccess) {
+      status = ATTN_ERR_HIP;
+    } else if (r.kind >= 0 && r.kind < ATTN_KERNEL_KINDS) {
+      if (counts) counts[r.kind] += 1;
+      if (total_ms) total_ms[r.kind] += ms;
+    }
+    (void)hipEventDestroy(r.start);
+    (void)hipEventDestroy(r.stop);
+  }
+  attn::g_recs.clear();
+  return status;
+}
+
+}  // extern "C"

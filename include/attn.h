@@ -27,13 +27,16 @@
  *            (1/sqrt(d) is the usual value).
  * Pointers:  device pointers (hipMalloc / torch CUDA tensors) on the current
  *            device, each 16-byte aligned.  The caller owns all memory; the
- *            library allocates nothing and keeps no state between calls.
+ *            library allocates no device memory and keeps no state between
+ *            calls (apart from the opt-in profiling window below).
  * Sizes:     B, H, N >= 1; d in {64, 128}; N a multiple of 64.
  * Streams:   work is enqueued on `stream` (a hipStream_t; NULL = the null
  *            stream) and the call returns without synchronising.
- * Errors:    every check runs before any HIP call; on a nonzero return no
- *            output has been written and nothing has been enqueued.  Faults
- *            inside a kernel surface at the caller's next synchronisation.
+ * Errors:    every argument check runs before any HIP call: an argument
+ *            error writes nothing and enqueues nothing.  ATTN_ERR_HIP means a
+ *            launch was refused (kernels of the same call launched before it
+ *            stay enqueued).  Faults inside a kernel surface at the caller's
+ *            next synchronisation.
  * Threads:   calls are re-entrant; calls on different streams may overlap.
  */
 #ifndef EXACT_ATTENTION_ATTN_H
@@ -107,6 +110,33 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o,
              const void* dO, const float* lse, void* dq, void* dk, void* dv,
              int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal,
              int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Kernels the library launches, as counted by the profiling window below. */
+enum attn_kernel_kind {
+  ATTN_KERNEL_FWD = 0,         /* forward: O and lse */
+  ATTN_KERNEL_BWD_PRE = 1,     /* backward: D = rowsum(dO * O), dQ accumulator cleared */
+  ATTN_KERNEL_BWD_MAIN = 2,    /* backward: recompute, dK, dV, dQ accumulation */
+  ATTN_KERNEL_BWD_DQ_CAST = 3, /* backward: dQ = scale * accumulator, rounded */
+  ATTN_KERNEL_KINDS = 4,
+};
+
+/*
+ * attn_profile_start / attn_profile_stop - kernel timing for measurement.
+ * Between the two calls (process-wide, all threads and streams) every kernel
+ * launch is bracketed by a HIP event pair recorded by the launch itself on
+ * the kernel's own stream; the events are created by the library and are the
+ * only resource it holds, until attn_profile_stop.  attn_profile_start
+ * discards earlier records and returns ATTN_OK.  attn_profile_stop closes the
+ * window, waits for the recorded events, and writes, per attn_kernel_kind,
+ * the number of launches (counts) and their summed duration in milliseconds
+ * (total_ms); either array may be NULL.  Returns ATTN_OK, or ATTN_ERR_HIP if
+ * an event could not be read (those launches are left out of the sums).
+ * Launches that fail to create their events return ATTN_ERR_HIP.  The
+ * timing is not part of the attention computation (not described on the
+ * pages); it exists to measure the kernels against their roofline.
+ */
+int attn_profile_start(void);
+int attn_profile_stop(int64_t counts[ATTN_KERNEL_KINDS], double total_ms[ATTN_KERNEL_KINDS]);
 
 /* attn_status_string - static, NUL-terminated description of a status code. */
 const char* attn_status_string(int status);
