@@ -35,7 +35,8 @@ PEAK_TFLOPS = 2516.6   # MI355X dense bf16/fp16 MFMA: 256 CU x 4096 flop/clk x 2
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 KERNEL_SOURCES = {
     "fwd": "exact_attention_66_amd/csrc/attn_fwd.hip",
-    "bwd_main": "exact_attention_66_amd/csrc/attn_bwd.hip",
+    "bwd_dkdv": "exact_attention_66_amd/csrc/attn_bwd.hip",
+    "bwd_dq": "exact_attention_66_amd/csrc/attn_bwd.hip",
 }
 
 
@@ -175,7 +176,10 @@ def main() -> int:
     flops = w.fwd_flops() + w.bwd_flops()
     value = flops / (ms_per_step * 1e-3) / 1e12
 
-    flops_per_launch = {"fwd": w.fwd_flops(), "bwd_main": w.bwd_flops()}
+    # algorithmic (counted) flops each kernel carries: the backward's five
+    # products are S, dP, dV, dK (in bwd_dkdv) and dQ (in bwd_dq, which also
+    # recomputes S and dP: extra work that is not counted)
+    flops_per_launch = {"fwd": w.fwd_flops(), "bwd_dkdv": 0.8 * w.bwd_flops(), "bwd_dq": 0.2 * w.bwd_flops()}
     kernels = {kname: {"launches": n, "avg_ms": round(t / n, 5)} for kname, (n, t) in prof.items() if n}
     dominant = max((kname for kname in kernels if kname in flops_per_launch),
                    key=lambda kname: prof[kname][1])

@@ -27,7 +27,7 @@ STATUS_NAMES = {
 EXPORTED = ["attn_fwd", "attn_bwd_workspace_bytes", "attn_bwd", "attn_profile_start", "attn_profile_stop",
             "attn_status_string", "attn_last_hip_error"]
 # attn_kernel_kind values
-KERNEL_KINDS = ["fwd", "bwd_pre", "bwd_main", "bwd_dq_cast"]
+KERNEL_KINDS = ["fwd", "bwd_prep", "bwd_dkdv", "bwd_dq"]
 
 _lib = None
 

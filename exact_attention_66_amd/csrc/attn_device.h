@@ -72,6 +72,28 @@ __device__ __forceinline__ constexpr int acc_row(int j, int h) { return 8 * (j /
 // reduction step kk with no data movement.
 __device__ __forceinline__ constexpr int slot_key(int i, int h) { return 8 * (i / 4) + 4 * h + (i % 4); }
 
+// Swizzled LDS tile of 16-bit elements, ROWLEN (32, 64 or 128) elements per row
+// and no padding: the 16-byte chunk c of row r is stored at chunk c ^ f(r).
+// f is chosen so that, with 64 four-byte banks, both access patterns the
+// kernels use are free of bank conflicts:
+//  * ds_read_b128 by 16 lanes of 16 consecutive rows at the same chunk:
+//    f is one-to-one on any 16 consecutive rows;
+//  * ds_read_b64_tr_b16 by 32 lanes of 4 consecutive rows (4-aligned) x 64
+//    contiguous bytes (4 chunks 4m..4m+3): the rows' f differ in bits 2..3
+//    (ROWLEN 128), or in bit 2 for rows of the same parity (ROWLEN 64, where
+//    two rows share one 256-byte bank cycle), so the 16 (row, chunk) pairs
+//    land on 16 distinct groups of 4 banks.
+// ROWLEN 32 (four rows per bank cycle): f = (row >> 2) & 3 separates the 16
+// consecutive rows of a b128 read; a transpose read covers 4 whole rows.
+template <int ROWLEN>
+__device__ __forceinline__ int swz(int row, int col) {
+  static_assert(ROWLEN == 32 || ROWLEN == 64 || ROWLEN == 128, "row length");
+  const int f = ROWLEN == 128  ? (4 * (row & 3) + ((row >> 2) & 3))
+                : ROWLEN == 64 ? (4 * ((row >> 1) & 1) + ((row >> 2) & 3))
+                               : ((row >> 2) & 3);
+  return row * ROWLEN + (((col >> 3) ^ f) << 3) + (col & 7);
+}
+
 // max / sum of a value across the two 32-lane halves (lane l and l ^ 32).
 __device__ __forceinline__ float xhalf_max(float x) {
   auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -83,6 +105,44 @@ __device__ __forceinline__ float xhalf_sum(float x) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Wait for every outstanding vector-memory load of this wave (vmcnt = 0,
+// other counters untouched).  Placed after loads issued before a main loop:
+// otherwise the compiler may leave them in flight into the loop, and since
+// the counter is in-order, its waits for them inside the loop end up waiting
+// for the loop's own prefetches as well.
+__device__ __forceinline__ void wait_all_vmem_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Pin a loaded value in registers at this point of the program: the (empty)
+// volatile asm reads it, so the load must have completed here and cannot be
+// sunk past later barriers into a loop.
+template <typename V>
+__device__ __forceinline__ void materialize(const V& x) { asm volatile("" : : "v"(x)); }
+
+// An integer the compiler cannot see through (so it keeps the register
+// instead of recomputing the expression inside a loop).
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// Wait out the latency of the MFMAs just issued, placed at the end of every
+// tile iteration, before the barrier.  The compiler may put register copies
+// of MFMA accumulators right after that barrier (loop header or epilogue)
+// without counting the barrier as wait states; a barrier that releases at
+// once would then let a copy read an accumulator before its MFMA has written
+// it (seen as a wrong last element of dK with a single query tile).
+// 32 cycles covers the 8-pass 32x32 MFMA.
+__device__ __forceinline__ void mfma_drain() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Scheduling fence: the compiler may not move any instruction across it.
+// Used to keep a block of LDS reads ahead of the MFMAs that consume them, so
+// that all reads are in flight at once instead of one pair at a time.
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
 // 8 fp32 -> 8 16-bit values (round to nearest even) packed as an MFMA operand.
 template <typename E>

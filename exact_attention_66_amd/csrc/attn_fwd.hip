@@ -35,8 +35,12 @@ constexpr float kLog2e = 1.44269504088896340736f;
 // Rescale O only when the running max grows by more than this (log2 units).
 constexpr float kRescaleSlack = 8.0f;
 
+#ifndef ATTN_FWD_MINW
+#define ATTN_FWD_MINW 2  // waves per SIMD the register budget is sized for
+#endif
+
 template <typename E, int D, bool CAUSAL, int QB, int NW, int BN>
-__global__ __launch_bounds__(NW * 64) void fwd_kernel(const typename E::T* __restrict__ Q,
+__global__ __launch_bounds__(NW * 64, ATTN_FWD_MINW) void fwd_kernel(const typename E::T* __restrict__ Q,
                                                       const typename E::T* __restrict__ K,
                                                       const typename E::T* __restrict__ V,
                                                       typename E::T* __restrict__ O,
@@ -49,13 +53,12 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(const typename E::T* __res
   constexpr int KS = D / 16;         // reduction steps over d for S
   constexpr int DB = D / 32;         // 32-wide d blocks of O^T
   constexpr int KB = BN / 32;        // 32-key blocks per tile
-  constexpr int LD = D + 8;          // padded LDS row, in elements
   constexpr int NT = NW * 64;
   constexpr int CPT = BN * D / 8 / NT;  // 16-byte chunks per thread per tensor
   static_assert(CPT >= 1 && (BN * D / 8) % NT == 0, "tile must split evenly over threads");
 
-  __shared__ __attribute__((aligned(16))) T lds_k[2][BN * LD];
-  __shared__ __attribute__((aligned(16))) T lds_v[2][BN * LD];
+  __shared__ __attribute__((aligned(16))) T lds_k[2][BN * D];  // swizzled rows (swz<D>)
+  __shared__ __attribute__((aligned(16))) T lds_v[2][BN * D];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -87,6 +90,10 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(const typename E::T* __res
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qf[qb][ks] = *(const v8*)(Qh + (size_t)q * D + ks * 16 + 8 * h);
   }
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) materialize(qf[qb][ks]);
 
   f32x16 oacc[QB][DB];
   // m_run: running max (log2 units, may trail the true max by < kRescaleSlack);
@@ -125,13 +132,14 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(const typename E::T* __res
       const int idx = tid + c * NT;
       const int row = idx / (D / 8);
       const int col = (idx % (D / 8)) * 8;
-      *(v8*)(&lds_k[buf][row * LD + col]) = kreg[c];
-      *(v8*)(&lds_v[buf][row * LD + col]) = vreg[c];
+      *(v8*)(&lds_k[buf][swz<D>(row, col)]) = kreg[c];
+      *(v8*)(&lds_v[buf][swz<D>(row, col)]) = vreg[c];
     }
   };
 
   gload(0);
   lstore(0);
+  wait_all_vmem_loads();
   __syncthreads();
 
   for (int t = 0; t < ntiles; ++t) {
@@ -152,7 +160,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(const typename E::T* __res
       for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-          const v8 kf = *(const v8*)(kl + (kb * 32 + r) * LD + ks * 16 + 8 * h);
+          const v8 kf = *(const v8*)(kl + swz<D>(kb * 32 + r, ks * 16 + 8 * h));
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) s[kb][qb] = E::mfma32(kf, qf[qb][ks], s[kb][qb]);
         }
@@ -219,8 +227,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(const typename E::T* __res
           const int vcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 #pragma unroll
           for (int db = 0; db < DB; ++db) {
-            const v4 lo = E::tr_read(vl + vrow * LD + db * 32 + vcol);
-            const v4 hi = E::tr_read(vl + (vrow + 8) * LD + db * 32 + vcol);
+            const v4 lo = E::tr_read(vl + swz<D>(vrow, db * 32 + vcol));
+            const v4 hi = E::tr_read(vl + swz<D>(vrow + 8, db * 32 + vcol));
             const v8 vf = concat44<E>(lo, hi);
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = E::mfma32(vf, pf[kb][kk][qb], oacc[qb][db]);
@@ -229,6 +237,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(const typename E::T* __res
       }
     }
     if (t + 1 < ntiles) lstore(buf ^ 1);
+    mfma_drain();
     __syncthreads();
   }
 

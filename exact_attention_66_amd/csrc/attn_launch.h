@@ -35,8 +35,11 @@ struct BwdArgs {
   float scale;
   bool causal;
   int dtype;
-  float* delta;   // [B,H,N] fp32 scratch: D_i = dO_i . O_i
-  float* dq_acc;  // [B,H,N,d] fp32 scratch: dQ accumulator
+  // workspace parts
+  float* delta;   // [B,H,N] fp32: D_i = dO_i . O_i
+  void* qt;       // [B,H,d,N] 16-bit: Q transposed (tokens in slot order per 16)
+  void* kt;       // [B,H,d,N] 16-bit: K transposed
+  void* dot;      // [B,H,d,N] 16-bit: dO transposed
   hipStream_t stream;
 };
 
@@ -47,10 +50,10 @@ hipError_t launch_kernel(const void* fn, dim3 grid, dim3 block, void** args, hip
 hipError_t launch_fwd(const FwdArgs& a);
 hipError_t launch_bwd(const BwdArgs& a);
 
-// Workspace split used by attn_bwd: delta first, then the dQ accumulator,
-// each starting on a 256-byte boundary.
+// Workspace split used by attn_bwd: delta, then Q^T, K^T, dO^T, each part
+// starting on a 256-byte boundary.
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 inline size_t bwd_delta_bytes(int64_t B, int64_t H, int64_t N) { return align256((size_t)(B * H * N) * 4); }
-inline size_t bwd_dqacc_bytes(int64_t B, int64_t H, int64_t N, int64_t d) { return align256((size_t)(B * H * N * d) * 4); }
+inline size_t bwd_tcopy_bytes(int64_t B, int64_t H, int64_t N, int64_t d) { return align256((size_t)(B * H * N * d) * 2); }
 
 }  // namespace attn

@@ -84,10 +84,11 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 
 /*
  * attn_bwd_workspace_bytes - size of the scratch buffer attn_bwd needs:
- * one fp32 per query row (D_i = dO_i . O_i) plus an fp32 [B,H,N,d] dQ
- * accumulator, rounded up to 256 bytes.  It grows as O(B*H*N*d), never with
- * N^2 (the memory bound of page "突破单卡显存极限…" §2.2).  Returns 0 when the
- * sizes are invalid (B, H, N < 1, d not in {64,128}, or overflow).
+ * one fp32 per query row (D_i = dO_i . O_i) plus three 16-bit [B,H,d,N]
+ * transposed copies of Q, K and dO, each part rounded up to 256 bytes:
+ * 4*B*H*N + 6*B*H*N*d bytes.  It grows as O(B*H*N*d), never with N^2 (the
+ * memory bound of page "突破单卡显存极限…" §2.2).  Returns 0 when the sizes
+ * are invalid (B, H, N < 1, d not in {64,128}, or overflow).
  */
 size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d);
 
@@ -101,9 +102,8 @@ size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d);
  *              bytes, 256-byte aligned; overwritten, contents undefined
  *              afterwards.  Concurrent calls need distinct workspaces.
  * dq, dk, dv and workspace must not overlap any input or each other.
- * dK and dV are accumulated per key block without atomics and are bitwise
- * reproducible; dQ is summed across key blocks with fp32 atomics, so its last
- * bits may vary from run to run.
+ * No atomics are used: every output element is accumulated by one lane, so
+ * dQ, dK and dV are bitwise reproducible from run to run.
  * Returns ATTN_OK or an attn_status error code.
  */
 int attn_bwd(const void* q, const void* k, const void* v, const void* o,
@@ -114,9 +114,9 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o,
 /* Kernels the library launches, as counted by the profiling window below. */
 enum attn_kernel_kind {
   ATTN_KERNEL_FWD = 0,         /* forward: O and lse */
-  ATTN_KERNEL_BWD_PRE = 1,     /* backward: D = rowsum(dO * O), dQ accumulator cleared */
-  ATTN_KERNEL_BWD_MAIN = 2,    /* backward: recompute, dK, dV, dQ accumulation */
-  ATTN_KERNEL_BWD_DQ_CAST = 3, /* backward: dQ = scale * accumulator, rounded */
+  ATTN_KERNEL_BWD_PREP = 1,    /* backward: D = rowsum(dO * O), transposed Q, K, dO */
+  ATTN_KERNEL_BWD_DKDV = 2,    /* backward: recompute per key block, dK and dV */
+  ATTN_KERNEL_BWD_DQ = 3,      /* backward: recompute per query block, dQ */
   ATTN_KERNEL_KINDS = 4,
 };
 

@@ -81,15 +81,14 @@ def test_backward_full_size_sampled_heads(name):
             check_grad(f64(g[b, h]), gr, f"{gname}[{b},{h}]")
 
 
-def test_backward_dk_dv_deterministic():
+def test_backward_deterministic():
+    """No atomics: every gradient element is accumulated by one lane, so runs are bitwise equal."""
     ea = require_gpu()
     w = workloads.Workload("det", 2, 4, 1024, 128, "bf16", True, True, seed=9100)
     x = workloads.make_inputs(w)
     _, (dq1, dk1, dv1) = _run(ea, x, w.scale, True)
     _, (dq2, dk2, dv2) = _run(ea, x, w.scale, True)
-    assert torch.equal(dk1, dk2) and torch.equal(dv1, dv2)
-    # dQ is summed with fp32 atomics: equal up to the last bits
-    assert (dq1.float() - dq2.float()).abs().max().item() <= 1e-2 * dq1.float().abs().max().item()
+    assert torch.equal(dk1, dk2) and torch.equal(dv1, dv2) and torch.equal(dq1, dq2)
 
 
 def test_backward_writes_every_output_element():
@@ -138,7 +137,7 @@ def test_backward_workspace_reuse_and_side_stream():
         g1 = ea.backward(q, k, v, o, lse, do, scale=w.scale, causal=True, workspace=ws)
         g2 = ea.backward(q, k, v, o, lse, do, scale=w.scale, causal=True, workspace=ws)
     s.synchronize()
-    assert torch.equal(g1[1], g2[1]) and torch.equal(g1[2], g2[2])
+    assert all(torch.equal(a, b) for a, b in zip(g1, g2))
     ref = oracle.backward(*(workloads.to_f64_numpy(x[n]) for n in ("q", "k", "v", "do")), w.scale, True)
     for name, g, gr in zip(("dQ", "dK", "dV"), g2, ref):
         check_grad(f64(g), gr, name)
