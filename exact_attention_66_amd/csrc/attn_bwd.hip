@@ -57,6 +57,12 @@ constexpr float kLog2e = 1.44269504088896340736f;
 #ifndef ATTN_DQ_MINW
 #define ATTN_DQ_MINW 2
 #endif
+#ifndef ATTN_DQ_KTSTAGE
+#define ATTN_DQ_KTSTAGE 0  // read all K^T fragments before the softmax
+#endif
+#ifndef ATTN_DQ_KSTAGE
+#define ATTN_DQ_KSTAGE 2  // K and V operand fragments read ahead per batch
+#endif
 
 // ---------------------------------------------------------------- prep
 // One workgroup per (batch*head, 64-token block).  Q, K, dO tiles go through
@@ -493,31 +499,33 @@ __global__ __launch_bounds__(NW * 64, ATTN_DQ_MINW) void bwd_dq(
     const T* vl = lds_v[buf] + offA + kb * 32 * LR;
     const T* ktl = lds_kt[buf] + offB + kb * 32;
     // S^T = K Q^T, dP^T = V dO^T: lane holds query qw0 + r, keys acc_row(j, h).
-    // Operand reads are issued in two half batches, each ahead of its MFMAs.
+    // Operand reads go in batches of KSTAGE per operand, each batch issued
+    // ahead of its MFMAs.
     f32x16 sacc = f32x16{}, dpacc = f32x16{};
-    constexpr int KH = KS / 2;
+    constexpr int KH = ATTN_DQ_KSTAGE < KS ? ATTN_DQ_KSTAGE : KS;
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
+    for (int part = 0; part < KS / KH; ++part) {
       v8 ka[KH], va[KH];
 #pragma unroll
       for (int u = 0; u < KH; ++u) {
-        ka[u] = *(const v8*)(kl + (half * KH + u) * 16);
-        va[u] = *(const v8*)(vl + (half * KH + u) * 16);
+        ka[u] = *(const v8*)(kl + (part * KH + u) * 16);
+        va[u] = *(const v8*)(vl + (part * KH + u) * 16);
       }
       sched_fence();
 #pragma unroll
       for (int u = 0; u < KH; ++u) {
-        sacc = E::mfma32(ka[u], qf[half * KH + u], sacc);
-        dpacc = E::mfma32(va[u], dof[half * KH + u], dpacc);
+        sacc = E::mfma32(ka[u], qf[part * KH + u], sacc);
+        dpacc = E::mfma32(va[u], dof[part * KH + u], dpacc);
       }
       sched_fence();
     }
+#if ATTN_DQ_KTSTAGE
     v8 kta[2][DB];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
       for (int db = 0; db < DB; ++db) kta[kk][db] = *(const v8*)(ktl + db * 32 * LT + 16 * kk);
-    sched_fence();
+#endif
     float ds[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) ds[j] = fast_exp2(fmaf(sacc[j], scale_log2, -lse2));
@@ -534,7 +542,14 @@ __global__ __launch_bounds__(NW * 64, ATTN_DQ_MINW) void bwd_dq(
       const v8 sb = pack8<E>(ds[8 * kk + 0], ds[8 * kk + 1], ds[8 * kk + 2], ds[8 * kk + 3], ds[8 * kk + 4],
                              ds[8 * kk + 5], ds[8 * kk + 6], ds[8 * kk + 7]);
 #pragma unroll
-      for (int db = 0; db < DB; ++db) acc[db] = E::mfma32(kta[kk][db], sb, acc[db]);
+      for (int db = 0; db < DB; ++db) {
+#if ATTN_DQ_KTSTAGE
+        const v8 a = kta[kk][db];
+#else
+        const v8 a = *(const v8*)(ktl + db * 32 * LT + 16 * kk);
+#endif
+        acc[db] = E::mfma32(a, sb, acc[db]);
+      }
     }
   };
 

@@ -35,17 +35,31 @@ constexpr float kLog2e = 1.44269504088896340736f;
 // Rescale O only when the running max grows by more than this (log2 units).
 constexpr float kRescaleSlack = 8.0f;
 
+#ifndef ATTN_FWD_QB
+#define ATTN_FWD_QB 1    // 32-query blocks per wave
+#endif
+#ifndef ATTN_FWD_NW
+#define ATTN_FWD_NW 8    // waves per workgroup
+#endif
+#ifndef ATTN_FWD_BN
+#define ATTN_FWD_BN 64   // keys per LDS tile
+#endif
 #ifndef ATTN_FWD_MINW
 #define ATTN_FWD_MINW 2  // waves per SIMD the register budget is sized for
 #endif
 
+// LDS tiles: K [BN][D + 8] is read with ds_read_b128 by 16 lanes of 16
+// consecutive rows (rows 4 banks apart: conflict free); V [BN][D + 32] is read
+// with ds_read_b64_tr_b16 by 32 lanes covering 4 rows x 64 bytes (rows 16
+// banks apart: the 4 rows land on 4 disjoint 16-bank groups).  Both are
+// affine, so every read is one per-lane base plus an immediate offset.
 template <typename E, int D, bool CAUSAL, int QB, int NW, int BN>
 __global__ __launch_bounds__(NW * 64, ATTN_FWD_MINW) void fwd_kernel(const typename E::T* __restrict__ Q,
-                                                      const typename E::T* __restrict__ K,
-                                                      const typename E::T* __restrict__ V,
-                                                      typename E::T* __restrict__ O,
-                                                      float* __restrict__ LSE, int BH, int N, int nqb,
-                                                      float scale_log2) {
+                                                                     const typename E::T* __restrict__ K,
+                                                                     const typename E::T* __restrict__ V,
+                                                                     typename E::T* __restrict__ O,
+                                                                     float* __restrict__ LSE, int BH, int N,
+                                                                     int nqb, float scale_log2) {
   using T = typename E::T;
   using v8 = typename E::v8;
   using v4 = typename E::v4;
@@ -53,12 +67,15 @@ __global__ __launch_bounds__(NW * 64, ATTN_FWD_MINW) void fwd_kernel(const typen
   constexpr int KS = D / 16;         // reduction steps over d for S
   constexpr int DB = D / 32;         // 32-wide d blocks of O^T
   constexpr int KB = BN / 32;        // 32-key blocks per tile
+  constexpr int LK = D + 8;          // K tile row (elements)
+  constexpr int LV = D + 32;         // V tile row (elements)
   constexpr int NT = NW * 64;
-  constexpr int CPT = BN * D / 8 / NT;  // 16-byte chunks per thread per tensor
-  static_assert(CPT >= 1 && (BN * D / 8) % NT == 0, "tile must split evenly over threads");
+  constexpr int CHUNKS = BN * D / 8;          // 16-byte chunks per tile and tensor
+  constexpr int CPT = (CHUNKS + NT - 1) / NT;
+  static_assert(CHUNKS % NT == 0 || CHUNKS < NT, "tile must split evenly over threads");
 
-  __shared__ __attribute__((aligned(16))) T lds_k[2][BN * D];  // swizzled rows (swz<D>)
-  __shared__ __attribute__((aligned(16))) T lds_v[2][BN * D];
+  __shared__ __attribute__((aligned(16))) T lds_k[2][BN * LK];
+  __shared__ __attribute__((aligned(16))) T lds_v[2][BN * LV];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -110,6 +127,10 @@ __global__ __launch_bounds__(NW * 64, ATTN_FWD_MINW) void fwd_kernel(const typen
     for (int db = 0; db < DB; ++db) oacc[qb][db] = f32x16{};
   }
 
+  // per-lane parts of the LDS read addresses (elements)
+  const int offK = opaque(r * LK + 8 * h);
+  const int offV = opaque((4 * h + ((lane & 15) >> 2)) * LV + 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+
   const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
   const int ntiles = (kv_end + BN - 1) / BN;
   const int q_last = qw0 + 32 * QB - 1;
@@ -119,6 +140,7 @@ __global__ __launch_bounds__(NW * 64, ATTN_FWD_MINW) void fwd_kernel(const typen
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const int idx = tid + c * NT;
+      if (idx >= CHUNKS) break;
       const int row = idx / (D / 8);
       const int col = (idx % (D / 8)) * 8;
       const int key = min(t * BN + row, N - 1);
@@ -130,10 +152,86 @@ __global__ __launch_bounds__(NW * 64, ATTN_FWD_MINW) void fwd_kernel(const typen
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const int idx = tid + c * NT;
+      if (idx >= CHUNKS) break;
       const int row = idx / (D / 8);
       const int col = (idx % (D / 8)) * 8;
-      *(v8*)(&lds_k[buf][swz<D>(row, col)]) = kreg[c];
-      *(v8*)(&lds_v[buf][swz<D>(row, col)]) = vreg[c];
+      *(v8*)(&lds_k[buf][row * LK + col]) = kreg[c];
+      *(v8*)(&lds_v[buf][row * LV + col]) = vreg[c];
+    }
+  };
+
+  // one 32-key block: S^T, mask, online softmax, O^T += V^T P^T
+  auto key_block = [&](const int buf, const int kb, const int kbk0) {
+    const T* kl = lds_k[buf] + offK + kb * 32 * LK;
+    const T* vl = lds_v[buf] + offV + kb * 32 * LV;
+    // ---- S^T = K Q^T (every K fragment read before the MFMAs)
+    v8 kf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kf[ks] = *(const v8*)(kl + ks * 16);
+    sched_fence();
+    f32x16 s[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) s[qb] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) s[qb] = E::mfma32(kf[ks], qf[qb][ks], s[qb]);
+    sched_fence();
+    // ---- causal mask (key > query -> -inf) on blocks that cross the diagonal
+    if (CAUSAL && kbk0 + 31 > qw0) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if (kbk0 + acc_row(j, h) > qw0 + qb * 32 + r) s[qb][j] = -__builtin_inff();
+    }
+    // ---- online softmax (log2 domain); P is rounded to 16 bits and kept
+    // packed as the B operand of the P V product
+    v8 pf[2][QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[qb][j]);
+      mx = xhalf_max(mx);
+      const float mt = mx * scale_log2;
+      const bool need = mt > m_run[qb] + kRescaleSlack;
+      if (__builtin_amdgcn_ballot_w64(need) != 0) {
+        const float mn = fmaxf(m_run[qb], mt);
+        const float alpha = fast_exp2(m_run[qb] - mn);
+        l_run[qb] *= alpha;
+        lr_run[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) oacc[qb][db] *= alpha;
+        m_run[qb] = mn;
+      }
+      const float neg_m = -m_run[qb];
+      float ls = 0.f, lr = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        float p[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          p[i] = fast_exp2(fmaf(s[qb][8 * kk + i], scale_log2, neg_m));
+          ls += p[i];
+        }
+        pf[kk][qb] = pack8<E>(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
+        lr = sum8<E>(pf[kk][qb], lr);
+      }
+      l_run[qb] += ls;
+      lr_run[qb] += lr;
+    }
+    // ---- O^T += V^T P^T; V^T fragments from LDS transpose reads
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const v4 lo = E::tr_read(vl + kk * 16 * LV + db * 32);
+        const v4 hi = E::tr_read(vl + (kk * 16 + 8) * LV + db * 32);
+        const v8 vf = concat44<E>(lo, hi);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = E::mfma32(vf, pf[kk][qb], oacc[qb][db]);
+      }
     }
   };
 
@@ -142,104 +240,26 @@ __global__ __launch_bounds__(NW * 64, ATTN_FWD_MINW) void fwd_kernel(const typen
   wait_all_vmem_loads();
   __syncthreads();
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
+  auto k_tile = [&](const int t, const int buf) {
     if (t + 1 < ntiles) gload(t + 1);
     const int k0 = t * BN;
-    const bool active = wave_valid && (!CAUSAL || k0 <= q_last);
-    if (active) {
-      const T* kl = lds_k[buf];
-      const T* vl = lds_v[buf];
-      // ---- S^T = K Q^T
-      f32x16 s[KB][QB];
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) s[kb][qb] = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          const v8 kf = *(const v8*)(kl + swz<D>(kb * 32 + r, ks * 16 + 8 * h));
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) s[kb][qb] = E::mfma32(kf, qf[qb][ks], s[kb][qb]);
-        }
-      }
-      // ---- causal mask (key > query -> -inf) on tiles that reach past the wave's first query
-      if (CAUSAL && k0 + BN - 1 > qw0) {
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-              const int key = k0 + kb * 32 + acc_row(j, h);
-              const int q = qw0 + qb * 32 + r;
-              if (key > q) s[kb][qb][j] = -__builtin_inff();
-            }
-      }
-      // ---- online softmax (log2 domain); P is rounded to 16 bits here and
-      // kept packed as the B operand of the P V product
-      v8 pf[KB][2][QB];
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        float mx = -__builtin_inff();
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[kb][qb][j]);
-        mx = xhalf_max(mx);
-        const float mt = mx * scale_log2;
-        const bool need = mt > m_run[qb] + kRescaleSlack;
-        if (__builtin_amdgcn_ballot_w64(need) != 0) {
-          const float mn = fmaxf(m_run[qb], mt);
-          const float alpha = fast_exp2(m_run[qb] - mn);
-          l_run[qb] *= alpha;
-          lr_run[qb] *= alpha;
-#pragma unroll
-          for (int db = 0; db < DB; ++db) oacc[qb][db] *= alpha;
-          m_run[qb] = mn;
-        }
-        const float neg_m = -m_run[qb];
-        float ls = 0.f, lr = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int kk = 0; kk < 2; ++kk) {
-            float p[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-              p[i] = fast_exp2(fmaf(s[kb][qb][8 * kk + i], scale_log2, neg_m));
-              ls += p[i];
-            }
-            pf[kb][kk][qb] = pack8<E>(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
-            lr = sum8<E>(pf[kb][kk][qb], lr);
-          }
-        l_run[qb] += ls;
-        lr_run[qb] += lr;
-      }
-      // ---- O^T += V^T P^T
+    if (wave_valid && (!CAUSAL || k0 <= q_last)) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const int vrow = kb * 32 + kk * 16 + 4 * h + ((lane & 15) >> 2);
-          const int vcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-#pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            const v4 lo = E::tr_read(vl + swz<D>(vrow, db * 32 + vcol));
-            const v4 hi = E::tr_read(vl + swz<D>(vrow + 8, db * 32 + vcol));
-            const v8 vf = concat44<E>(lo, hi);
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = E::mfma32(vf, pf[kb][kk][qb], oacc[qb][db]);
-          }
-        }
+        const int kbk0 = k0 + kb * 32;
+        if (!CAUSAL || kbk0 <= q_last) key_block(buf, kb, kbk0);
       }
     }
     if (t + 1 < ntiles) lstore(buf ^ 1);
     mfma_drain();
     __syncthreads();
+  };
+  int t = 0;
+  for (; t + 1 < ntiles; t += 2) {
+    k_tile(t, 0);
+    k_tile(t + 1, 1);
   }
+  if (t < ntiles) k_tile(t, 0);
 
   if (!wave_valid) return;
   // ---- epilogue: O = acc / l, lse = (m + log2 l) ln 2
@@ -284,8 +304,8 @@ hipError_t launch_fwd_cfg(const FwdArgs& a) {
 
 template <typename E, int D>
 hipError_t launch_fwd_d(const FwdArgs& a) {
-  if (a.causal) return launch_fwd_cfg<E, D, true, 1, 4, 64>(a);
-  return launch_fwd_cfg<E, D, false, 1, 4, 64>(a);
+  if (a.causal) return launch_fwd_cfg<E, D, true, ATTN_FWD_QB, ATTN_FWD_NW, ATTN_FWD_BN>(a);
+  return launch_fwd_cfg<E, D, false, ATTN_FWD_QB, ATTN_FWD_NW, ATTN_FWD_BN>(a);
 }
 
 }  // namespace
