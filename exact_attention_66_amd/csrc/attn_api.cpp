@@ -73,7 +73,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
 
 size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d) {
   if (checked_elems(B, H, N, d) < 0 || (d != 64 && d != 128)) return 0;
-  return attn::bwd_delta_bytes(B, H, N) + 3 * attn::bwd_tcopy_bytes(B, H, N, d);
+  return 2 * attn::bwd_delta_bytes(B, H, N) + 3 * attn::bwd_tcopy_bytes(B, H, N, d);
 }
 
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
@@ -99,9 +99,9 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
   }
 
   char* ws = (char*)workspace;
-  const size_t t0 = attn::bwd_delta_bytes(B, H, N), tcb = attn::bwd_tcopy_bytes(B, H, N, d);
+  const size_t sb = attn::bwd_delta_bytes(B, H, N), t0 = 2 * sb, tcb = attn::bwd_tcopy_bytes(B, H, N, d);
   attn::BwdArgs a{q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal != 0, dtype,
-                  (float*)ws, ws + t0, ws + t0 + tcb, ws + t0 + 2 * tcb, (hipStream_t)stream};
+                  (float*)ws, (float*)(ws + sb), ws + t0, ws + t0 + tcb, ws + t0 + 2 * tcb, (hipStream_t)stream};
   return launch_status(attn::launch_bwd(a));
 }
 

@@ -39,14 +39,11 @@ namespace {
 
 constexpr float kLog2e = 1.44269504088896340736f;
 
-#ifndef ATTN_DKDV_NW
-#define ATTN_DKDV_NW 4   // waves per workgroup (32 keys each)
+#ifndef ATTN_DKDV_GRID_XCD
+#define ATTN_DKDV_GRID_XCD 1    // workgroup order: xcd_head_major (1) or heavy-first over all heads (0)
 #endif
-#ifndef ATTN_DKDV_BMQ
-#define ATTN_DKDV_BMQ 64  // queries per LDS tile
-#endif
-#ifndef ATTN_DKDV_MINW
-#define ATTN_DKDV_MINW 1  // waves per SIMD the register budget is sized for
+#ifndef ATTN_DQ_GRID_XCD
+#define ATTN_DQ_GRID_XCD 0
 #endif
 #ifndef ATTN_DQ_NW
 #define ATTN_DQ_NW 8      // waves per workgroup (32 queries each)
@@ -74,7 +71,8 @@ __global__ __launch_bounds__(256) void bwd_prep(const typename E::T* __restrict_
                                                 const typename E::T* __restrict__ K,
                                                 const typename E::T* __restrict__ O,
                                                 const typename E::T* __restrict__ dO,
-                                                float* __restrict__ Dvec, typename E::T* __restrict__ QT,
+                                                const float* __restrict__ LSE, float* __restrict__ Dvec,
+                                                float* __restrict__ LSE2, typename E::T* __restrict__ QT,
                                                 typename E::T* __restrict__ KT, typename E::T* __restrict__ dOT,
                                                 int N) {
   using T = typename E::T;
@@ -114,7 +112,11 @@ __global__ __launch_bounds__(256) void bwd_prep(const typename E::T* __restrict_
     for (int i = 0; i < 8; ++i) acc = fmaf((float)ov[i], (float)dov[i], acc);
 #pragma unroll
     for (int off = CPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, CPR);
-    if ((idx % CPR) == 0) Dvec[(size_t)bh * N + row0 + row] = acc;
+    if ((idx % CPR) == 0) {
+      const size_t i = (size_t)bh * N + row0 + row;
+      Dvec[i] = acc;
+      LSE2[i] = LSE[i] * kLog2e;
+    }
   }
   __syncthreads();
 
@@ -137,47 +139,74 @@ __global__ __launch_bounds__(256) void bwd_prep(const typename E::T* __restrict_
 }
 
 // ---------------------------------------------------------------- dK, dV
-// LDS tiles here are read only with ds_read_b128 by 16 lanes of 16
-// consecutive rows at the same column, so plain row padding keeps them free
-// of bank conflicts and their addresses affine (one per-lane base plus
-// immediate offsets): rows of D + 8 elements (D*2 + 16 bytes, 4 banks of
-// shift per row) and, for the transposed tiles, rows of BMQ + 8 elements
-// (BMQ = 64: 144 bytes, 36 banks of shift: 16 distinct 4-bank groups).
+// One workgroup of NW waves per (batch*head, block of 32*NW keys); a wave
+// keeps its 32 keys' K and V as MFMA operands and their dK, dV fp32
+// accumulators for the whole sweep over 64-query tiles.
+//
+// Tiles reach LDS by direct global->LDS copies (no staging registers, no LDS
+// write instructions), double-buffered.  LDS rows are padded so that the
+// 16-lane groups of every ds_read_b128 hit distinct banks and every read
+// address is one per-lane base plus an immediate: row-major Q and dO tiles
+// use rows of D + 8 elements, the transposed Q^T and dO^T tiles rows of
+// 64 + 8.  A copy instruction fills 64 consecutive 16-byte slots, so the
+// padding slot at the end of each row is filled with a duplicate of the
+// row's last chunk, and a tile is a whole number of 64-slot blocks.
+//
+// Each 32-query sub-tile runs as four groups of MFMAs, and every group has
+// the LDS reads or the softmax work of a later group interleaved with it,
+// so that each read has a whole group of MFMAs to arrive in:
+//   X  S = Q K^T          | dO^T fragments (B operands of Z)
+//   Y  dP = dO V^T        | P = exp2(S scale log2e - lse log2e); Q^T fragments (W)
+//   Z  dV += P^T dO       | dS = P (dP - D); next sub-tile's Q fragments (X)
+//   W  dK += dS^T Q       | next sub-tile's dO fragments (Y) and lse, D (Y, Z)
+// (S, dP with one key per lane: P and dS are directly the A operands of the
+// dV and dK products.)  The barrier between tiles sits after Y of the second
+// sub-tile: every read of the tile has then been issued, so the next tile's
+// first reads (Z, W) can already use the other buffer, and the copy of the
+// tile after it starts into the buffer just released.  Tiles that reach the
+// causal diagonal come first and run the same pipeline with the mask applied
+// (sub-tiles entirely above the diagonal come out as P = 0).
 template <typename E, int D, bool CAUSAL, int NW, int BMQ>
-__global__ __launch_bounds__(NW * 64, ATTN_DKDV_MINW) void bwd_dkdv(
+__global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv(
     const typename E::T* __restrict__ Q, const typename E::T* __restrict__ K,
     const typename E::T* __restrict__ V, const typename E::T* __restrict__ dO,
     const typename E::T* __restrict__ QT, const typename E::T* __restrict__ dOT,
-    const float* __restrict__ LSE, const float* __restrict__ Dvec, typename E::T* __restrict__ dK,
+    const float* __restrict__ LSE2, const float* __restrict__ Dvec, typename E::T* __restrict__ dK,
     typename E::T* __restrict__ dV, int BH, int N, int nkb, float scale, float scale_log2) {
   using T = typename E::T;
   using v8 = typename E::v8;
-  constexpr int BN = NW * 32;     // keys per workgroup
-  constexpr int KS = D / 16;      // reduction steps over d
-  constexpr int DB = D / 32;      // 32-wide d blocks
-  constexpr int QSB = BMQ / 32;   // 32-query sub-blocks per tile
-  constexpr int NT = NW * 64;
-  constexpr int CHUNKS = BMQ * D / 8;       // 16-byte chunks per tile
-  constexpr int CPT = (CHUNKS + NT - 1) / NT;  // chunks per thread per tile
-  constexpr int LR = D + 8;       // row-major tile row (elements)
-  constexpr int LT = BMQ + 8;     // transposed tile row (elements)
-  static_assert(CHUNKS % NT == 0 || CHUNKS < NT, "query tile must split evenly over threads");
-  static_assert(BMQ <= NT, "lse/D staging uses one thread per query");
+  static_assert(BMQ == 64, "the pipeline handles two 32-query sub-tiles per tile");
+  static_assert(!CAUSAL || NW * 32 == 2 * BMQ, "causal: exactly two diagonal tiles per workgroup");
+  static_assert((NW & (NW - 1)) == 0, "power-of-two wave count");
+  constexpr int BN = NW * 32;          // keys per workgroup
+  constexpr int KS = D / 16;           // reduction steps over d
+  constexpr int DB = D / 32;           // 32-wide d blocks
+  constexpr int LR = D + 8;            // padded row-major row (elements)
+  constexpr int LT = BMQ + 8;          // padded transposed row (elements)
+  constexpr int RSL = LR / 8;          // 16-byte slots per row-major row
+  constexpr int TSL = LT / 8;          // 16-byte slots per transposed row
+  constexpr int RI = (BMQ * RSL + 63) / 64;  // 64-slot copy blocks per row-major tile
+  constexpr int TI = (D * TSL + 63) / 64;    // 64-slot copy blocks per transposed tile
+  constexpr int RC = (RI + NW - 1) / NW;     // blocks per wave
+  constexpr int TC = (TI + NW - 1) / NW;
+  constexpr int RSZ = RI * 64 * 8;     // elements per row-major tile buffer
+  constexpr int TSZ = TI * 64 * 8;
 
-  __shared__ __attribute__((aligned(16))) T lds_q[2][BMQ * LR];
-  __shared__ __attribute__((aligned(16))) T lds_do[2][BMQ * LR];
-  __shared__ __attribute__((aligned(16))) T lds_qt[2][D * LT];
-  __shared__ __attribute__((aligned(16))) T lds_dot[2][D * LT];
-  __shared__ __attribute__((aligned(16))) float lds_lse[2][BMQ];
-  __shared__ __attribute__((aligned(16))) float lds_dd[2][BMQ];
+  // separate objects per buffer; buffer indices are compile-time constants
+  __shared__ __attribute__((aligned(16))) T lq0[RSZ], lq1[RSZ], ldo0[RSZ], ldo1[RSZ];
+  __shared__ __attribute__((aligned(16))) T lqt0[TSZ], lqt1[TSZ], ldot0[TSZ], ldot1[TSZ];
+  __shared__ __attribute__((aligned(16))) float ll0[64], ll1[64], ld0[64], ld1[64];
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wu = wave_id() & (NW - 1);
   const int h = lane >> 5;
   const int r = lane & 31;
 
   int kblk, bh;
+#if ATTN_DKDV_GRID_XCD
+  // key blocks near the start of a head see the most queries: they come first
+  xcd_head_major((int)blockIdx.x, (int)gridDim.x, nkb, bh, kblk);
+#else
   if (CAUSAL) {  // key blocks near the start see the most queries: run them first
     kblk = (int)(blockIdx.x / BH);
     bh = (int)(blockIdx.x % BH);
@@ -185,15 +214,15 @@ __global__ __launch_bounds__(NW * 64, ATTN_DKDV_MINW) void bwd_dkdv(
     bh = (int)(blockIdx.x / nkb);
     kblk = (int)(blockIdx.x % nkb);
   }
+#endif
   const int kb0 = kblk * BN;
-  const int kw0 = kb0 + w * 32;            // first key of this wave
-  const bool wave_valid = kw0 < N;
+  const int kw0 = kb0 + wu * 32;            // first key of this wave
   const size_t head = (size_t)bh * (size_t)N * D;
   const T* Qh = Q + head;
   const T* dOh = dO + head;
   const T* QTh = QT + head;
   const T* dOTh = dOT + head;
-  const float* lse_h = LSE + (size_t)bh * N;
+  const float* lse_h = LSE2 + (size_t)bh * N;
   const float* dd_h = Dvec + (size_t)bh * N;
 
   // this wave's K and V as B operands: lane holds row kw0 + r, d = 16ks + 8h .. +7
@@ -206,9 +235,9 @@ __global__ __launch_bounds__(NW * 64, ATTN_DKDV_MINW) void bwd_dkdv(
       vB[ks] = *(const v8*)(V + head + (size_t)key * D + ks * 16 + 8 * h);
     }
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      materialize(kB[ks]);
-      materialize(vB[ks]);
+    for (int ks = 0; ks < KS; ++ks) {  // MFMA operands only: keep them in AGPRs
+      asm volatile("" : "+a"(kB[ks]));
+      asm volatile("" : "+a"(vB[ks]));
     }
   }
   f32x16 dk_acc[DB], dv_acc[DB];
@@ -218,163 +247,205 @@ __global__ __launch_bounds__(NW * 64, ATTN_DKDV_MINW) void bwd_dkdv(
     dv_acc[db] = f32x16{};
   }
 
-  // per-lane parts of the LDS read addresses (element offsets); everything
-  // else in an address is a compile-time immediate
+  // per-lane byte offsets of the tile copies, the same for every tile
+  unsigned roff[RC], toff[TC];
+#pragma unroll
+  for (int c = 0; c < RC; ++c) {
+    const int s = 64 * (wu + NW * c) + lane;
+    const int row = min(s / RSL, BMQ - 1);
+    const int col = min(s % RSL, RSL - 2);
+    roff[c] = (unsigned)(row * D + col * 8) * 2u;
+  }
+#pragma unroll
+  for (int c = 0; c < TC; ++c) {
+    const int s = 64 * (wu + NW * c) + lane;
+    const int row = min(s / TSL, D - 1);
+    const int col = min(s % TSL, TSL - 2);
+    toff[c] = ((unsigned)row * (unsigned)N + (unsigned)(col * 8)) * 2u;
+  }
+  auto copy_tile = [&](const int it, auto bufc) {
+    constexpr int b = decltype(bufc)::value;
+    T* const dq_ = b ? lq1 : lq0;
+    T* const ddo = b ? ldo1 : ldo0;
+    T* const dqt = b ? lqt1 : lqt0;
+    T* const ddot = b ? ldot1 : ldot0;
+    const char* gq = (const char*)(Qh + (size_t)it * BMQ * D);
+    const char* gdo = (const char*)(dOh + (size_t)it * BMQ * D);
+    const char* gqt = (const char*)(QTh + (size_t)it * BMQ);
+    const char* gdot = (const char*)(dOTh + (size_t)it * BMQ);
+#pragma unroll
+    for (int c = 0; c < RC; ++c) {
+      const int i = wu + NW * c;
+      if (i < RI) {
+        lds_copy16(gq, roff[c], dq_ + i * 512);
+        lds_copy16(gdo, roff[c], ddo + i * 512);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < TC; ++c) {
+      const int i = wu + NW * c;
+      if (i < TI) {
+        lds_copy16(gqt, toff[c], dqt + i * 512);
+        lds_copy16(gdot, toff[c], ddot + i * 512);
+      }
+    }
+    if (wu == 0) lds_copy4(lse_h + (size_t)it * BMQ, 4u * lane, b ? ll1 : ll0);
+    if (wu == NW - 1) lds_copy4(dd_h + (size_t)it * BMQ, 4u * lane, b ? ld1 : ld0);
+  };
+
+  // per-lane parts of the LDS read addresses (elements); everything else in
+  // an address is a compile-time immediate
   const int offA = opaque(r * LR + 8 * h);      // row-major tiles: row r, column 8h
   const int offB = opaque(r * LT + 8 * h);      // transposed tiles: row r (d), column 8h
-  const int offL = opaque(4 * h);               // lse / D: 4 consecutive queries
+  const int offL = opaque(h);                   // lse / D: 4 consecutive queries (16-byte units)
 
-  const int nqt = N / BMQ;
-  const int it0 = CAUSAL ? kb0 / BMQ : 0;
-
-  v8 qreg[CPT], doreg[CPT], qtreg[CPT], dotreg[CPT];
-  float lse_reg = 0.f, d_reg = 0.f;
-  auto gload = [&](int it) {
-    const int qt0 = it * BMQ;
+  auto read_q = [&](auto bufc, const int qs, v8 (&qa)[KS]) {
+    const T* ql = (decltype(bufc)::value ? lq1 : lq0) + offA + qs * 32 * LR;
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int idx = tid + c * NT;
-      if (idx >= CHUNKS) break;
-      const int row = idx / (D / 8);           // row-major tile: query, d chunk
-      const int col = (idx % (D / 8)) * 8;
-      qreg[c] = *(const v8*)(Qh + (size_t)(qt0 + row) * D + col);
-      doreg[c] = *(const v8*)(dOh + (size_t)(qt0 + row) * D + col);
-      const int trow = idx / (BMQ / 8);        // transposed tile: d, token chunk
-      const int tcol = (idx % (BMQ / 8)) * 8;
-      qtreg[c] = *(const v8*)(QTh + (size_t)trow * N + qt0 + tcol);
-      dotreg[c] = *(const v8*)(dOTh + (size_t)trow * N + qt0 + tcol);
-    }
-    if (tid < BMQ) {
-      lse_reg = lse_h[qt0 + tid];
-      d_reg = dd_h[qt0 + tid];
+    for (int ks = 0; ks < KS; ++ks) qa[ks] = *(const v8*)(ql + ks * 16);
+  };
+  auto read_do = [&](auto bufc, const int qs, v8 (&da)[KS]) {
+    const T* dol = (decltype(bufc)::value ? ldo1 : ldo0) + offA + qs * 32 * LR;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) da[ks] = *(const v8*)(dol + ks * 16);
+  };
+  auto read_stats = [&](auto bufc, const int qs, f32x4 (&l4)[4], f32x4 (&d4)[4]) {
+    constexpr int b = decltype(bufc)::value;
+    const f32x4* lp = (const f32x4*)(b ? ll1 : ll0) + offL;
+    const f32x4* dp = (const f32x4*)(b ? ld1 : ld0) + offL;
+#pragma unroll
+    for (int jg = 0; jg < 4; ++jg) {
+      l4[jg] = lp[qs * 8 + 2 * jg];
+      d4[jg] = dp[qs * 8 + 2 * jg];
     }
   };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int idx = tid + c * NT;
-      if (idx >= CHUNKS) break;
-      const int row = idx / (D / 8);
-      const int col = (idx % (D / 8)) * 8;
-      *(v8*)(&lds_q[buf][row * LR + col]) = qreg[c];
-      *(v8*)(&lds_do[buf][row * LR + col]) = doreg[c];
-      const int trow = idx / (BMQ / 8);
-      const int tcol = (idx % (BMQ / 8)) * 8;
-      *(v8*)(&lds_qt[buf][trow * LT + tcol]) = qtreg[c];
-      *(v8*)(&lds_dot[buf][trow * LT + tcol]) = dotreg[c];
-    }
-    if (tid < BMQ) {
-      lds_lse[buf][tid] = lse_reg * kLog2e;
-      lds_dd[buf][tid] = d_reg;
-    }
-  };
-
-  // one 32-query sub-block: S, dP, softmax, dV, dK
-  auto sub_tile = [&](const int buf, const int qs, const int qs0) {
-    const T* ql = lds_q[buf] + offA + qs * 32 * LR;
-    const T* dol = lds_do[buf] + offA + qs * 32 * LR;
-    const T* qtl = lds_qt[buf] + offB + qs * 32;
-    const T* dotl = lds_dot[buf] + offB + qs * 32;
-    // every LDS read of the S/dP operands is issued before their MFMAs
-    v8 qa[KS], da[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      qa[ks] = *(const v8*)(ql + ks * 16);
-      da[ks] = *(const v8*)(dol + ks * 16);
-    }
-    sched_fence();
-    // S = Q K^T and dP = dO V^T: lane holds key kw0 + r, queries acc_row(j, h)
-    f32x16 sacc = f32x16{}, dpacc = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      sacc = E::mfma32(qa[ks], kB[ks], sacc);
-      dpacc = E::mfma32(da[ks], vB[ks], dpacc);
-    }
-    sched_fence();
-    // operands of the dV / dK products and the row statistics: their reads
-    // do not depend on the softmax, so their latency hides behind it
-    v8 dob[2][DB], qbv[2][DB];
+  // B operands of dV (dO^T) or dK (Q^T): row 32db + r of the transposed tile, 8 queries in slot order
+  auto read_t = [&](const T* tl, const int qs, v8 (&x)[2][DB]) {
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        dob[kk][db] = *(const v8*)(dotl + db * 32 * LT + 16 * kk);
-        qbv[kk][db] = *(const v8*)(qtl + db * 32 * LT + 16 * kk);
-      }
-    f32x4 l4[4], d4[4];
+      for (int db = 0; db < DB; ++db) x[kk][db] = *(const v8*)(tl + offB + qs * 32 + db * 32 * LT + 16 * kk);
+  };
+
+  const int nqt = N / BMQ;
+  const int it0 = CAUSAL ? kb0 / BMQ : 0;   // earlier tiles lie entirely above the diagonal
+  const int ntile = nqt - it0;              // visited in order it0, it0 + 1, ...; the first two are on the diagonal
+  const int nmask = CAUSAL ? min(2, ntile) : 0;
+
+  // operands of the sub-tile about to start, read one group ahead
+  v8 qa[KS], da[KS];
+  f32x4 l4[4], d4[4];
+
+  copy_tile(it0, std::integral_constant<int, 0>{});
+  wait_all_vmem_loads();
+  __syncthreads();
+  read_q(std::integral_constant<int, 0>{}, 0, qa);
+  read_do(std::integral_constant<int, 0>{}, 0, da);
+  read_stats(std::integral_constant<int, 0>{}, 0, l4, d4);
+  if (ntile > 1) copy_tile(it0 + 1, std::integral_constant<int, 1>{});
+
+  auto sub_tile = [&](const int it, auto maskc, auto bufc, auto qsc) {
+    constexpr int b = decltype(bufc)::value;
+    constexpr int qs = decltype(qsc)::value;
+    // where the next sub-tile's operands live
+    using NB = std::integral_constant<int, qs == 0 ? b : (b ^ 1)>;
+    constexpr int nqs = qs ^ 1;
+    const int qs0 = it * BMQ + qs * 32;
+
+    // X: S = Q K^T | dO^T fragments
+    v8 dob[2][DB];
+    read_t(b ? ldot1 : ldot0, qs, dob);
+    f32x16 sacc = f32x16{};
 #pragma unroll
-    for (int jg = 0; jg < 4; ++jg) {
-      l4[jg] = *(const f32x4*)(&lds_lse[buf][offL + qs * 32 + 8 * jg]);
-      d4[jg] = *(const f32x4*)(&lds_dd[buf][offL + qs * 32 + 8 * jg]);
-    }
+    for (int ks = 0; ks < KS; ++ks) sacc = E::mfma32(qa[ks], kB[ks], sacc);
+    sched_interleave<KS, kSchedMfma, 1, kSchedDsRead, 2 * DB / KS>();
     sched_fence();
-    float p[16], ds[16];
+
+    // Y: dP = dO V^T | P, Q^T fragments
+    v8 qbv[2][DB];
+    read_t(b ? lqt1 : lqt0, qs, qbv);
+    f32x16 dpacc = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) dpacc = E::mfma32(da[ks], vB[ks], dpacc);
+    float p[16];
 #pragma unroll
     for (int jg = 0; jg < 4; ++jg)
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int j = 4 * jg + u;
-        p[j] = fast_exp2(fmaf(sacc[j], scale_log2, -l4[jg][u]));
-      }
-    if (CAUSAL && qs0 < kw0 + 31) {   // sub-block crosses the diagonal: key > query -> P = 0
+      for (int u = 0; u < 4; ++u) p[4 * jg + u] = fast_exp2(fmaf(sacc[4 * jg + u], scale_log2, -l4[jg][u]));
+    if constexpr (decltype(maskc)::value) {  // key > query -> P = 0
 #pragma unroll
       for (int j = 0; j < 16; ++j)
         if (kw0 + r > qs0 + acc_row(j, h)) p[j] = 0.f;
     }
+    v8 pa[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+      pa[kk] = pack8<E>(p[8 * kk + 0], p[8 * kk + 1], p[8 * kk + 2], p[8 * kk + 3], p[8 * kk + 4], p[8 * kk + 5],
+                        p[8 * kk + 6], p[8 * kk + 7]);
+    sched_interleave<KS, kSchedMfma, 1, kSchedDsRead, 2 * DB / KS, kSchedValu, 6>();
+    sched_fence();
+
+    if constexpr (qs == 1) {
+      // every read of this tile is issued: wait for the next tile's copy,
+      // meet the other waves, then refill this buffer
+      mfma_drain();
+      wait_all_vmem_loads();
+      __syncthreads();
+      if (it + 2 < nqt) copy_tile(it + 2, bufc);
+      sched_fence();
+    }
+
+    // Z: dV += P^T dO | dS, next Q fragments (stale but harmless after the last tile)
+    read_q(NB{}, nqs, qa);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) dv_acc[db] = E::mfma32(pa[kk], dob[kk][db], dv_acc[db]);
+    float ds[16];
 #pragma unroll
     for (int jg = 0; jg < 4; ++jg)
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int j = 4 * jg + u;
-        ds[j] = p[j] * (dpacc[j] - d4[jg][u]);
-      }
-    // dV += P^T dO and dK += dS^T Q (scale applied at the end)
+      for (int u = 0; u < 4; ++u) ds[4 * jg + u] = p[4 * jg + u] * (dpacc[4 * jg + u] - d4[jg][u]);
+    v8 sa[2];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const v8 pa = pack8<E>(p[8 * kk + 0], p[8 * kk + 1], p[8 * kk + 2], p[8 * kk + 3], p[8 * kk + 4],
-                             p[8 * kk + 5], p[8 * kk + 6], p[8 * kk + 7]);
-      const v8 sa = pack8<E>(ds[8 * kk + 0], ds[8 * kk + 1], ds[8 * kk + 2], ds[8 * kk + 3], ds[8 * kk + 4],
-                             ds[8 * kk + 5], ds[8 * kk + 6], ds[8 * kk + 7]);
+    for (int kk = 0; kk < 2; ++kk)
+      sa[kk] = pack8<E>(ds[8 * kk + 0], ds[8 * kk + 1], ds[8 * kk + 2], ds[8 * kk + 3], ds[8 * kk + 4],
+                        ds[8 * kk + 5], ds[8 * kk + 6], ds[8 * kk + 7]);
+    sched_interleave<2 * DB, kSchedMfma, 1, kSchedDsRead, KS / (2 * DB), kSchedValu, 5>();
+    sched_fence();
+
+    // W: dK += dS^T Q | next dO fragments and statistics
+    read_do(NB{}, nqs, da);
+    read_stats(NB{}, nqs, l4, d4);
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        dv_acc[db] = E::mfma32(pa, dob[kk][db], dv_acc[db]);
-        dk_acc[db] = E::mfma32(sa, qbv[kk][db], dk_acc[db]);
-      }
-    }
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) dk_acc[db] = E::mfma32(sa[kk], qbv[kk][db], dk_acc[db]);
+    sched_interleave<2 * DB, kSchedMfma, 1, kSchedDsRead, (KS + 8) / (2 * DB)>();
+    sched_fence();
+  };
+  auto tile = [&](const int it, auto maskc, auto bufc) {
+    sub_tile(it, maskc, bufc, std::integral_constant<int, 0>{});
+    sub_tile(it, maskc, bufc, std::integral_constant<int, 1>{});
   };
 
-  if (it0 < nqt) {
-    gload(it0);
-    lstore(it0 & 1);
-  }
-  wait_all_vmem_loads();
-  __syncthreads();
-
-  auto q_tile = [&](const int it, const int buf) {
-    const int qt0 = it * BMQ;
-    if (it + 1 < nqt) gload(it + 1);
-#pragma unroll
-    for (int qs = 0; qs < QSB; ++qs) {
-      const int qs0 = qt0 + qs * 32;
-      if (wave_valid && (!CAUSAL || qs0 + 31 >= kw0)) sub_tile(buf, qs, qs0);
-    }
-    if (it + 1 < nqt) lstore(buf ^ 1);
-    mfma_drain();
-    __syncthreads();
-  };
-  // unrolled by two so that the LDS buffer index is a compile-time constant
+  // tiles it0 .. nqt-1 on buffers 0, 1, 0, ...; the diagonal ones first
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  using MaskOn = std::integral_constant<bool, true>;
+  using MaskOff = std::integral_constant<bool, false>;
   int it = it0;
-  if (it < nqt && (it & 1)) {
-    q_tile(it, 1);
-    ++it;
-  }
+  if (nmask > 0) tile(it++, MaskOn{}, B0{});
+  if (nmask > 1) tile(it++, MaskOn{}, B1{});
+  // nmask is 0 or 2 unless a single tile remains, so the unmasked tiles start on buffer 0
   for (; it + 1 < nqt; it += 2) {
-    q_tile(it, 0);
-    q_tile(it + 1, 1);
+    tile(it, MaskOff{}, B0{});
+    tile(it + 1, MaskOff{}, B1{});
   }
-  if (it < nqt) q_tile(it, 0);
+  if (it < nqt) tile(it, MaskOff{}, B0{});
+  mfma_drain();
 
-  if (!wave_valid) return;
+  if (kw0 >= N) return;
   // epilogue: dK = scale * acc, dV = acc; lane holds key kw0 + acc_row(j, h), d = 32db + r
 #pragma unroll
   for (int db = 0; db < DB; ++db)
@@ -419,6 +490,10 @@ __global__ __launch_bounds__(NW * 64, ATTN_DQ_MINW) void bwd_dq(
   const int r = lane & 31;
 
   int qblk, bh;
+#if ATTN_DQ_GRID_XCD
+  xcd_head_major((int)blockIdx.x, (int)gridDim.x, nqb, bh, qblk);
+  if (CAUSAL) qblk = nqb - 1 - qblk;  // heaviest query blocks of a head first
+#else
   if (CAUSAL) {  // heaviest query blocks first
     qblk = nqb - 1 - (int)(blockIdx.x / BH);
     bh = (int)(blockIdx.x % BH);
@@ -426,6 +501,7 @@ __global__ __launch_bounds__(NW * 64, ATTN_DQ_MINW) void bwd_dq(
     bh = (int)(blockIdx.x / nqb);
     qblk = (int)(blockIdx.x % nqb);
   }
+#endif
   const int q0 = qblk * BM;
   const int qw0 = q0 + w * 32;
   const bool wave_valid = qw0 < N;
@@ -597,8 +673,7 @@ __global__ __launch_bounds__(NW * 64, ATTN_DQ_MINW) void bwd_dq(
 
 template <typename E, int D, bool CAUSAL>
 hipError_t launch_bwd_cfg(const BwdArgs& a) {
-  constexpr int NWK = ATTN_DKDV_NW;
-  constexpr int BMQ = ATTN_DKDV_BMQ;
+  constexpr int NWK = 4;            // dK/dV: waves per workgroup (32 keys each)
   constexpr int NWQ = ATTN_DQ_NW;
   constexpr int BNQ = ATTN_DQ_BN;
   const int BH = (int)(a.B * a.H);
@@ -614,6 +689,7 @@ hipError_t launch_bwd_cfg(const BwdArgs& a) {
   T* dk = (T*)a.dk;
   T* dv = (T*)a.dv;
   float* delta = a.delta;
+  float* lse2 = a.lse2;
   T* qt = (T*)a.qt;
   T* kt = (T*)a.kt;
   T* dot = (T*)a.dot;
@@ -621,18 +697,18 @@ hipError_t launch_bwd_cfg(const BwdArgs& a) {
   float scale_log2 = a.scale * kLog2e;
 
   {
-    void* args[] = {(void*)&q, (void*)&k, (void*)&o, (void*)&dO, (void*)&delta, (void*)&qt, (void*)&kt,
-                    (void*)&dot, (void*)&N};
+    void* args[] = {(void*)&q, (void*)&k, (void*)&o, (void*)&dO, (void*)&lse, (void*)&delta, (void*)&lse2,
+                    (void*)&qt, (void*)&kt, (void*)&dot, (void*)&N};
     hipError_t e = launch_kernel((const void*)bwd_prep<E, D>, dim3((unsigned)(BH * (N / 64))), dim3(256), args,
                                  a.stream, 1);
     if (e != hipSuccess) return e;
   }
   {
     const int nkb = (N + NWK * 32 - 1) / (NWK * 32);
-    void* args[] = {(void*)&q, (void*)&k, (void*)&v, (void*)&dO, (void*)&qt, (void*)&dot, (void*)&lse,
+    void* args[] = {(void*)&q, (void*)&k, (void*)&v, (void*)&dO, (void*)&qt, (void*)&dot, (void*)&lse2,
                     (void*)&delta, (void*)&dk, (void*)&dv, (void*)&BH, (void*)&N, (void*)&nkb,
                     (void*)&scale, (void*)&scale_log2};
-    hipError_t e = launch_kernel((const void*)bwd_dkdv<E, D, CAUSAL, NWK, BMQ>, dim3((unsigned)(nkb * BH)),
+    hipError_t e = launch_kernel((const void*)bwd_dkdv<E, D, CAUSAL, NWK, 64>, dim3((unsigned)(nkb * BH)),
                                  dim3(NWK * 64), args, a.stream, 2);
     if (e != hipSuccess) return e;
   }

@@ -144,6 +144,72 @@ __device__ __forceinline__ void mfma_drain() {
 // that all reads are in flight at once instead of one pair at a time.
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
+// Instruction classes of __builtin_amdgcn_sched_group_barrier.
+enum : int {
+  kSchedValu = 0x002 | 0x400,  // vector ALU, transcendental included
+  kSchedMfma = 0x008,
+  kSchedDsRead = 0x100,
+};
+
+// Ask the scheduler for REP repetitions of the group sequence
+// (N1 of class M1, N2 of class M2, N3 of class M3) in the current scheduling
+// region, e.g. one MFMA, then two LDS reads, then four VALU, 16 times over.
+template <int REP, int M1, int N1, int M2 = 0, int N2 = 0, int M3 = 0, int N3 = 0>
+__device__ __forceinline__ void sched_interleave() {
+  if constexpr (REP > 0) {
+    __builtin_amdgcn_sched_group_barrier(M1, N1, 0);
+    if constexpr (N2 > 0) __builtin_amdgcn_sched_group_barrier(M2, N2, 0);
+    if constexpr (N3 > 0) __builtin_amdgcn_sched_group_barrier(M3, N3, 0);
+    sched_interleave<REP - 1, M1, N1, M2, N2, M3, N3>();
+  }
+}
+
+// Direct global -> LDS copy (gfx950 global_load_lds_dwordx4 / _dword): lane
+// l's 16 (4) bytes from gbase + voff (its own byte offset) land at
+// lds_base + 16 l (4 l); gbase and lds_base are the same for the whole wave
+// (scalar registers).  Completion is counted by vmcnt like an ordinary load.
+// Issued as inline asm so that the compiler does not track the LDS write
+// itself: its wait insertion cannot tell a copy into one buffer from reads
+// of the other and would wait for every copy right after issuing it.  The
+// kernels wait for their copies explicitly (wait_all_vmem_loads) before the
+// barrier that publishes a buffer.  No other code in these kernels uses m0.
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>((ATTN_LDS const void*)p);
+}
+__device__ __forceinline__ void lds_copy16(const void* gbase, uint32_t voff, const void* lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(lds_address(lds_base)), "v"(voff), "s"(gbase)
+               : "memory");
+}
+__device__ __forceinline__ void lds_copy4(const void* gbase, uint32_t voff, const void* lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2"
+               :
+               : "s"(lds_address(lds_base)), "v"(voff), "s"(gbase)
+               : "memory");
+}
+
+// Workgroup order for kernels whose workgroups of one (batch, head) read the
+// same tiles of that head: the dispatcher deals consecutive workgroup
+// indices to the 8 XCDs in turn (index b runs on XCD b % 8, each XCD with
+// its own L2), so index b is mapped to a head-major position L such that
+// each XCD works through one contiguous range of L: the blocks of one head
+// then share one L2 and run at about the same time, and the heads in flight
+// at any moment are few (their tiles fit in the caches) instead of all.
+// T is the grid size; returns (head, block) with block in [0, nblk).
+__device__ __forceinline__ void xcd_head_major(int b, int T, int nblk, int& bh, int& blk) {
+  constexpr int X = 8;
+  const int x = b % X, p = b / X;
+  const int C = T / X, rem = T % X;  // XCD x receives C + (x < rem) workgroups
+  const int L = x * C + min(x, rem) + p;
+  bh = L / nblk;
+  blk = L % nblk;
+}
+
+// The wave index as a wave-uniform (scalar) value, so that branches on it
+// are scalar branches.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
+
 // 8 fp32 -> 8 16-bit values (round to nearest even) packed as an MFMA operand.
 template <typename E>
 __device__ __forceinline__ typename E::v8 pack8(float a0, float a1, float a2, float a3,

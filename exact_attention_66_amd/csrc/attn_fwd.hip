@@ -47,6 +47,9 @@ constexpr float kRescaleSlack = 8.0f;
 #ifndef ATTN_FWD_MINW
 #define ATTN_FWD_MINW 2  // waves per SIMD the register budget is sized for
 #endif
+#ifndef ATTN_FWD_GRID_XCD
+#define ATTN_FWD_GRID_XCD 0  // workgroup order: xcd_head_major (1) or heavy-first over all heads (0)
+#endif
 
 // LDS tiles: K [BN][D + 8] is read with ds_read_b128 by 16 lanes of 16
 // consecutive rows (rows 4 banks apart: conflict free); V [BN][D + 32] is read
@@ -84,6 +87,10 @@ __global__ __launch_bounds__(NW * 64, ATTN_FWD_MINW) void fwd_kernel(const typen
   const int r = lane & 31;
 
   int qblk, bh;
+#if ATTN_FWD_GRID_XCD
+  xcd_head_major((int)blockIdx.x, (int)gridDim.x, nqb, bh, qblk);
+  if (CAUSAL) qblk = nqb - 1 - qblk;  // heaviest query blocks of a head first
+#else
   if (CAUSAL) {  // heaviest query blocks first, across all heads
     qblk = nqb - 1 - (int)(blockIdx.x / BH);
     bh = (int)(blockIdx.x % BH);
@@ -91,6 +98,7 @@ __global__ __launch_bounds__(NW * 64, ATTN_FWD_MINW) void fwd_kernel(const typen
     bh = (int)(blockIdx.x / nqb);
     qblk = (int)(blockIdx.x % nqb);
   }
+#endif
   const int q0 = qblk * BM;
   const int qw0 = q0 + w * 32 * QB;
   const bool wave_valid = qw0 < N;

@@ -37,6 +37,7 @@ struct BwdArgs {
   int dtype;
   // workspace parts
   float* delta;   // [B,H,N] fp32: D_i = dO_i . O_i
+  float* lse2;    // [B,H,N] fp32: lse_i * log2(e)
   void* qt;       // [B,H,d,N] 16-bit: Q transposed (tokens in slot order per 16)
   void* kt;       // [B,H,d,N] 16-bit: K transposed
   void* dot;      // [B,H,d,N] 16-bit: dO transposed
@@ -50,8 +51,8 @@ hipError_t launch_kernel(const void* fn, dim3 grid, dim3 block, void** args, hip
 hipError_t launch_fwd(const FwdArgs& a);
 hipError_t launch_bwd(const BwdArgs& a);
 
-// Workspace split used by attn_bwd: delta, then Q^T, K^T, dO^T, each part
-// starting on a 256-byte boundary.
+// Workspace split used by attn_bwd: delta, lse2, then Q^T, K^T, dO^T, each
+// part starting on a 256-byte boundary.
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 inline size_t bwd_delta_bytes(int64_t B, int64_t H, int64_t N) { return align256((size_t)(B * H * N) * 4); }
 inline size_t bwd_tcopy_bytes(int64_t B, int64_t H, int64_t N, int64_t d) { return align256((size_t)(B * H * N * d) * 2); }

@@ -49,11 +49,12 @@ def test_status_strings(lib):
 
 
 def test_workspace_bytes():
-    # delta [B,H,N] fp32 + three 16-bit [B,H,d,N] transposed copies, each padded to 256 bytes
-    assert ea.attn_bwd_workspace_bytes(1, 1, 64, 64) == 256 + 3 * 64 * 64 * 2
-    assert ea.attn_bwd_workspace_bytes(4, 32, 4096, 128) == 4 * 32 * 4096 * 4 + 3 * 4 * 32 * 4096 * 128 * 2
+    # D and log2-scaled lse, [B,H,N] fp32 each, + three 16-bit [B,H,d,N] transposed copies,
+    # each part padded to 256 bytes
+    assert ea.attn_bwd_workspace_bytes(1, 1, 64, 64) == 2 * 256 + 3 * 64 * 64 * 2
+    assert ea.attn_bwd_workspace_bytes(4, 32, 4096, 128) == 2 * 4 * 32 * 4096 * 4 + 3 * 4 * 32 * 4096 * 128 * 2
     n = 32768
-    assert ea.attn_bwd_workspace_bytes(1, 16, n, 128) < 16 * n * (4 + 6 * 128) + 1024  # O(N d), never N^2
+    assert ea.attn_bwd_workspace_bytes(1, 16, n, 128) < 16 * n * (8 + 6 * 128) + 1024  # O(N d), never N^2
     for bad in [(0, 1, 64, 64), (1, 0, 64, 64), (1, 1, 0, 64), (1, 1, 64, 96), (1, 1, 64, -1),
                 (1 << 40, 1 << 20, 1 << 20, 128)]:
         assert ea.attn_bwd_workspace_bytes(*bad) == 0, bad
