@@ -458,7 +458,15 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv(
 }
 
 // ---------------------------------------------------------------- dQ
-// Same padding rule as above: K and V tiles [BN][D + 8], K^T tile [D][BN + 8].
+// Shaped like the forward: each wave keeps 32 queries' Q and dO rows as B
+// operands and dQ^T in accumulators, computes S^T = K Q^T and dP^T = V dO^T
+// (one query per lane: lse and D are per-lane scalars), and adds
+// dQ^T += K^T dS^T (A operands from the K^T tile).  K, V [BN][D + 8] and
+// K^T [D][BN + 8] tiles (padded rows: conflict-free ds_read_b128, affine
+// addresses) reach LDS by direct global->LDS copies into three rotating
+// buffers, two tiles ahead of their use; a copy instruction fills 64
+// consecutive 16-byte slots, so the padding slot of each row gets a
+// duplicate of the row's last chunk and a tile is a whole number of blocks.
 template <typename E, int D, bool CAUSAL, int NW, int BN>
 __global__ __launch_bounds__(NW * 64, ATTN_DQ_MINW) void bwd_dq(
     const typename E::T* __restrict__ Q, const typename E::T* __restrict__ K,
@@ -472,20 +480,25 @@ __global__ __launch_bounds__(NW * 64, ATTN_DQ_MINW) void bwd_dq(
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
   constexpr int KB = BN / 32;        // 32-key blocks per tile
-  constexpr int NT = NW * 64;
-  constexpr int CHUNKS = BN * D / 8;
-  constexpr int CPT = (CHUNKS + NT - 1) / NT;
-  constexpr int LR = D + 8;
-  constexpr int LT = BN + 8;
-  static_assert(CHUNKS % NT == 0 || CHUNKS < NT, "key tile must split evenly over threads");
+  constexpr int LR = D + 8;          // padded K / V row (elements)
+  constexpr int LT = BN + 8;         // padded K^T row (elements)
+  constexpr int RSL = LR / 8;        // 16-byte slots per K / V row
+  constexpr int TSL = LT / 8;        // 16-byte slots per K^T row
+  constexpr int RI = (BN * RSL + 63) / 64;   // 64-slot copy blocks per K or V tile
+  constexpr int TI = (D * TSL + 63) / 64;    // per K^T tile
+  constexpr int RC = (RI + NW - 1) / NW;
+  constexpr int TC = (TI + NW - 1) / NW;
+  constexpr int RSZ = RI * 64 * 8;   // elements per K or V tile buffer
+  constexpr int TSZ = TI * 64 * 8;
+  constexpr int NBUF = 3;            // tile t in buffer t % 3, copied two tiles ahead
+  static_assert(BN == 64, "K^T rows of 64 keys");
 
-  __shared__ __attribute__((aligned(16))) T lds_k[2][BN * LR];
-  __shared__ __attribute__((aligned(16))) T lds_v[2][BN * LR];
-  __shared__ __attribute__((aligned(16))) T lds_kt[2][D * LT];
+  __shared__ __attribute__((aligned(16))) T lds_k[NBUF][RSZ];
+  __shared__ __attribute__((aligned(16))) T lds_v[NBUF][RSZ];
+  __shared__ __attribute__((aligned(16))) T lds_kt[NBUF][TSZ];
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wu = wave_id() & (NW - 1);
   const int h = lane >> 5;
   const int r = lane & 31;
 
@@ -503,7 +516,7 @@ __global__ __launch_bounds__(NW * 64, ATTN_DQ_MINW) void bwd_dq(
   }
 #endif
   const int q0 = qblk * BM;
-  const int qw0 = q0 + w * 32;
+  const int qw0 = q0 + wu * 32;
   const bool wave_valid = qw0 < N;
   const size_t head = (size_t)bh * (size_t)N * D;
   const T* Kh = K + head;
@@ -539,34 +552,56 @@ __global__ __launch_bounds__(NW * 64, ATTN_DQ_MINW) void bwd_dq(
   const int ntiles = (kv_end + BN - 1) / BN;
   const int q_last = qw0 + 31;
 
-  v8 kreg[CPT], vreg[CPT], ktreg[CPT];
-  auto gload = [&](int t) {
+  // ---- tile copies: per-lane byte offsets, the same for every tile
+  unsigned roff[RC], toff[TC];
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int idx = tid + c * NT;
-      if (idx >= CHUNKS) break;
-      const int row = idx / (D / 8);
-      const int col = (idx % (D / 8)) * 8;
-      const int key = min(t * BN + row, N - 1);
-      kreg[c] = *(const v8*)(Kh + (size_t)key * D + col);
-      vreg[c] = *(const v8*)(Vh + (size_t)key * D + col);
-      const int trow = idx / (BN / 8);
-      const int tcol = (idx % (BN / 8)) * 8;
-      ktreg[c] = *(const v8*)(KTh + (size_t)trow * N + min(t * BN + tcol, N - 8));
-    }
+  for (int c = 0; c < RC; ++c) {
+    const int sl = 64 * (wu + NW * c) + lane;
+    const int row = min(sl / RSL, BN - 1);
+    const int col = min(sl % RSL, D / 8 - 1);
+    roff[c] = (unsigned)(row * D + col * 8) * 2u;
+  }
+#pragma unroll
+  for (int c = 0; c < TC; ++c) {
+    const int sl = 64 * (wu + NW * c) + lane;
+    const int row = min(sl / TSL, D - 1);
+    const int col = min(sl % TSL, BN / 8 - 1);
+    toff[c] = ((unsigned)row * (unsigned)N + (unsigned)(col * 8)) * 2u;
+  }
+  auto copy_tile = [&](const int t, const int b) {
+    const char* gk = (const char*)(Kh + (size_t)t * BN * D);
+    const char* gv = (const char*)(Vh + (size_t)t * BN * D);
+    const char* gkt = (const char*)(KTh + (size_t)t * BN);
+#pragma unroll
+    for (int c = 0; c < RC; ++c)
+      if (wu + NW * c < RI) {
+        lds_copy16(gk, roff[c], &lds_k[b][(wu + NW * c) * 512]);
+        lds_copy16(gv, roff[c], &lds_v[b][(wu + NW * c) * 512]);
+      }
+#pragma unroll
+    for (int c = 0; c < TC; ++c)
+      if (wu + NW * c < TI) lds_copy16(gkt, toff[c], &lds_kt[b][(wu + NW * c) * 512]);
   };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int idx = tid + c * NT;
-      if (idx >= CHUNKS) break;
-      const int row = idx / (D / 8);
-      const int col = (idx % (D / 8)) * 8;
-      *(v8*)(&lds_k[buf][row * LR + col]) = kreg[c];
-      *(v8*)(&lds_v[buf][row * LR + col]) = vreg[c];
-      const int trow = idx / (BN / 8);
-      const int tcol = (idx % (BN / 8)) * 8;
-      *(v8*)(&lds_kt[buf][trow * LT + tcol]) = ktreg[c];
+  // Wait until at most one tile's copies (the most recent) are outstanding:
+  // vmcnt counts this wave's copies in issue order.
+  auto wait_copies_but_last = [&]() {
+    constexpr auto cnt = [](int w) {
+      int n = 0;
+      for (int c = 0; c < RC; ++c) n += 2 * (w + NW * c < RI);
+      for (int c = 0; c < TC; ++c) n += (w + NW * c < TI);
+      return n;
+    };
+    static_assert(2 * RC + TC < 16, "vmcnt immediate");
+    static_assert(NW == 8, "one case per wave");
+    switch (wu) {
+      case 0: __builtin_amdgcn_s_waitcnt(0x0F70 | cnt(0)); break;
+      case 1: __builtin_amdgcn_s_waitcnt(0x0F70 | cnt(1)); break;
+      case 2: __builtin_amdgcn_s_waitcnt(0x0F70 | cnt(2)); break;
+      case 3: __builtin_amdgcn_s_waitcnt(0x0F70 | cnt(3)); break;
+      case 4: __builtin_amdgcn_s_waitcnt(0x0F70 | cnt(4)); break;
+      case 5: __builtin_amdgcn_s_waitcnt(0x0F70 | cnt(5)); break;
+      case 6: __builtin_amdgcn_s_waitcnt(0x0F70 | cnt(6)); break;
+      default: __builtin_amdgcn_s_waitcnt(0x0F70 | cnt(7)); break;
     }
   };
 
@@ -629,13 +664,15 @@ __global__ __launch_bounds__(NW * 64, ATTN_DQ_MINW) void bwd_dq(
     }
   };
 
-  gload(0);
-  lstore(0);
+  copy_tile(0, 0);
+  if (ntiles > 1) copy_tile(1, 1);
   wait_all_vmem_loads();
   __syncthreads();
 
-  auto k_tile = [&](const int t, const int buf) {
-    if (t + 1 < ntiles) gload(t + 1);
+  auto k_tile = [&](const int t, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
+    // buffer (t + 2) % 3 held tile t - 1, which every wave has finished
+    if (t + 2 < ntiles) copy_tile(t + 2, (buf + 2) % NBUF);
     const int k0 = t * BN;
     if (wave_valid && (!CAUSAL || k0 <= q_last)) {
 #pragma unroll
@@ -644,16 +681,23 @@ __global__ __launch_bounds__(NW * 64, ATTN_DQ_MINW) void bwd_dq(
         if (!CAUSAL || kbk0 <= q_last) key_block(buf, kb, kbk0);
       }
     }
-    if (t + 1 < ntiles) lstore(buf ^ 1);
     mfma_drain();
+    // tile t + 1 must be in LDS: its copies are the ones before the most recent
+    if (t + 2 < ntiles) wait_copies_but_last();
+    else wait_all_vmem_loads();
     __syncthreads();
   };
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  using B2 = std::integral_constant<int, 2>;
   int t = 0;
-  for (; t + 1 < ntiles; t += 2) {
-    k_tile(t, 0);
-    k_tile(t + 1, 1);
+  for (; t + 2 < ntiles; t += 3) {
+    k_tile(t, B0{});
+    k_tile(t + 1, B1{});
+    k_tile(t + 2, B2{});
   }
-  if (t < ntiles) k_tile(t, 0);
+  if (t < ntiles) k_tile(t, B0{});
+  if (t + 1 < ntiles) k_tile(t + 1, B1{});
 
   if (!wave_valid) return;
   // epilogue: dQ = scale * dQ^T; lane holds query qw0 + r, d = 32db + acc_row(j, h)

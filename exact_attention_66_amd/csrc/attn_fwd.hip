@@ -17,8 +17,9 @@
 //  * the S^T accumulator, converted to 16-bit, is directly the B operand of
 //    O^T += V^T P^T (keys relabelled per slot_key), and V^T comes from LDS
 //    with ds_read_b64_tr_b16, so P never leaves registers;
-//  * K/V tiles are double-buffered in LDS, the next tile's global loads are
-//    issued before the current tile's math;
+//  * K/V tiles reach LDS by direct global->LDS copies into three rotating
+//    buffers, two tiles ahead of their use (no staging registers, no LDS
+//    write instructions);
 //  * exponentials use exp2 with scale*log2(e) folded into one FMA, and the
 //    O rescale is skipped while the running max grows by less than 2^8
 //    (exact: the same stale max is used for O, l and lse);
@@ -42,7 +43,7 @@ constexpr float kRescaleSlack = 8.0f;
 #define ATTN_FWD_NW 8    // waves per workgroup
 #endif
 #ifndef ATTN_FWD_BN
-#define ATTN_FWD_BN 64   // keys per LDS tile
+#define ATTN_FWD_BN 0    // keys per LDS tile; 0: 128 for d = 128 (two buffers), 64 for d = 64 (three)
 #endif
 #ifndef ATTN_FWD_MINW
 #define ATTN_FWD_MINW 2  // waves per SIMD the register budget is sized for
@@ -72,15 +73,23 @@ __global__ __launch_bounds__(NW * 64, ATTN_FWD_MINW) void fwd_kernel(const typen
   constexpr int KB = BN / 32;        // 32-key blocks per tile
   constexpr int LK = D + 8;          // K tile row (elements)
   constexpr int LV = D + 32;         // V tile row (elements)
-  constexpr int NT = NW * 64;
-  constexpr int CHUNKS = BN * D / 8;          // 16-byte chunks per tile and tensor
-  constexpr int CPT = (CHUNKS + NT - 1) / NT;
-  static_assert(CHUNKS % NT == 0 || CHUNKS < NT, "tile must split evenly over threads");
+  constexpr int KSL = LK / 8;        // 16-byte slots per K row (D/8 data + padding)
+  constexpr int VSL = LV / 8;        // 16-byte slots per V row
+  constexpr int KI = (BN * KSL + 63) / 64;   // 64-slot copy blocks per K tile
+  constexpr int VI = (BN * VSL + 63) / 64;   // 64-slot copy blocks per V tile
+  constexpr int KC = (KI + NW - 1) / NW;     // blocks per wave (upper bound)
+  constexpr int VC = (VI + NW - 1) / NW;
+  constexpr int KSZ = KI * 64 * 8;           // elements per K tile buffer
+  constexpr int VSZ = VI * 64 * 8;
+  // tile t in buffer t % NBUF: 64-key tiles in three buffers, copied two
+  // tiles ahead; 128-key tiles in two, copied one tile ahead
+  constexpr int NBUF = BN == 64 ? 3 : 2;
 
-  __shared__ __attribute__((aligned(16))) T lds_k[2][BN * LK];
-  __shared__ __attribute__((aligned(16))) T lds_v[2][BN * LV];
+  __shared__ __attribute__((aligned(16))) T lds_k[NBUF][KSZ];
+  __shared__ __attribute__((aligned(16))) T lds_v[NBUF][VSZ];
 
   const int tid = threadIdx.x;
+  (void)tid;
   const int lane = tid & 63;
   const int w = tid >> 6;
   const int h = lane >> 5;
@@ -143,28 +152,63 @@ __global__ __launch_bounds__(NW * 64, ATTN_FWD_MINW) void fwd_kernel(const typen
   const int ntiles = (kv_end + BN - 1) / BN;
   const int q_last = qw0 + 32 * QB - 1;
 
-  v8 kreg[CPT], vreg[CPT];
-  auto gload = [&](int t) {
+  // Tiles reach LDS by direct global->LDS copies: a copy instruction fills
+  // 64 consecutive 16-byte slots, so the padding slots at the end of each
+  // row get duplicates of the row's last chunk and a tile is a whole number
+  // of 64-slot blocks.  Per-lane byte offsets are the same for every tile.
+  const int wu = wave_id() & (NW - 1);
+  unsigned koff[KC], voff[VC];
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int idx = tid + c * NT;
-      if (idx >= CHUNKS) break;
-      const int row = idx / (D / 8);
-      const int col = (idx % (D / 8)) * 8;
-      const int key = min(t * BN + row, N - 1);
-      kreg[c] = *(const v8*)(Kh + (size_t)key * D + col);
-      vreg[c] = *(const v8*)(Vh + (size_t)key * D + col);
-    }
+  for (int c = 0; c < KC; ++c) {
+    const int sl = 64 * (wu + NW * c) + lane;
+    const int row = min(sl / KSL, BN - 1);
+    const int col = min(sl % KSL, D / 8 - 1);
+    koff[c] = (unsigned)(row * D + col * 8) * 2u;
+  }
+#pragma unroll
+  for (int c = 0; c < VC; ++c) {
+    const int sl = 64 * (wu + NW * c) + lane;
+    const int row = min(sl / VSL, BN - 1);
+    const int col = min(sl % VSL, D / 8 - 1);
+    voff[c] = (unsigned)(row * D + col * 8) * 2u;
+  }
+  // A tile past the end of the sequence (N is a multiple of 64, so only a
+  // 128-key tile can be cut) holds 64 keys: exactly the first half of its
+  // copy blocks, since 64 rows of either layout fill whole 64-slot blocks.
+  static_assert((64 * KSL) % 64 == 0 && (64 * VSL) % 64 == 0, "half tiles are whole blocks");
+  auto copy_tile = [&](const int t, const int b) {
+    const char* gk = (const char*)(Kh + (size_t)t * BN * D);
+    const char* gv = (const char*)(Vh + (size_t)t * BN * D);
+    const bool half = t * BN + BN > N;
+    const int ki = half ? 64 * KSL / 64 : KI;
+    const int vi = half ? 64 * VSL / 64 : VI;
+#pragma unroll
+    for (int c = 0; c < KC; ++c)
+      if (wu + NW * c < ki) lds_copy16(gk, koff[c], &lds_k[b][(wu + NW * c) * 512]);
+#pragma unroll
+    for (int c = 0; c < VC; ++c)
+      if (wu + NW * c < vi) lds_copy16(gv, voff[c], &lds_v[b][(wu + NW * c) * 512]);
   };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int idx = tid + c * NT;
-      if (idx >= CHUNKS) break;
-      const int row = idx / (D / 8);
-      const int col = (idx % (D / 8)) * 8;
-      *(v8*)(&lds_k[buf][row * LK + col]) = kreg[c];
-      *(v8*)(&lds_v[buf][row * LV + col]) = vreg[c];
+  // Wait until at most one tile's copies (the most recent) are outstanding:
+  // vmcnt counts this wave's copies in issue order.
+  auto wait_copies_but_last = [&]() {
+    constexpr auto cnt = [](int w) {
+      int n = 0;
+      for (int c = 0; c < KC; ++c) n += (w + NW * c < KI);
+      for (int c = 0; c < VC; ++c) n += (w + NW * c < VI);
+      return n;
+    };
+    static_assert(NBUF == 2 || KC + VC < 16, "vmcnt immediate");
+    static_assert(NW == 8, "one case per wave");
+    switch (wu) {
+      case 0: __builtin_amdgcn_s_waitcnt(0x0F70 | cnt(0)); break;
+      case 1: __builtin_amdgcn_s_waitcnt(0x0F70 | cnt(1)); break;
+      case 2: __builtin_amdgcn_s_waitcnt(0x0F70 | cnt(2)); break;
+      case 3: __builtin_amdgcn_s_waitcnt(0x0F70 | cnt(3)); break;
+      case 4: __builtin_amdgcn_s_waitcnt(0x0F70 | cnt(4)); break;
+      case 5: __builtin_amdgcn_s_waitcnt(0x0F70 | cnt(5)); break;
+      case 6: __builtin_amdgcn_s_waitcnt(0x0F70 | cnt(6)); break;
+      default: __builtin_amdgcn_s_waitcnt(0x0F70 | cnt(7)); break;
     }
   };
 
@@ -243,31 +287,49 @@ __global__ __launch_bounds__(NW * 64, ATTN_FWD_MINW) void fwd_kernel(const typen
     }
   };
 
-  gload(0);
-  lstore(0);
+  copy_tile(0, 0);
+  if (NBUF == 3 && ntiles > 1) copy_tile(1, 1);
   wait_all_vmem_loads();
   __syncthreads();
 
-  auto k_tile = [&](const int t, const int buf) {
-    if (t + 1 < ntiles) gload(t + 1);
+  constexpr int AHEAD = NBUF - 1;   // tiles between a copy and its use
+  auto k_tile = [&](const int t, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
+    // buffer (t + AHEAD) % NBUF held tile t - 1, which every wave has finished
+    if (t + AHEAD < ntiles) copy_tile(t + AHEAD, (buf + AHEAD) % NBUF);
     const int k0 = t * BN;
     if (wave_valid && (!CAUSAL || k0 <= q_last)) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         const int kbk0 = k0 + kb * 32;
-        if (!CAUSAL || kbk0 <= q_last) key_block(buf, kb, kbk0);
+        if ((!CAUSAL || kbk0 <= q_last) && kbk0 < N) key_block(buf, kb, kbk0);
       }
     }
-    if (t + 1 < ntiles) lstore(buf ^ 1);
     mfma_drain();
+    // tile t + 1 must be in LDS: with three buffers its copies are the ones
+    // before the most recent, with two they are the most recent
+    if (NBUF == 3 && t + 2 < ntiles) wait_copies_but_last();
+    else wait_all_vmem_loads();
     __syncthreads();
   };
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  using B2 = std::integral_constant<int, NBUF == 3 ? 2 : 0>;
   int t = 0;
-  for (; t + 1 < ntiles; t += 2) {
-    k_tile(t, 0);
-    k_tile(t + 1, 1);
+  if constexpr (NBUF == 3) {
+    for (; t + 2 < ntiles; t += 3) {
+      k_tile(t, B0{});
+      k_tile(t + 1, B1{});
+      k_tile(t + 2, B2{});
+    }
+  } else {
+    for (; t + 1 < ntiles; t += 2) {
+      k_tile(t, B0{});
+      k_tile(t + 1, B1{});
+    }
   }
-  if (t < ntiles) k_tile(t, 0);
+  if (t < ntiles) k_tile(t, B0{});
+  if (NBUF == 3 && t + 1 < ntiles) k_tile(t + 1, B1{});
 
   if (!wave_valid) return;
   // ---- epilogue: O = acc / l, lse = (m + log2 l) ln 2
@@ -312,8 +374,9 @@ hipError_t launch_fwd_cfg(const FwdArgs& a) {
 
 template <typename E, int D>
 hipError_t launch_fwd_d(const FwdArgs& a) {
-  if (a.causal) return launch_fwd_cfg<E, D, true, ATTN_FWD_QB, ATTN_FWD_NW, ATTN_FWD_BN>(a);
-  return launch_fwd_cfg<E, D, false, ATTN_FWD_QB, ATTN_FWD_NW, ATTN_FWD_BN>(a);
+  constexpr int BN = ATTN_FWD_BN ? ATTN_FWD_BN : (D == 128 ? 128 : 64);
+  if (a.causal) return launch_fwd_cfg<E, D, true, ATTN_FWD_QB, ATTN_FWD_NW, BN>(a);
+  return launch_fwd_cfg<E, D, false, ATTN_FWD_QB, ATTN_FWD_NW, BN>(a);
 }
 
 }  // namespace
