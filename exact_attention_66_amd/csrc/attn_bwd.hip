@@ -12,8 +12,8 @@
 // Three kernels on the caller's stream, no atomics anywhere (every output
 // element is written by exactly one lane, so all of dQ, dK, dV are bitwise
 // reproducible):
-//  1. bwd_prep: D_i = dO_i . O_i (fp32), and transposed copies Q^T, dO^T,
-//     K^T ([B*H][d][N]) in the workspace.  Inside every group of 16 tokens
+//  1. bwd_prep: -D_i = -dO_i . O_i and -lse_i log2(e) (fp32), and transposed
+//     copies Q^T, dO^T, K^T ([B*H][d][N]) in the workspace.  Inside every group of 16 tokens
 //     the copies store tokens in MFMA reduction-slot order (slot_key), so
 //     each operand fragment the main kernels need is one contiguous 16-byte
 //     LDS read; the LDS transpose reads happen once here instead of once per
@@ -30,6 +30,14 @@
 //     lane: lse and D are per-lane scalars), and adds dQ^T += K^T dS^T.
 // The price of (3) is recomputing S and dP once more (7 matrix products in
 // total instead of 5); in exchange there is no cross-workgroup reduction.
+//
+// Softmax arithmetic folded into the products: (2) and (3) scale their
+// register-resident K (resp. Q) operand by scale log2(e) once, and start the
+// S and dP accumulators at -lse log2(e) and -D instead of zero, so the MFMAs
+// deliver scale S log2(e) - lse log2(e) and dP - D directly: per score only
+// P = exp2(acc) and dS = P acc remain.  This file is compiled with MFMA
+// results in VGPRs (the softmax reads them without copies out of AGPRs); the
+// operands read from LDS are steered into AGPRs instead (in_agpr).
 #include "attn_device.h"
 #include "attn_launch.h"
 
@@ -114,8 +122,8 @@ __global__ __launch_bounds__(256) void bwd_prep(const typename E::T* __restrict_
     for (int off = CPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, CPR);
     if ((idx % CPR) == 0) {
       const size_t i = (size_t)bh * N + row0 + row;
-      Dvec[i] = acc;
-      LSE2[i] = LSE[i] * kLog2e;
+      Dvec[i] = -acc;
+      LSE2[i] = -LSE[i] * kLog2e;
     }
   }
   __syncthreads();
@@ -155,9 +163,9 @@ __global__ __launch_bounds__(256) void bwd_prep(const typename E::T* __restrict_
 // Each 32-query sub-tile runs as four groups of MFMAs, and every group has
 // the LDS reads or the softmax work of a later group interleaved with it,
 // so that each read has a whole group of MFMAs to arrive in:
-//   X  S = Q K^T          | dO^T fragments (B operands of Z)
-//   Y  dP = dO V^T        | P = exp2(S scale log2e - lse log2e); Q^T fragments (W)
-//   Z  dV += P^T dO       | dS = P (dP - D); next sub-tile's Q fragments (X)
+//   X  S' = -lse log2e + Q (scale log2e K)^T   | dO^T fragments (B operands of Z)
+//   Y  dP' = -D + dO V^T  | P = exp2(S'); Q^T fragments (W)
+//   Z  dV += P^T dO       | dS = P dP'; next sub-tile's Q fragments (X)
 //   W  dK += dS^T Q       | next sub-tile's dO fragments (Y) and lse, D (Y, Z)
 // (S, dP with one key per lane: P and dS are directly the A operands of the
 // dV and dK products.)  The barrier between tiles sits after Y of the second
@@ -225,13 +233,14 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv(
   const float* lse_h = LSE2 + (size_t)bh * N;
   const float* dd_h = Dvec + (size_t)bh * N;
 
-  // this wave's K and V as B operands: lane holds row kw0 + r, d = 16ks + 8h .. +7
+  // this wave's K (times scale log2e) and V as B operands: lane holds row
+  // kw0 + r, d = 16ks + 8h .. +7
   v8 kB[KS], vB[KS];
   {
     const int key = min(kw0 + r, N - 1);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      kB[ks] = *(const v8*)(K + head + (size_t)key * D + ks * 16 + 8 * h);
+      kB[ks] = scaled8<E>(*(const v8*)(K + head + (size_t)key * D + ks * 16 + 8 * h), scale_log2);
       vB[ks] = *(const v8*)(V + head + (size_t)key * D + ks * 16 + 8 * h);
     }
 #pragma unroll
@@ -355,23 +364,28 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv(
     // X: S = Q K^T | dO^T fragments
     v8 dob[2][DB];
     read_t(b ? ldot1 : ldot0, qs, dob);
-    f32x16 sacc = f32x16{};
+    f32x16 sacc = join16(l4);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) sacc = E::mfma32(qa[ks], kB[ks], sacc);
+    for (int ks = 0; ks < KS; ++ks) {
+      in_agpr(qa[ks]);
+      sacc = E::mfma32(qa[ks], kB[ks], sacc);
+    }
     sched_interleave<KS, kSchedMfma, 1, kSchedDsRead, 2 * DB / KS>();
-    sched_fence();
+    // (no fence: X and Y form one scheduling region, so the group patterns
+    // place the whole S chain first and the exponentials between dP MFMAs)
 
     // Y: dP = dO V^T | P, Q^T fragments
     v8 qbv[2][DB];
     read_t(b ? lqt1 : lqt0, qs, qbv);
-    f32x16 dpacc = f32x16{};
+    f32x16 dpacc = join16(d4);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) dpacc = E::mfma32(da[ks], vB[ks], dpacc);
+    for (int ks = 0; ks < KS; ++ks) {
+      in_agpr(da[ks]);
+      dpacc = E::mfma32(da[ks], vB[ks], dpacc);
+    }
     float p[16];
 #pragma unroll
-    for (int jg = 0; jg < 4; ++jg)
-#pragma unroll
-      for (int u = 0; u < 4; ++u) p[4 * jg + u] = fast_exp2(fmaf(sacc[4 * jg + u], scale_log2, -l4[jg][u]));
+    for (int j = 0; j < 16; ++j) p[j] = fast_exp2(sacc[j]);
     if constexpr (decltype(maskc)::value) {  // key > query -> P = 0
 #pragma unroll
       for (int j = 0; j < 16; ++j)
@@ -382,7 +396,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv(
     for (int kk = 0; kk < 2; ++kk)
       pa[kk] = pack8<E>(p[8 * kk + 0], p[8 * kk + 1], p[8 * kk + 2], p[8 * kk + 3], p[8 * kk + 4], p[8 * kk + 5],
                         p[8 * kk + 6], p[8 * kk + 7]);
-    sched_interleave<KS, kSchedMfma, 1, kSchedDsRead, 2 * DB / KS, kSchedValu, 6>();
+    sched_interleave<KS, kSchedMfma, 1, kSchedDsRead, 2 * DB / KS, kSchedValu, 3>();
     sched_fence();
 
     if constexpr (qs == 1) {
@@ -400,18 +414,19 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv(
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-      for (int db = 0; db < DB; ++db) dv_acc[db] = E::mfma32(pa[kk], dob[kk][db], dv_acc[db]);
+      for (int db = 0; db < DB; ++db) {
+        in_agpr(dob[kk][db]);
+        dv_acc[db] = E::mfma32(pa[kk], dob[kk][db], dv_acc[db]);
+      }
     float ds[16];
 #pragma unroll
-    for (int jg = 0; jg < 4; ++jg)
-#pragma unroll
-      for (int u = 0; u < 4; ++u) ds[4 * jg + u] = p[4 * jg + u] * (dpacc[4 * jg + u] - d4[jg][u]);
+    for (int j = 0; j < 16; ++j) ds[j] = p[j] * dpacc[j];
     v8 sa[2];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
       sa[kk] = pack8<E>(ds[8 * kk + 0], ds[8 * kk + 1], ds[8 * kk + 2], ds[8 * kk + 3], ds[8 * kk + 4],
                         ds[8 * kk + 5], ds[8 * kk + 6], ds[8 * kk + 7]);
-    sched_interleave<2 * DB, kSchedMfma, 1, kSchedDsRead, KS / (2 * DB), kSchedValu, 5>();
+    sched_interleave<2 * DB, kSchedMfma, 1, kSchedDsRead, KS / (2 * DB), kSchedValu, 3>();
     sched_fence();
 
     // W: dK += dS^T Q | next dO fragments and statistics
@@ -420,7 +435,10 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv(
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-      for (int db = 0; db < DB; ++db) dk_acc[db] = E::mfma32(sa[kk], qbv[kk][db], dk_acc[db]);
+      for (int db = 0; db < DB; ++db) {
+        in_agpr(qbv[kk][db]);
+        dk_acc[db] = E::mfma32(sa[kk], qbv[kk][db], dk_acc[db]);
+      }
     sched_interleave<2 * DB, kSchedMfma, 1, kSchedDsRead, (KS + 8) / (2 * DB)>();
     sched_fence();
   };
@@ -458,8 +476,8 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv(
 }
 
 // ---------------------------------------------------------------- dQ
-// Shaped like the forward: each wave keeps 32 queries' Q and dO rows as B
-// operands and dQ^T in accumulators, computes S^T = K Q^T and dP^T = V dO^T
+// Shaped like the forward: each wave keeps 32 queries' Q (times scale log2e)
+// and dO rows as B operands and dQ^T in accumulators, computes S^T = K Q^T and dP^T = V dO^T
 // (one query per lane: lse and D are per-lane scalars), and adds
 // dQ^T += K^T dS^T (A operands from the K^T tile).  K, V [BN][D + 8] and
 // K^T [D][BN + 8] tiles (padded rows: conflict-free ds_read_b128, affine
@@ -471,7 +489,7 @@ template <typename E, int D, bool CAUSAL, int NW, int BN>
 __global__ __launch_bounds__(NW * 64, ATTN_DQ_MINW) void bwd_dq(
     const typename E::T* __restrict__ Q, const typename E::T* __restrict__ K,
     const typename E::T* __restrict__ V, const typename E::T* __restrict__ dO,
-    const typename E::T* __restrict__ KT, const float* __restrict__ LSE, const float* __restrict__ Dvec,
+    const typename E::T* __restrict__ KT, const float* __restrict__ NLSE2, const float* __restrict__ ND,
     typename E::T* __restrict__ dQ, int BH, int N, int nqb, float scale, float scale_log2) {
   using T = typename E::T;
   using v8 = typename E::v8;
@@ -528,18 +546,23 @@ __global__ __launch_bounds__(NW * 64, ATTN_DQ_MINW) void bwd_dq(
   v8 qf[KS], dof[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    qf[ks] = *(const v8*)(Q + head + (size_t)qrow * D + ks * 16 + 8 * h);
+    qf[ks] = scaled8<E>(*(const v8*)(Q + head + (size_t)qrow * D + ks * 16 + 8 * h), scale_log2);
     dof[ks] = *(const v8*)(dO + head + (size_t)qrow * D + ks * 16 + 8 * h);
   }
-  const float lse2 = LSE[(size_t)bh * N + qrow] * kLog2e;
-  const float dd = Dvec[(size_t)bh * N + qrow];
+  // accumulator starting values: -lse log2e for S^T, -D for dP^T (one query per lane)
+  const float nlse2 = NLSE2[(size_t)bh * N + qrow];
+  const float ndd = ND[(size_t)bh * N + qrow];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     materialize(qf[ks]);
     materialize(dof[ks]);
   }
-  materialize(lse2);
-  materialize(dd);
+  f32x16 s_init, dp_init;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    s_init[j] = nlse2;
+    dp_init[j] = ndd;
+  }
 
   f32x16 acc[DB];
 #pragma unroll
@@ -612,7 +635,7 @@ __global__ __launch_bounds__(NW * 64, ATTN_DQ_MINW) void bwd_dq(
     // S^T = K Q^T, dP^T = V dO^T: lane holds query qw0 + r, keys acc_row(j, h).
     // Operand reads go in batches of KSTAGE per operand, each batch issued
     // ahead of its MFMAs.
-    f32x16 sacc = f32x16{}, dpacc = f32x16{};
+    f32x16 sacc = s_init, dpacc = dp_init;
     constexpr int KH = ATTN_DQ_KSTAGE < KS ? ATTN_DQ_KSTAGE : KS;
 #pragma unroll
     for (int part = 0; part < KS / KH; ++part) {
@@ -639,14 +662,14 @@ __global__ __launch_bounds__(NW * 64, ATTN_DQ_MINW) void bwd_dq(
 #endif
     float ds[16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) ds[j] = fast_exp2(fmaf(sacc[j], scale_log2, -lse2));
+    for (int j = 0; j < 16; ++j) ds[j] = fast_exp2(sacc[j]);
     if (CAUSAL && kbk0 + 31 > qw0) {   // block crosses the diagonal: key > query -> P = 0
 #pragma unroll
       for (int j = 0; j < 16; ++j)
         if (kbk0 + acc_row(j, h) > qw0 + r) ds[j] = 0.f;
     }
 #pragma unroll
-    for (int j = 0; j < 16; ++j) ds[j] = ds[j] * (dpacc[j] - dd);
+    for (int j = 0; j < 16; ++j) ds[j] = ds[j] * dpacc[j];
     // dQ^T += K^T dS^T: A from the K^T tile (row d, 8 keys in slot order)
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
@@ -758,7 +781,7 @@ hipError_t launch_bwd_cfg(const BwdArgs& a) {
   }
   {
     const int nqb = (N + NWQ * 32 - 1) / (NWQ * 32);
-    void* args[] = {(void*)&q, (void*)&k, (void*)&v, (void*)&dO, (void*)&kt, (void*)&lse, (void*)&delta,
+    void* args[] = {(void*)&q, (void*)&k, (void*)&v, (void*)&dO, (void*)&kt, (void*)&lse2, (void*)&delta,
                     (void*)&dq, (void*)&BH, (void*)&N, (void*)&nqb, (void*)&scale, (void*)&scale_log2};
     return launch_kernel((const void*)bwd_dq<E, D, CAUSAL, NWQ, BNQ>, dim3((unsigned)(nqb * BH)), dim3(NWQ * 64),
                          args, a.stream, 3);

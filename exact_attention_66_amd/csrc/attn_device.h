@@ -104,6 +104,25 @@ __device__ __forceinline__ float xhalf_sum(float x) {
   return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
+// Ask the register allocator to keep an MFMA A/B operand in AGPRs (LDS reads
+// can write AGPRs and MFMAs can read them).  A non-volatile asm statement is
+// only a data dependence: it orders nothing else and forces no earlier wait
+// than the MFMA that uses the operand.
+template <typename V>
+__device__ __forceinline__ void in_agpr(V& x) {
+  asm("" : "+a"(x));
+}
+
+// Four f32x4 (accumulator rows 4jg .. 4jg+3) as one MFMA accumulator.
+__device__ __forceinline__ f32x16 join16(const f32x4 (&x)[4]) {
+  f32x16 r;
+#pragma unroll
+  for (int jg = 0; jg < 4; ++jg)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) r[4 * jg + u] = x[jg][u];
+  return r;
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Wait for every outstanding vector-memory load of this wave (vmcnt = 0,
@@ -218,6 +237,13 @@ __device__ __forceinline__ typename E::v8 pack8(float a0, float a1, float a2, fl
   r[0] = (typename E::T)a0; r[1] = (typename E::T)a1; r[2] = (typename E::T)a2; r[3] = (typename E::T)a3;
   r[4] = (typename E::T)a4; r[5] = (typename E::T)a5; r[6] = (typename E::T)a6; r[7] = (typename E::T)a7;
   return r;
+}
+
+// Eight operand elements times c, rounded back to the element type.
+template <typename E>
+__device__ __forceinline__ typename E::v8 scaled8(typename E::v8 x, float c) {
+  return pack8<E>((float)x[0] * c, (float)x[1] * c, (float)x[2] * c, (float)x[3] * c, (float)x[4] * c,
+                  (float)x[5] * c, (float)x[6] * c, (float)x[7] * c);
 }
 
 // acc + sum of the 8 packed 16-bit values (exact products by 1.0, fp32 sums).

@@ -36,8 +36,8 @@ struct BwdArgs {
   bool causal;
   int dtype;
   // workspace parts
-  float* delta;   // [B,H,N] fp32: D_i = dO_i . O_i
-  float* lse2;    // [B,H,N] fp32: lse_i * log2(e)
+  float* delta;   // [B,H,N] fp32: -D_i = -dO_i . O_i
+  float* lse2;    // [B,H,N] fp32: -lse_i * log2(e)
   void* qt;       // [B,H,d,N] 16-bit: Q transposed (tokens in slot order per 16)
   void* kt;       // [B,H,d,N] 16-bit: K transposed
   void* dot;      // [B,H,d,N] 16-bit: dO transposed

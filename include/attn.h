@@ -84,7 +84,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 
 /*
  * attn_bwd_workspace_bytes - size of the scratch buffer attn_bwd needs:
- * two fp32 per query row (D_i = dO_i . O_i and lse_i * log2(e)) plus three
+ * two fp32 per query row (-D_i = -dO_i . O_i and -lse_i * log2(e)) plus three
  * 16-bit [B,H,d,N] transposed copies of Q, K and dO, each part rounded up to
  * 256 bytes: 8*B*H*N + 6*B*H*N*d bytes.  It grows as O(B*H*N*d), never with N^2 (the
  * memory bound of page "突破单卡显存极限…" §2.2).  Returns 0 when the sizes
