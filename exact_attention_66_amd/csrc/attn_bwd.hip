@@ -18,9 +18,10 @@
 //     each operand fragment the main kernels need is one contiguous 16-byte
 //     LDS read; the LDS transpose reads happen once here instead of once per
 //     wave per tile.
-//  2. bwd_dkdv: one workgroup per (batch*head, block of 32*NW keys).  Each
-//     wave keeps its 32 keys' K and V as MFMA operands and their dK, dV fp32
-//     accumulators for the whole sweep over query tiles.  S = Q K^T and
+//  2. bwd_dkdv: a persistent grid; each workgroup runs a list of units
+//     (batch*head, block of 32*NW keys).  Each wave keeps its 32 keys' K and
+//     V as MFMA operands and their dK, dV fp32 accumulators for the whole
+//     sweep over query tiles.  S = Q K^T and
 //     dP = dO V^T put one key per lane, so P and dS are directly the A
 //     operands of dV += P^T dO and dK += dS^T Q (B operands from the
 //     transposed tiles).
@@ -47,9 +48,6 @@ namespace {
 
 constexpr float kLog2e = 1.44269504088896340736f;
 
-#ifndef ATTN_DKDV_GRID_XCD
-#define ATTN_DKDV_GRID_XCD 1    // workgroup order: xcd_head_major (1) or heavy-first over all heads (0)
-#endif
 #ifndef ATTN_DQ_GRID_XCD
 #define ATTN_DQ_GRID_XCD 0
 #endif
@@ -147,12 +145,17 @@ __global__ __launch_bounds__(256) void bwd_prep(const typename E::T* __restrict_
 }
 
 // ---------------------------------------------------------------- dK, dV
-// One workgroup of NW waves per (batch*head, block of 32*NW keys); a wave
+// A persistent grid of NW-wave workgroups, as many as fit on the device; each
+// runs its share of the units (batch*head, block of 32*NW keys) one after
+// another (xcd_snake_unit), which saves the launch gap between workgroups
+// and lets the next unit's first loads overlap this unit's stores.  A wave
 // keeps its 32 keys' K and V as MFMA operands and their dK, dV fp32
 // accumulators for the whole sweep over 64-query tiles.
 //
 // Tiles reach LDS by direct global->LDS copies (no staging registers, no LDS
-// write instructions), double-buffered.  LDS rows are padded so that the
+// write instructions), double-buffered; a tile's copies go out in four
+// parts spread over four MFMA groups (a wave that issues a whole tile's
+// copies at once stalls on its full memory queue).  LDS rows are padded so that the
 // 16-lane groups of every ds_read_b128 hit distinct banks and every read
 // address is one per-lane base plus an immediate: row-major Q and dO tiles
 // use rows of D + 8 elements, the transposed Q^T and dO^T tiles rows of
@@ -166,7 +169,7 @@ __global__ __launch_bounds__(256) void bwd_prep(const typename E::T* __restrict_
 //   X  S' = -lse log2e + Q (scale log2e K)^T   | dO^T fragments (B operands of Z)
 //   Y  dP' = -D + dO V^T  | P = exp2(S'); Q^T fragments (W)
 //   Z  dV += P^T dO       | dS = P dP'; next sub-tile's Q fragments (X)
-//   W  dK += dS^T Q       | next sub-tile's dO fragments (Y) and lse, D (Y, Z)
+//   W  dK += dS^T Q       | next sub-tile's dO fragments (Y) and lse, D (X, Y)
 // (S, dP with one key per lane: P and dS are directly the A operands of the
 // dV and dK products.)  The barrier between tiles sits after Y of the second
 // sub-tile: every read of the tile has then been issued, so the next tile's
@@ -210,45 +213,35 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv(
   const int h = lane >> 5;
   const int r = lane & 31;
 
-  int kblk, bh;
-#if ATTN_DKDV_GRID_XCD
-  // key blocks near the start of a head see the most queries: they come first
-  xcd_head_major((int)blockIdx.x, (int)gridDim.x, nkb, bh, kblk);
-#else
-  if (CAUSAL) {  // key blocks near the start see the most queries: run them first
-    kblk = (int)(blockIdx.x / BH);
-    bh = (int)(blockIdx.x % BH);
-  } else {
-    bh = (int)(blockIdx.x / nkb);
-    kblk = (int)(blockIdx.x % nkb);
-  }
-#endif
-  const int kb0 = kblk * BN;
-  const int kw0 = kb0 + wu * 32;            // first key of this wave
-  const size_t head = (size_t)bh * (size_t)N * D;
-  const T* Qh = Q + head;
-  const T* dOh = dO + head;
-  const T* QTh = QT + head;
-  const T* dOTh = dOT + head;
-  const float* lse_h = LSE2 + (size_t)bh * N;
-  const float* dd_h = Dvec + (size_t)bh * N;
+  // Persistent grid: the workgroup runs its units (batch*head, block of BN
+  // keys; xcd_snake_unit) one after another.  The next unit's first tile
+  // copy and K, V loads are issued before this unit's dK, dV stores, so the
+  // stores and both load latencies overlap.
+  int round = 0;
+  int unit = xcd_snake_unit((int)blockIdx.x, (int)gridDim.x, BH * nkb, 0);
+  if (unit < 0) return;
+  const int nqt = N / BMQ;
+  int kb0, kw0, it0, ntile, nmask;
+  size_t head;
+  const T *Qh, *dOh, *QTh, *dOTh;
+  const float *lse_h, *dd_h;
+  auto set_unit = [&](const int u) {
+    const int bh = u / nkb;
+    kb0 = (u % nkb) * BN;
+    kw0 = kb0 + wu * 32;                 // first key of this wave
+    head = (size_t)bh * (size_t)N * D;
+    Qh = Q + head;
+    dOh = dO + head;
+    QTh = QT + head;
+    dOTh = dOT + head;
+    lse_h = LSE2 + (size_t)bh * N;
+    dd_h = Dvec + (size_t)bh * N;
+    it0 = CAUSAL ? kb0 / BMQ : 0;        // earlier tiles lie entirely above the diagonal
+    ntile = nqt - it0;                   // visited in order it0, it0 + 1, ...; the first two are on the diagonal
+    nmask = CAUSAL ? min(2, ntile) : 0;
+  };
+  set_unit(unit);
 
-  // this wave's K (times scale log2e) and V as B operands: lane holds row
-  // kw0 + r, d = 16ks + 8h .. +7
-  v8 kB[KS], vB[KS];
-  {
-    const int key = min(kw0 + r, N - 1);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      kB[ks] = scaled8<E>(*(const v8*)(K + head + (size_t)key * D + ks * 16 + 8 * h), scale_log2);
-      vB[ks] = *(const v8*)(V + head + (size_t)key * D + ks * 16 + 8 * h);
-    }
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {  // MFMA operands only: keep them in AGPRs
-      asm volatile("" : "+a"(kB[ks]));
-      asm volatile("" : "+a"(vB[ks]));
-    }
-  }
   f32x16 dk_acc[DB], dv_acc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
@@ -272,34 +265,39 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv(
     const int col = min(s % TSL, TSL - 2);
     toff[c] = ((unsigned)row * (unsigned)N + (unsigned)(col * 8)) * 2u;
   }
-  auto copy_tile = [&](const int it, auto bufc) {
+  // A tile's copies in four parts (Q, dO, Q^T, dO^T with the statistics),
+  // so that they can be spread over the MFMA groups instead of filling the
+  // wave's memory queue at once.
+  auto copy_part = [&](const int it, auto bufc, auto partc) {
     constexpr int b = decltype(bufc)::value;
-    T* const dq_ = b ? lq1 : lq0;
-    T* const ddo = b ? ldo1 : ldo0;
-    T* const dqt = b ? lqt1 : lqt0;
-    T* const ddot = b ? ldot1 : ldot0;
-    const char* gq = (const char*)(Qh + (size_t)it * BMQ * D);
-    const char* gdo = (const char*)(dOh + (size_t)it * BMQ * D);
-    const char* gqt = (const char*)(QTh + (size_t)it * BMQ);
-    const char* gdot = (const char*)(dOTh + (size_t)it * BMQ);
+    constexpr int part = decltype(partc)::value;
+    if constexpr (part < 2) {
+      T* const dst = part == 0 ? (b ? lq1 : lq0) : (b ? ldo1 : ldo0);
+      const char* g = (const char*)((part == 0 ? Qh : dOh) + (size_t)it * BMQ * D);
 #pragma unroll
-    for (int c = 0; c < RC; ++c) {
-      const int i = wu + NW * c;
-      if (i < RI) {
-        lds_copy16(gq, roff[c], dq_ + i * 512);
-        lds_copy16(gdo, roff[c], ddo + i * 512);
+      for (int c = 0; c < RC; ++c)
+        if (wu + NW * c < RI) lds_copy16(g, roff[c], dst + (wu + NW * c) * 512);
+    } else {
+      T* const dst = part == 2 ? (b ? lqt1 : lqt0) : (b ? ldot1 : ldot0);
+      const char* g = (const char*)((part == 2 ? QTh : dOTh) + (size_t)it * BMQ);
+#pragma unroll
+      for (int c = 0; c < TC; ++c)
+        if (wu + NW * c < TI) lds_copy16(g, toff[c], dst + (wu + NW * c) * 512);
+      if constexpr (part == 3) {
+        if (wu == 0) lds_copy4(lse_h + (size_t)it * BMQ, 4u * lane, b ? ll1 : ll0);
+        if (wu == NW - 1) lds_copy4(dd_h + (size_t)it * BMQ, 4u * lane, b ? ld1 : ld0);
       }
     }
-#pragma unroll
-    for (int c = 0; c < TC; ++c) {
-      const int i = wu + NW * c;
-      if (i < TI) {
-        lds_copy16(gqt, toff[c], dqt + i * 512);
-        lds_copy16(gdot, toff[c], ddot + i * 512);
-      }
-    }
-    if (wu == 0) lds_copy4(lse_h + (size_t)it * BMQ, 4u * lane, b ? ll1 : ll0);
-    if (wu == NW - 1) lds_copy4(dd_h + (size_t)it * BMQ, 4u * lane, b ? ld1 : ld0);
+  };
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  using P2 = std::integral_constant<int, 2>;
+  using P3 = std::integral_constant<int, 3>;
+  auto copy_tile = [&](const int it, auto bufc) {
+    copy_part(it, bufc, P0{});
+    copy_part(it, bufc, P1{});
+    copy_part(it, bufc, P2{});
+    copy_part(it, bufc, P3{});
   };
 
   // per-lane parts of the LDS read addresses (elements); everything else in
@@ -336,22 +334,21 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv(
       for (int db = 0; db < DB; ++db) x[kk][db] = *(const v8*)(tl + offB + qs * 32 + db * 32 * LT + 16 * kk);
   };
 
-  const int nqt = N / BMQ;
-  const int it0 = CAUSAL ? kb0 / BMQ : 0;   // earlier tiles lie entirely above the diagonal
-  const int ntile = nqt - it0;              // visited in order it0, it0 + 1, ...; the first two are on the diagonal
-  const int nmask = CAUSAL ? min(2, ntile) : 0;
-
   // operands of the sub-tile about to start, read one group ahead
   v8 qa[KS], da[KS];
   f32x4 l4[4], d4[4];
 
-  copy_tile(it0, std::integral_constant<int, 0>{});
-  wait_all_vmem_loads();
-  __syncthreads();
-  read_q(std::integral_constant<int, 0>{}, 0, qa);
-  read_do(std::integral_constant<int, 0>{}, 0, da);
-  read_stats(std::integral_constant<int, 0>{}, 0, l4, d4);
-  if (ntile > 1) copy_tile(it0 + 1, std::integral_constant<int, 1>{});
+  // this wave's K and V as B operands: lane holds row kw0 + r, d = 16ks + 8h .. +7
+  // (K is scaled by scale log2e once it has arrived)
+  v8 kB[KS], vB[KS];
+  auto load_kv = [&]() {
+    const int key = min(kw0 + r, N - 1);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      kB[ks] = *(const v8*)(K + head + (size_t)key * D + ks * 16 + 8 * h);
+      vB[ks] = *(const v8*)(V + head + (size_t)key * D + ks * 16 + 8 * h);
+    }
+  };
 
   auto sub_tile = [&](const int it, auto maskc, auto bufc, auto qsc) {
     constexpr int b = decltype(bufc)::value;
@@ -360,6 +357,14 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv(
     using NB = std::integral_constant<int, qs == 0 ? b : (b ^ 1)>;
     constexpr int nqs = qs ^ 1;
     const int qs0 = it * BMQ + qs * 32;
+
+    // Tile it + 2 is copied into this tile's buffer in four parts: Q and dO
+    // in Z and W of the second sub-tile (after the barrier has released the
+    // buffer), Q^T and dO^T in X and Y of the next tile's first sub-tile.
+    // The first two tiles of a unit are copied whole before the loop.
+    using OB = std::integral_constant<int, b ^ 1>;
+    const bool spread = qs == 0 && it >= it0 + 1 && it + 1 < nqt;
+    if (spread) copy_part(it + 1, OB{}, P2{});
 
     // X: S = Q K^T | dO^T fragments
     v8 dob[2][DB];
@@ -375,6 +380,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv(
     // place the whole S chain first and the exponentials between dP MFMAs)
 
     // Y: dP = dO V^T | P, Q^T fragments
+    if (spread) copy_part(it + 1, OB{}, P3{});
     v8 qbv[2][DB];
     read_t(b ? lqt1 : lqt0, qs, qbv);
     f32x16 dpacc = join16(d4);
@@ -405,11 +411,11 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv(
       mfma_drain();
       wait_all_vmem_loads();
       __syncthreads();
-      if (it + 2 < nqt) copy_tile(it + 2, bufc);
       sched_fence();
     }
 
     // Z: dV += P^T dO | dS, next Q fragments (stale but harmless after the last tile)
+    if (qs == 1 && it + 2 < nqt) copy_part(it + 2, bufc, P0{});
     read_q(NB{}, nqs, qa);
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
@@ -430,6 +436,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv(
     sched_fence();
 
     // W: dK += dS^T Q | next dO fragments and statistics
+    if (qs == 1 && it + 2 < nqt) copy_part(it + 2, bufc, P1{});
     read_do(NB{}, nqs, da);
     read_stats(NB{}, nqs, l4, d4);
 #pragma unroll
@@ -452,27 +459,62 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv(
   using B1 = std::integral_constant<int, 1>;
   using MaskOn = std::integral_constant<bool, true>;
   using MaskOff = std::integral_constant<bool, false>;
-  int it = it0;
-  if (nmask > 0) tile(it++, MaskOn{}, B0{});
-  if (nmask > 1) tile(it++, MaskOn{}, B1{});
-  // nmask is 0 or 2 unless a single tile remains, so the unmasked tiles start on buffer 0
-  for (; it + 1 < nqt; it += 2) {
-    tile(it, MaskOff{}, B0{});
-    tile(it + 1, MaskOff{}, B1{});
-  }
-  if (it < nqt) tile(it, MaskOff{}, B0{});
-  mfma_drain();
 
-  if (kw0 >= N) return;
-  // epilogue: dK = scale * acc, dV = acc; lane holds key kw0 + acc_row(j, h), d = 32db + r
+  copy_tile(it0, B0{});
+  load_kv();
+  for (;;) {
+    wait_all_vmem_loads();
+    __syncthreads();
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const size_t off = head + (size_t)(kw0 + acc_row(j, h)) * D + db * 32 + r;
-      dK[off] = (T)(dk_acc[db][j] * scale);
-      dV[off] = (T)dv_acc[db][j];
+    for (int ks = 0; ks < KS; ++ks) {  // MFMA operands only: keep them in AGPRs
+      kB[ks] = scaled8<E>(kB[ks], scale_log2);
+      asm volatile("" : "+a"(kB[ks]));
+      asm volatile("" : "+a"(vB[ks]));
     }
+    read_q(B0{}, 0, qa);
+    read_do(B0{}, 0, da);
+    read_stats(B0{}, 0, l4, d4);
+    if (ntile > 1) copy_tile(it0 + 1, B1{});
+
+    int it = it0;
+    if (nmask > 0) tile(it++, MaskOn{}, B0{});
+    if (nmask > 1) tile(it++, MaskOn{}, B1{});
+    // nmask is 0 or 2 unless a single tile remains, so the unmasked tiles start on buffer 0
+    for (; it + 1 < nqt; it += 2) {
+      tile(it, MaskOff{}, B0{});
+      tile(it + 1, MaskOff{}, B1{});
+    }
+    if (it < nqt) tile(it, MaskOff{}, B0{});
+    mfma_drain();
+
+    // start the next unit, then store this one's dK = scale * acc, dV = acc
+    // (lane holds key kw0 + acc_row(j, h), d = 32db + r)
+    const size_t out = head + (size_t)kw0 * D;
+    const bool valid = kw0 < N;
+    unit = xcd_snake_unit((int)blockIdx.x, (int)gridDim.x, BH * nkb, ++round);
+    __syncthreads();  // every wave is done with this unit's tiles
+    if (unit >= 0) {
+      set_unit(unit);
+      copy_tile(it0, B0{});
+      load_kv();
+    }
+    if (valid) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const size_t off = out + (size_t)acc_row(j, h) * D + db * 32 + r;
+          dK[off] = (T)(dk_acc[db][j] * scale);
+          dV[off] = (T)dv_acc[db][j];
+        }
+    }
+    if (unit < 0) break;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      dk_acc[db] = f32x16{};
+      dv_acc[db] = f32x16{};
+    }
+  }
 }
 
 // ---------------------------------------------------------------- dQ
@@ -541,29 +583,10 @@ __global__ __launch_bounds__(NW * 64, ATTN_DQ_MINW) void bwd_dq(
   const T* Vh = V + head;
   const T* KTh = KT + head;
 
-  // Q and dO rows as B operands of S^T = K Q^T and dP^T = V dO^T
-  const int qrow = min(qw0 + r, N - 1);
+  // this wave's Q (times scale log2e) and dO rows and the accumulator
+  // starting values; filled in once the first tile copies are issued
   v8 qf[KS], dof[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    qf[ks] = scaled8<E>(*(const v8*)(Q + head + (size_t)qrow * D + ks * 16 + 8 * h), scale_log2);
-    dof[ks] = *(const v8*)(dO + head + (size_t)qrow * D + ks * 16 + 8 * h);
-  }
-  // accumulator starting values: -lse log2e for S^T, -D for dP^T (one query per lane)
-  const float nlse2 = NLSE2[(size_t)bh * N + qrow];
-  const float ndd = ND[(size_t)bh * N + qrow];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    materialize(qf[ks]);
-    materialize(dof[ks]);
-  }
   f32x16 s_init, dp_init;
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    s_init[j] = nlse2;
-    dp_init[j] = ndd;
-  }
-
   f32x16 acc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
@@ -689,6 +712,28 @@ __global__ __launch_bounds__(NW * 64, ATTN_DQ_MINW) void bwd_dq(
 
   copy_tile(0, 0);
   if (ntiles > 1) copy_tile(1, 1);
+  // Q and dO rows as B operands of S^T = K Q^T and dP^T = V dO^T (loaded
+  // while the first tiles' copies are in flight)
+  const int qrow = min(qw0 + r, N - 1);
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    qf[ks] = scaled8<E>(*(const v8*)(Q + head + (size_t)qrow * D + ks * 16 + 8 * h), scale_log2);
+    dof[ks] = *(const v8*)(dO + head + (size_t)qrow * D + ks * 16 + 8 * h);
+  }
+  // accumulator starting values: -lse log2e for S^T, -D for dP^T (one query per lane)
+  const float nlse2 = NLSE2[(size_t)bh * N + qrow];
+  const float ndd = ND[(size_t)bh * N + qrow];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    materialize(qf[ks]);
+    materialize(dof[ks]);
+  }
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    s_init[j] = nlse2;
+    dp_init[j] = ndd;
+  }
+
   wait_all_vmem_loads();
   __syncthreads();
 
@@ -775,8 +820,9 @@ hipError_t launch_bwd_cfg(const BwdArgs& a) {
     void* args[] = {(void*)&q, (void*)&k, (void*)&v, (void*)&dO, (void*)&qt, (void*)&dot, (void*)&lse2,
                     (void*)&delta, (void*)&dk, (void*)&dv, (void*)&BH, (void*)&N, (void*)&nkb,
                     (void*)&scale, (void*)&scale_log2};
-    hipError_t e = launch_kernel((const void*)bwd_dkdv<E, D, CAUSAL, NWK, 64>, dim3((unsigned)(nkb * BH)),
-                                 dim3(NWK * 64), args, a.stream, 2);
+    const void* fn = (const void*)bwd_dkdv<E, D, CAUSAL, NWK, 64>;
+    hipError_t e = launch_kernel(fn, dim3((unsigned)persistent_grid(fn, NWK * 64, nkb * BH)), dim3(NWK * 64), args,
+                                 a.stream, 2);
     if (e != hipSuccess) return e;
   }
   {

@@ -227,6 +227,22 @@ __device__ __forceinline__ void xcd_head_major(int b, int T, int nblk, int& bh, 
 
 // The wave index as a wave-uniform (scalar) value, so that branches on it
 // are scalar branches.
+// Work split of a persistent grid of G workgroups (G a multiple of 8) over
+// T units listed heaviest first within each head: the units are dealt to the
+// 8 XCDs in contiguous ranges (the same split as xcd_head_major, so the units
+// of one head stay on one XCD and share its L2), and within an XCD the P =
+// G / 8 workgroups take them in rounds of P, alternately front to back and
+// back to front, so every workgroup gets about the same amount of work.
+// Returns the unit of round k for workgroup b, or -1 when it has no more.
+__device__ __forceinline__ int xcd_snake_unit(int b, int G, int T, int k) {
+  constexpr int X = 8;
+  const int x = b % X, p = b / X, P = G / X;
+  const int C = T / X, rem = T % X;
+  const int base = x * C + min(x, rem), cnt = C + (x < rem ? 1 : 0);
+  const int i = P * k + ((k & 1) ? P - 1 - p : p);
+  return i < cnt ? base + i : -1;
+}
+
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
 
 // 8 fp32 -> 8 16-bit values (round to nearest even) packed as an MFMA operand.

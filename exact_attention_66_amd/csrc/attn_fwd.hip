@@ -116,18 +116,9 @@ __global__ __launch_bounds__(NW * 64, ATTN_FWD_MINW) void fwd_kernel(const typen
   const T* Kh = K + head;
   const T* Vh = V + head;
 
-  // Q fragments, B operand of S^T = K Q^T: lane holds Q[q = qw0+32qb+r][16ks + 8h .. +7].
+  // Q fragments, B operand of S^T = K Q^T: lane holds Q[q = qw0+32qb+r][16ks + 8h .. +7]
+  // (loaded below, while the first tile copies are in flight)
   v8 qf[QB][KS];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int q = min(qw0 + qb * 32 + r, N - 1);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[qb][ks] = *(const v8*)(Qh + (size_t)q * D + ks * 16 + 8 * h);
-  }
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) materialize(qf[qb][ks]);
 
   f32x16 oacc[QB][DB];
   // m_run: running max (log2 units, may trail the true max by < kRescaleSlack);
@@ -289,6 +280,16 @@ __global__ __launch_bounds__(NW * 64, ATTN_FWD_MINW) void fwd_kernel(const typen
 
   copy_tile(0, 0);
   if (NBUF == 3 && ntiles > 1) copy_tile(1, 1);
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int q = min(qw0 + qb * 32 + r, N - 1);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[qb][ks] = *(const v8*)(Qh + (size_t)q * D + ks * 16 + 8 * h);
+  }
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) materialize(qf[qb][ks]);
   wait_all_vmem_loads();
   __syncthreads();
 

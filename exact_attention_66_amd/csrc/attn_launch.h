@@ -48,6 +48,11 @@ struct BwdArgs {
 // kind is an attn_kernel_kind value.
 hipError_t launch_kernel(const void* fn, dim3 grid, dim3 block, void** args, hipStream_t stream, int kind);
 
+// Grid of a persistent kernel: as many workgroups of `block` threads as fit
+// on the device at once, rounded to a multiple of 8 (one share per XCD), and
+// no more than `units` work units need.
+int persistent_grid(const void* fn, int block, int units);
+
 hipError_t launch_fwd(const FwdArgs& a);
 hipError_t launch_bwd(const BwdArgs& a);
 

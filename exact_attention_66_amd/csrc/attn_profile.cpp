@@ -48,6 +48,23 @@ hipError_t launch_kernel(const void* fn, dim3 grid, dim3 block, void** args, hip
   return hipSuccess;
 }
 
+int persistent_grid(const void* fn, int block, int units) {
+  constexpr int kMaxDev = 64;
+  static std::atomic<int> cus[kMaxDev];
+  int dev = 0;
+  int n = 0;
+  if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDev) n = cus[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    if (dev >= 0 && dev < kMaxDev) cus[dev].store(n, std::memory_order_relaxed);
+  }
+  int per_cu = 1;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, block, 0) != hipSuccess || per_cu < 1) per_cu = 1;
+  const int per_xcd = (n * per_cu + 7) / 8;
+  const int need = (units + 7) / 8;
+  return 8 * (need < per_xcd ? need : per_xcd);
+}
+
 }  // namespace attn
 
 extern "C" {
