@@ -17,12 +17,16 @@
 //  * the S^T accumulator, converted to 16-bit, is directly the B operand of
 //    O^T += V^T P^T (keys relabelled per slot_key), and V^T comes from LDS
 //    with ds_read_b64_tr_b16, so P never leaves registers;
-//  * K/V tiles reach LDS by direct global->LDS copies into three rotating
-//    buffers, two tiles ahead of their use (no staging registers, no LDS
-//    write instructions);
+//  * K/V tiles reach LDS by direct global->LDS copies (no staging registers,
+//    no LDS write instructions): 128-key tiles in two buffers at d = 128,
+//    64-key tiles in three at d = 64;
+//  * within a tile each wave pipelines its 32-key blocks: a block's V^T
+//    fragments are read before its S^T product and the next block's K
+//    fragments before its P V product, so the LDS latency hides under MFMAs;
 //  * exponentials use exp2 with scale*log2(e) folded into one FMA, and the
 //    O rescale is skipped while the running max grows by less than 2^8
-//    (exact: the same stale max is used for O, l and lse);
+//    (exact: the same stale max is used for O, l and lse); row max and sums
+//    are trees rather than dependent chains;
 //  * causal launches order work units heaviest query block first.
 #include "attn_device.h"
 #include "attn_launch.h"
@@ -204,14 +208,25 @@ __global__ __launch_bounds__(NW * 64, ATTN_FWD_MINW) void fwd_kernel(const typen
   };
 
   // one 32-key block: S^T, mask, online softmax, O^T += V^T P^T
-  auto key_block = [&](const int buf, const int kb, const int kbk0) {
+  // K fragments of a 32-key block, A operand of S^T = K Q^T
+  auto read_k = [&](const int buf, const int kb, v8 (&kf)[KS]) {
     const T* kl = lds_k[buf] + offK + kb * 32 * LK;
-    const T* vl = lds_v[buf] + offV + kb * 32 * LV;
-    // ---- S^T = K Q^T (every K fragment read before the MFMAs)
-    v8 kf[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) kf[ks] = *(const v8*)(kl + ks * 16);
-    sched_fence();
+  };
+  // one 32-key block: S^T, mask, online softmax, O^T += V^T P^T.  The block's
+  // K fragments are already in kf (read during the previous block's P V);
+  // its V^T fragments are read first, to arrive during S^T; the next block's
+  // K fragments are read before the P V product.
+  auto key_block = [&](const int buf, const int kb, const int kbk0, v8 (&kf)[KS]) {
+    const T* vl = lds_v[buf] + offV + kb * 32 * LV;
+    v8 vf[2][DB];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        vf[kk][db] = concat44<E>(E::tr_read(vl + kk * 16 * LV + db * 32), E::tr_read(vl + (kk * 16 + 8) * LV + db * 32));
+    // ---- S^T = K Q^T
     f32x16 s[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) s[qb] = f32x16{};
@@ -229,13 +244,16 @@ __global__ __launch_bounds__(NW * 64, ATTN_FWD_MINW) void fwd_kernel(const typen
           if (kbk0 + acc_row(j, h) > qw0 + qb * 32 + r) s[qb][j] = -__builtin_inff();
     }
     // ---- online softmax (log2 domain); P is rounded to 16 bits and kept
-    // packed as the B operand of the P V product
+    // packed as the B operand of the P V product.  Max and sums are trees,
+    // not chains, so that the dependent latency stays short.
     v8 pf[2][QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      float mx = -__builtin_inff();
-#pragma unroll
-      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[qb][j]);
+      const f32x16& x = s[qb];
+      const float m0 = fmaxf(fmaxf(x[0], x[1]), x[2]), m1 = fmaxf(fmaxf(x[3], x[4]), x[5]);
+      const float m2 = fmaxf(fmaxf(x[6], x[7]), x[8]), m3 = fmaxf(fmaxf(x[9], x[10]), x[11]);
+      const float m4 = fmaxf(fmaxf(x[12], x[13]), x[14]);
+      float mx = fmaxf(fmaxf(fmaxf(m0, m1), m2), fmaxf(fmaxf(m3, m4), x[15]));
       mx = xhalf_max(mx);
       const float mt = mx * scale_log2;
       const bool need = mt > m_run[qb] + kRescaleSlack;
@@ -249,33 +267,28 @@ __global__ __launch_bounds__(NW * 64, ATTN_FWD_MINW) void fwd_kernel(const typen
         m_run[qb] = mn;
       }
       const float neg_m = -m_run[qb];
-      float ls = 0.f, lr = 0.f;
+      float p[16];
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        float p[8];
+      for (int j = 0; j < 16; ++j) p[j] = fast_exp2(fmaf(x[j], scale_log2, neg_m));
+      float q4[4];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          p[i] = fast_exp2(fmaf(s[qb][8 * kk + i], scale_log2, neg_m));
-          ls += p[i];
-        }
-        pf[kk][qb] = pack8<E>(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
-        lr = sum8<E>(pf[kk][qb], lr);
-      }
-      l_run[qb] += ls;
-      lr_run[qb] += lr;
+      for (int g = 0; g < 4; ++g) q4[g] = (p[4 * g] + p[4 * g + 1]) + (p[4 * g + 2] + p[4 * g + 3]);
+      l_run[qb] += (q4[0] + q4[1]) + (q4[2] + q4[3]);
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+        pf[kk][qb] = pack8<E>(p[8 * kk + 0], p[8 * kk + 1], p[8 * kk + 2], p[8 * kk + 3], p[8 * kk + 4],
+                              p[8 * kk + 5], p[8 * kk + 6], p[8 * kk + 7]);
+      lr_run[qb] += sum8<E>(pf[0][qb], 0.f) + sum8<E>(pf[1][qb], 0.f);
     }
-    // ---- O^T += V^T P^T; V^T fragments from LDS transpose reads
+    if (kb + 1 < KB) read_k(buf, kb + 1, kf);
+    sched_fence();
+    // ---- O^T += V^T P^T
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+    for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const v4 lo = E::tr_read(vl + kk * 16 * LV + db * 32);
-        const v4 hi = E::tr_read(vl + (kk * 16 + 8) * LV + db * 32);
-        const v8 vf = concat44<E>(lo, hi);
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = E::mfma32(vf, pf[kk][qb], oacc[qb][db]);
-      }
-    }
+        for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = E::mfma32(vf[kk][db], pf[kk][qb], oacc[qb][db]);
   };
 
   copy_tile(0, 0);
@@ -300,10 +313,12 @@ __global__ __launch_bounds__(NW * 64, ATTN_FWD_MINW) void fwd_kernel(const typen
     if (t + AHEAD < ntiles) copy_tile(t + AHEAD, (buf + AHEAD) % NBUF);
     const int k0 = t * BN;
     if (wave_valid && (!CAUSAL || k0 <= q_last)) {
+      v8 kf[KS];
+      read_k(buf, 0, kf);
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         const int kbk0 = k0 + kb * 32;
-        if ((!CAUSAL || kbk0 <= q_last) && kbk0 < N) key_block(buf, kb, kbk0);
+        if ((!CAUSAL || kbk0 <= q_last) && kbk0 < N) key_block(buf, kb, kbk0, kf);
       }
     }
     mfma_drain();
