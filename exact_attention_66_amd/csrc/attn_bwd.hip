@@ -614,19 +614,26 @@ __global__ __launch_bounds__(NW * 64, ATTN_DQ_MINW) void bwd_dq(
     const int col = min(sl % TSL, BN / 8 - 1);
     toff[c] = ((unsigned)row * (unsigned)N + (unsigned)(col * 8)) * 2u;
   }
+  // a tile's copies in three parts (K, V, K^T), so that they can be spread
+  // over the tile instead of filling the wave's memory queue at once
+  auto copy_part = [&](const int t, const int b, const int part) {
+    if (part < 2) {
+      const char* g = (const char*)((part == 0 ? Kh : Vh) + (size_t)t * BN * D);
+      T* const dst = part == 0 ? lds_k[b] : lds_v[b];
+#pragma unroll
+      for (int c = 0; c < RC; ++c)
+        if (wu + NW * c < RI) lds_copy16(g, roff[c], dst + (wu + NW * c) * 512);
+    } else {
+      const char* g = (const char*)(KTh + (size_t)t * BN);
+#pragma unroll
+      for (int c = 0; c < TC; ++c)
+        if (wu + NW * c < TI) lds_copy16(g, toff[c], &lds_kt[b][(wu + NW * c) * 512]);
+    }
+  };
   auto copy_tile = [&](const int t, const int b) {
-    const char* gk = (const char*)(Kh + (size_t)t * BN * D);
-    const char* gv = (const char*)(Vh + (size_t)t * BN * D);
-    const char* gkt = (const char*)(KTh + (size_t)t * BN);
-#pragma unroll
-    for (int c = 0; c < RC; ++c)
-      if (wu + NW * c < RI) {
-        lds_copy16(gk, roff[c], &lds_k[b][(wu + NW * c) * 512]);
-        lds_copy16(gv, roff[c], &lds_v[b][(wu + NW * c) * 512]);
-      }
-#pragma unroll
-    for (int c = 0; c < TC; ++c)
-      if (wu + NW * c < TI) lds_copy16(gkt, toff[c], &lds_kt[b][(wu + NW * c) * 512]);
+    copy_part(t, b, 0);
+    copy_part(t, b, 1);
+    copy_part(t, b, 2);
   };
   // Wait until at most one tile's copies (the most recent) are outstanding:
   // vmcnt counts this wave's copies in issue order.
@@ -739,16 +746,21 @@ __global__ __launch_bounds__(NW * 64, ATTN_DQ_MINW) void bwd_dq(
 
   auto k_tile = [&](const int t, auto bufc) {
     constexpr int buf = decltype(bufc)::value;
-    // buffer (t + 2) % 3 held tile t - 1, which every wave has finished
-    if (t + 2 < ntiles) copy_tile(t + 2, (buf + 2) % NBUF);
+    // buffer (t + 2) % 3 held tile t - 1, which every wave has finished; the
+    // copy of tile t + 2 into it goes out in three parts: K before the first
+    // key block, V before the second, K^T after the last
+    constexpr int NB = (buf + 2) % NBUF;
+    const bool more = t + 2 < ntiles;
+    if (more) copy_part(t + 2, NB, 0);
     const int k0 = t * BN;
-    if (wave_valid && (!CAUSAL || k0 <= q_last)) {
+    const bool run = wave_valid && (!CAUSAL || k0 <= q_last);
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const int kbk0 = k0 + kb * 32;
-        if (!CAUSAL || kbk0 <= q_last) key_block(buf, kb, kbk0);
-      }
+    for (int kb = 0; kb < KB; ++kb) {
+      if (kb == KB / 2 && more) copy_part(t + 2, NB, 1);
+      const int kbk0 = k0 + kb * 32;
+      if (run && (!CAUSAL || kbk0 <= q_last)) key_block(buf, kb, kbk0);
     }
+    if (more) copy_part(t + 2, NB, 2);
     mfma_drain();
     // tile t + 1 must be in LDS: its copies are the ones before the most recent
     if (t + 2 < ntiles) wait_copies_but_last();
