@@ -34,6 +34,8 @@ SMALL = [
     (2, 2, 512, 128, "fp16", True),
     (1, 1, 1024, 128, "bf16", False),
     (1, 2, 1088, 64, "fp16", True),
+    (3, 48, 256, 128, "bf16", True),     # more dK/dV units than resident workgroups:
+    (4, 72, 256, 64, "fp16", True),      # workgroups run several units in turn
 ]
 
 
