@@ -21,14 +21,14 @@
 //  2. bwd_dkdv: a persistent grid; each workgroup runs a list of units
 //     (batch*head, block of 32*NW keys).  Each wave keeps its 32 keys' K and
 //     V as MFMA operands and their dK, dV fp32 accumulators for the whole
-//     sweep over query tiles.  S = Q K^T and
-//     dP = dO V^T put one key per lane, so P and dS are directly the A
-//     operands of dV += P^T dO and dK += dS^T Q (B operands from the
-//     transposed tiles).
-//  3. bwd_dq: one workgroup per (batch*head, block of 32*NW queries), shaped
-//     like the forward: each wave keeps Q and dO rows as operands and dQ^T
-//     in accumulators, computes S^T = K Q^T and dP^T = V dO^T (one query per
-//     lane: lse and D are per-lane scalars), and adds dQ^T += K^T dS^T.
+//     sweep over query tiles.  S = Q K^T and dP = dO V^T put one key per
+//     lane, so P and dS are directly the A operands of dV += P^T dO and
+//     dK += dS^T Q (B operands from the transposed tiles).
+//  3. bwd_dq: a persistent grid walking units (batch*head, block of 32*NW
+//     queries), shaped like the forward: each wave keeps Q and dO rows as
+//     operands and dQ^T in accumulators, computes S^T = K Q^T and
+//     dP^T = V dO^T (one query per lane: lse and D are per-lane scalars),
+//     and adds dQ^T += K^T dS^T.
 // The price of (3) is recomputing S and dP once more (7 matrix products in
 // total instead of 5); in exchange there is no cross-workgroup reduction.
 //
@@ -48,9 +48,6 @@ namespace {
 
 constexpr float kLog2e = 1.44269504088896340736f;
 
-#ifndef ATTN_DQ_GRID_XCD
-#define ATTN_DQ_GRID_XCD 0
-#endif
 #ifndef ATTN_DQ_NW
 #define ATTN_DQ_NW 8      // waves per workgroup (32 queries each)
 #endif
@@ -518,10 +515,14 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv(
 }
 
 // ---------------------------------------------------------------- dQ
-// Shaped like the forward: each wave keeps 32 queries' Q (times scale log2e)
-// and dO rows as B operands and dQ^T in accumulators, computes S^T = K Q^T and dP^T = V dO^T
-// (one query per lane: lse and D are per-lane scalars), and adds
-// dQ^T += K^T dS^T (A operands from the K^T tile).  K, V [BN][D + 8] and
+// Shaped like the forward: each wave keeps 32 queries' Q (times scale
+// log2e) and dO rows as B operands and dQ^T in accumulators, computes
+// S^T = K Q^T and dP^T = V dO^T (one query per lane: lse and D are per-lane
+// scalars), and adds dQ^T += K^T dS^T (A operands from the K^T tile).  A
+// persistent grid, like the dK/dV kernel's: workgroups walk their units
+// (xcd_snake_unit) and start the next unit's loads before the dQ stores;
+// keeping a head's units on one XCD lets them share its K, V, K^T tiles in
+// that XCD's L2.  K, V [BN][D + 8] and
 // K^T [D][BN + 8] tiles (padded rows: conflict-free ds_read_b128, affine
 // addresses) reach LDS by direct global->LDS copies into three rotating
 // buffers, two tiles ahead of their use; a copy instruction fills 64
@@ -562,26 +563,33 @@ __global__ __launch_bounds__(NW * 64, ATTN_DQ_MINW) void bwd_dq(
   const int h = lane >> 5;
   const int r = lane & 31;
 
-  int qblk, bh;
-#if ATTN_DQ_GRID_XCD
-  xcd_head_major((int)blockIdx.x, (int)gridDim.x, nqb, bh, qblk);
-  if (CAUSAL) qblk = nqb - 1 - qblk;  // heaviest query blocks of a head first
-#else
-  if (CAUSAL) {  // heaviest query blocks first
-    qblk = nqb - 1 - (int)(blockIdx.x / BH);
-    bh = (int)(blockIdx.x % BH);
-  } else {
-    bh = (int)(blockIdx.x / nqb);
-    qblk = (int)(blockIdx.x % nqb);
-  }
-#endif
-  const int q0 = qblk * BM;
-  const int qw0 = q0 + wu * 32;
-  const bool wave_valid = qw0 < N;
-  const size_t head = (size_t)bh * (size_t)N * D;
-  const T* Kh = K + head;
-  const T* Vh = V + head;
-  const T* KTh = KT + head;
+  // Persistent grid: the workgroup runs its units (batch*head, block of BM
+  // queries) one after another (xcd_snake_unit: the units of a head stay on
+  // one XCD, so its K, V, K^T tiles are shared in that XCD's L2; within a
+  // head the heaviest query blocks come first).  The next unit's first tile
+  // copies and Q, dO loads are issued before this unit's dQ stores.
+  int round = 0;
+  int unit = xcd_snake_unit((int)blockIdx.x, (int)gridDim.x, BH * nqb, 0);
+  if (unit < 0) return;
+  int bh, q0, qw0, kv_end, ntiles, q_last;
+  bool wave_valid;
+  size_t head;
+  const T *Kh, *Vh, *KTh;
+  auto set_unit = [&](const int u) {
+    bh = u / nqb;
+    const int qblk = CAUSAL ? nqb - 1 - u % nqb : u % nqb;
+    q0 = qblk * BM;
+    qw0 = q0 + wu * 32;
+    wave_valid = qw0 < N;
+    head = (size_t)bh * (size_t)N * D;
+    Kh = K + head;
+    Vh = V + head;
+    KTh = KT + head;
+    kv_end = CAUSAL ? min(N, q0 + BM) : N;
+    ntiles = (kv_end + BN - 1) / BN;
+    q_last = qw0 + 31;
+  };
+  set_unit(unit);
 
   // this wave's Q (times scale log2e) and dO rows and the accumulator
   // starting values; filled in once the first tile copies are issued
@@ -593,10 +601,6 @@ __global__ __launch_bounds__(NW * 64, ATTN_DQ_MINW) void bwd_dq(
 
   const int offA = opaque(r * LR + 8 * h);
   const int offB = opaque(r * LT + 8 * h);
-
-  const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
-  const int ntiles = (kv_end + BN - 1) / BN;
-  const int q_last = qw0 + 31;
 
   // ---- tile copies: per-lane byte offsets, the same for every tile
   unsigned roff[RC], toff[TC];
@@ -717,32 +721,19 @@ __global__ __launch_bounds__(NW * 64, ATTN_DQ_MINW) void bwd_dq(
     }
   };
 
-  copy_tile(0, 0);
-  if (ntiles > 1) copy_tile(1, 1);
-  // Q and dO rows as B operands of S^T = K Q^T and dP^T = V dO^T (loaded
-  // while the first tiles' copies are in flight)
-  const int qrow = min(qw0 + r, N - 1);
+  // Q and dO rows as B operands of S^T = K Q^T and dP^T = V dO^T, and the
+  // statistics (raw; scaled and spread once they have arrived)
+  float nlse2, ndd;
+  auto load_q = [&]() {
+    const int qrow = min(qw0 + r, N - 1);
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    qf[ks] = scaled8<E>(*(const v8*)(Q + head + (size_t)qrow * D + ks * 16 + 8 * h), scale_log2);
-    dof[ks] = *(const v8*)(dO + head + (size_t)qrow * D + ks * 16 + 8 * h);
-  }
-  // accumulator starting values: -lse log2e for S^T, -D for dP^T (one query per lane)
-  const float nlse2 = NLSE2[(size_t)bh * N + qrow];
-  const float ndd = ND[(size_t)bh * N + qrow];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    materialize(qf[ks]);
-    materialize(dof[ks]);
-  }
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    s_init[j] = nlse2;
-    dp_init[j] = ndd;
-  }
-
-  wait_all_vmem_loads();
-  __syncthreads();
+    for (int ks = 0; ks < KS; ++ks) {
+      qf[ks] = *(const v8*)(Q + head + (size_t)qrow * D + ks * 16 + 8 * h);
+      dof[ks] = *(const v8*)(dO + head + (size_t)qrow * D + ks * 16 + 8 * h);
+    }
+    nlse2 = NLSE2[(size_t)bh * N + qrow];
+    ndd = ND[(size_t)bh * N + qrow];
+  };
 
   auto k_tile = [&](const int t, auto bufc) {
     constexpr int buf = decltype(bufc)::value;
@@ -770,29 +761,63 @@ __global__ __launch_bounds__(NW * 64, ATTN_DQ_MINW) void bwd_dq(
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
   using B2 = std::integral_constant<int, 2>;
-  int t = 0;
-  for (; t + 2 < ntiles; t += 3) {
-    k_tile(t, B0{});
-    k_tile(t + 1, B1{});
-    k_tile(t + 2, B2{});
-  }
-  if (t < ntiles) k_tile(t, B0{});
-  if (t + 1 < ntiles) k_tile(t + 1, B1{});
 
-  if (!wave_valid) return;
-  // epilogue: dQ = scale * dQ^T; lane holds query qw0 + r, d = 32db + acc_row(j, h)
-  T* qrow_out = dQ + head + (size_t)(qw0 + r) * D;
+  copy_tile(0, 0);
+  if (ntiles > 1) copy_tile(1, 1);
+  load_q();
+  for (;;) {
+    wait_all_vmem_loads();
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int jg = 0; jg < 4; ++jg) {
-      v4 ov;
-      ov[0] = (T)(acc[db][4 * jg + 0] * scale);
-      ov[1] = (T)(acc[db][4 * jg + 1] * scale);
-      ov[2] = (T)(acc[db][4 * jg + 2] * scale);
-      ov[3] = (T)(acc[db][4 * jg + 3] * scale);
-      *(v4*)(qrow_out + db * 32 + 8 * jg + 4 * h) = ov;
+    for (int ks = 0; ks < KS; ++ks) {
+      qf[ks] = scaled8<E>(qf[ks], scale_log2);
+      materialize(qf[ks]);
+      materialize(dof[ks]);
     }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      s_init[j] = nlse2;
+      dp_init[j] = ndd;
+    }
+    __syncthreads();
+
+    int t = 0;
+    for (; t + 2 < ntiles; t += 3) {
+      k_tile(t, B0{});
+      k_tile(t + 1, B1{});
+      k_tile(t + 2, B2{});
+    }
+    if (t < ntiles) k_tile(t, B0{});
+    if (t + 1 < ntiles) k_tile(t + 1, B1{});
+
+    // every wave has passed the last tile's barrier: start the next unit,
+    // then store this one's dQ = scale * dQ^T (lane holds query qw0 + r,
+    // d = 32db + acc_row(j, h))
+    const bool valid = wave_valid;
+    T* const qrow_out = dQ + head + (size_t)(qw0 + r) * D;
+    unit = xcd_snake_unit((int)blockIdx.x, (int)gridDim.x, BH * nqb, ++round);
+    if (unit >= 0) {
+      set_unit(unit);
+      copy_tile(0, 0);
+      if (ntiles > 1) copy_tile(1, 1);
+      load_q();
+    }
+    if (valid) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int jg = 0; jg < 4; ++jg) {
+          v4 ov;
+          ov[0] = (T)(acc[db][4 * jg + 0] * scale);
+          ov[1] = (T)(acc[db][4 * jg + 1] * scale);
+          ov[2] = (T)(acc[db][4 * jg + 2] * scale);
+          ov[3] = (T)(acc[db][4 * jg + 3] * scale);
+          *(v4*)(qrow_out + db * 32 + 8 * jg + 4 * h) = ov;
+        }
+    }
+    if (unit < 0) break;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+  }
 }
 
 template <typename E, int D, bool CAUSAL>
@@ -841,8 +866,9 @@ hipError_t launch_bwd_cfg(const BwdArgs& a) {
     const int nqb = (N + NWQ * 32 - 1) / (NWQ * 32);
     void* args[] = {(void*)&q, (void*)&k, (void*)&v, (void*)&dO, (void*)&kt, (void*)&lse2, (void*)&delta,
                     (void*)&dq, (void*)&BH, (void*)&N, (void*)&nqb, (void*)&scale, (void*)&scale_log2};
-    return launch_kernel((const void*)bwd_dq<E, D, CAUSAL, NWQ, BNQ>, dim3((unsigned)(nqb * BH)), dim3(NWQ * 64),
-                         args, a.stream, 3);
+    const void* fn = (const void*)bwd_dq<E, D, CAUSAL, NWQ, BNQ>;
+    return launch_kernel(fn, dim3((unsigned)persistent_grid(fn, NWQ * 64, nqb * BH)), dim3(NWQ * 64), args,
+                         a.stream, 3);
   }
 }
 
