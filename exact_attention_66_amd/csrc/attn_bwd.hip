@@ -152,9 +152,9 @@ __global__ __launch_bounds__(256) void bwd_prep(const typename E::T* __restrict_
 // Tiles reach LDS by direct global->LDS copies (no staging registers, no LDS
 // write instructions), double-buffered; a tile's copies go out in four
 // parts spread over four MFMA groups (a wave that issues a whole tile's
-// copies at once stalls on its full memory queue).  LDS rows are padded so that the
-// 16-lane groups of every ds_read_b128 hit distinct banks and every read
-// address is one per-lane base plus an immediate: row-major Q and dO tiles
+// copies at once stalls on its full memory queue).  LDS rows are padded so
+// that the 16-lane groups of every ds_read_b128 hit distinct banks and every
+// read address is one per-lane base plus an immediate: row-major Q and dO tiles
 // use rows of D + 8 elements, the transposed Q^T and dO^T tiles rows of
 // 64 + 8.  A copy instruction fills 64 consecutive 16-byte slots, so the
 // padding slot at the end of each row is filled with a duplicate of the
