@@ -28,7 +28,9 @@
  * Pointers:  device pointers (hipMalloc / torch CUDA tensors) on the current
  *            device, each 16-byte aligned.  The caller owns all memory; the
  *            library allocates no device memory and keeps no state between
- *            calls (apart from the opt-in profiling window below).
+ *            calls (apart from the opt-in profiling window below and a
+ *            per-device cache of the compute-unit count, read once and used
+ *            to size the persistent backward grids).
  * Sizes:     B, H, N >= 1; d in {64, 128}; N a multiple of 64.
  * Streams:   work is enqueued on `stream` (a hipStream_t; NULL = the null
  *            stream) and the call returns without synchronising.
