@@ -37,10 +37,10 @@ int check_common(int64_t B, int64_t H, int64_t N, int64_t d, float scale, int dt
   const int64_t elems = checked_elems(B, H, N, d);
   if (elems < 0) return ATTN_ERR_BAD_SHAPE;
   // grid sizes: B*H*ceil(N/64) work units must fit the launch limits
-  if (B * H > (int64_t)1 << 24 || N > (int64_t)1 << 24 || B * H * (N / 64) > (int64_t)INT32_MAX) return ATTN_ERR_BAD_SHAPE;
+  if (B * H > (int64_t)1 << 24 || N > (int64_t)1 << 24 || B * H * ((N + 63) / 64) > (int64_t)INT32_MAX)
+    return ATTN_ERR_BAD_SHAPE;
   if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED_HEAD_DIM;
   if (dtype != ATTN_DTYPE_BF16 && dtype != ATTN_DTYPE_FP16) return ATTN_ERR_BAD_DTYPE;
-  if (N % 64 != 0) return ATTN_ERR_UNSUPPORTED_SEQLEN;
   if (!std::isfinite(scale) || !(scale > 0.0f)) return ATTN_ERR_BAD_SCALE;
   return ATTN_OK;
 }
@@ -72,8 +72,11 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
 }
 
 size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d) {
-  if (checked_elems(B, H, N, d) < 0 || (d != 64 && d != 128)) return 0;
-  return 2 * attn::bwd_delta_bytes(B, H, N) + 3 * attn::bwd_tcopy_bytes(B, H, N, d);
+  // the padded length (N rounded up to 64) must not overflow either
+  if (checked_elems(B, H, N, d) < 0 || checked_elems(B, H, attn::bwd_padded_n(N), d) < 0 || (d != 64 && d != 128))
+    return 0;
+  return 2 * attn::bwd_delta_bytes(B, H, N) + 3 * attn::bwd_tcopy_bytes(B, H, N, d) +
+         4 * attn::bwd_tail_bytes(B, H, N, d);
 }
 
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
@@ -83,6 +86,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
   int st = check_common(B, H, N, d, scale, dtype);
   if (st != ATTN_OK) return st;
   const size_t need = attn_bwd_workspace_bytes(B, H, N, d);
+  if (need == 0) return ATTN_ERR_BAD_SHAPE;
   if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE_TOO_SMALL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dO) || !aligned16(lse) ||
       !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || (reinterpret_cast<uintptr_t>(workspace) & 255u))
@@ -100,8 +104,12 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
 
   char* ws = (char*)workspace;
   const size_t sb = attn::bwd_delta_bytes(B, H, N), t0 = 2 * sb, tcb = attn::bwd_tcopy_bytes(B, H, N, d);
+  const size_t tl0 = t0 + 3 * tcb, tlb = attn::bwd_tail_bytes(B, H, N, d);
+  char* tail = tlb ? ws + tl0 : nullptr;
   attn::BwdArgs a{q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal != 0, dtype,
-                  (float*)ws, (float*)(ws + sb), ws + t0, ws + t0 + tcb, ws + t0 + 2 * tcb, (hipStream_t)stream};
+                  (float*)ws, (float*)(ws + sb), ws + t0, ws + t0 + tcb, ws + t0 + 2 * tcb,
+                  tail, tail ? tail + tlb : nullptr, tail ? tail + 2 * tlb : nullptr, tail ? tail + 3 * tlb : nullptr,
+                  (hipStream_t)stream};
   return launch_status(attn::launch_bwd(a));
 }
 
@@ -113,7 +121,7 @@ const char* attn_status_string(int status) {
     case ATTN_ERR_UNSUPPORTED_HEAD_DIM: return "head dimension d must be 64 or 128";
     case ATTN_ERR_BAD_DTYPE: return "dtype must be ATTN_DTYPE_BF16 (0) or ATTN_DTYPE_FP16 (1)";
     case ATTN_ERR_MISALIGNED: return "pointers must be 16-byte aligned (workspace 256-byte aligned)";
-    case ATTN_ERR_UNSUPPORTED_SEQLEN: return "sequence length N must be a multiple of 64";
+    case ATTN_ERR_UNSUPPORTED_SEQLEN: return "unsupported sequence length (reserved; not returned)";
     case ATTN_ERR_BAD_SCALE: return "scale must be finite and > 0";
     case ATTN_ERR_WORKSPACE_TOO_SMALL: return "workspace is NULL or smaller than attn_bwd_workspace_bytes()";
     case ATTN_ERR_ALIASING: return "an output overlaps an input or another output";

@@ -12,8 +12,8 @@
 // Three kernels on the caller's stream, no atomics anywhere (every output
 // element is written by exactly one lane, so all of dQ, dK, dV are bitwise
 // reproducible):
-//  1. bwd_prep: -D_i = -dO_i . O_i and -lse_i log2(e) (fp32), and transposed
-//     copies Q^T, dO^T, K^T ([B*H][d][N]) in the workspace.  Inside every group of 16 tokens
+//  1. bwd_prep: -D_i = -dO_i . O_i and -lse_i / scale (fp32), and transposed
+//     copies Q^T, dO^T, K^T ([B*H][d][Np]) in the workspace.  Inside every group of 16 tokens
 //     the copies store tokens in MFMA reduction-slot order (slot_key), so
 //     each operand fragment the main kernels need is one contiguous 16-byte
 //     LDS read; the LDS transpose reads happen once here instead of once per
@@ -31,14 +31,21 @@
 //     and adds dQ^T += K^T dS^T.
 // The price of (3) is recomputing S and dP once more (7 matrix products in
 // total instead of 5); in exchange there is no cross-workgroup reduction.
+// Any N is accepted: the workspace is padded to Np = 64 ceil(N / 64) tokens
+// and (TAIL instantiations, N not a multiple of 64) the last partial tiles of
+// Q, dO, K, V come from zero-padded copies made by (1).
 //
-// Softmax arithmetic folded into the products: (2) and (3) scale their
-// register-resident K (resp. Q) operand by scale log2(e) once, and start the
-// S and dP accumulators at -lse log2(e) and -D instead of zero, so the MFMAs
-// deliver scale S log2(e) - lse log2(e) and dP - D directly: per score only
-// P = exp2(acc) and dS = P acc remain.  This file is compiled with MFMA
-// results in VGPRs (the softmax reads them without copies out of AGPRs); the
-// operands read from LDS are steered into AGPRs instead (in_agpr).
+// Softmax arithmetic folded into the products: (2) and (3) start the S and
+// dP accumulators at -lse / scale and -D instead of zero, so the MFMAs
+// deliver S - lse / scale and dP - D directly: per score only
+// P = exp2(scale log2(e) acc) and dS = P acc remain.  The 16-bit Q and K
+// operands stay exactly as given (scaling one of them by scale log2(e) in
+// 16 bits would save the multiply but round the operand, an error of up to
+// 2^-9 |S| log2(e) in the exponent, large for rows of large scores); the
+// fp32 start value carries lse / scale with a relative error of 2^-24.
+// This file is compiled with MFMA results in VGPRs (the softmax reads them
+// without copies out of AGPRs); the operands read from LDS are steered into
+// AGPRs instead (in_agpr).
 #include "attn_device.h"
 #include "attn_launch.h"
 
@@ -65,19 +72,31 @@ constexpr float kLog2e = 1.44269504088896340736f;
 #endif
 
 // ---------------------------------------------------------------- prep
-// One workgroup per (batch*head, 64-token block).  Q, K, dO tiles go through
-// swizzled LDS; the transposed copies are read back with ds_read_b64_tr_b16
-// (lane gets 4 tokens of one d column, twice = 8 tokens in slot order) and
-// written as 16-byte rows of [d][token].
-template <typename E, int D>
+// One workgroup per (batch*head, 64-token block) of the padded length
+// Np = 64 ceil(N / 64).  Q, K, dO tiles go through swizzled LDS; the
+// transposed copies are read back with ds_read_b64_tr_b16 (lane gets 4
+// tokens of one d column, twice = 8 tokens in slot order) and written as
+// 16-byte rows of [d][token] with row stride Np.  Tokens past N are padding:
+// zero in the transposed copies, -D = 0 and -lse / scale = -inf, so a padded
+// query gets P = 0 and dS = 0 in the kernels that follow and adds nothing to
+// dK, dV.  When N is not a multiple of 64 the block holding the last tokens
+// also writes them, zero-padded to 64 rows, as row-major tail tiles of Q,
+// dO, K and V ([B*H][64][d]): the main kernels take their last partial tile
+// from there and never read past the end of an input.  TAIL (N not a
+// multiple of 64) is a template flag, so that the checks cost nothing when
+// there is no padding.
+template <typename E, int D, bool TAIL>
 __global__ __launch_bounds__(256) void bwd_prep(const typename E::T* __restrict__ Q,
                                                 const typename E::T* __restrict__ K,
+                                                const typename E::T* __restrict__ V,
                                                 const typename E::T* __restrict__ O,
                                                 const typename E::T* __restrict__ dO,
                                                 const float* __restrict__ LSE, float* __restrict__ Dvec,
-                                                float* __restrict__ LSE2, typename E::T* __restrict__ QT,
+                                                float* __restrict__ NLSE, typename E::T* __restrict__ QT,
                                                 typename E::T* __restrict__ KT, typename E::T* __restrict__ dOT,
-                                                int N) {
+                                                typename E::T* __restrict__ QTail, typename E::T* __restrict__ dOTail,
+                                                typename E::T* __restrict__ KTail, typename E::T* __restrict__ VTail,
+                                                int N, int Np, float inv_scale) {
   using T = typename E::T;
   using v8 = typename E::v8;
   constexpr int R = 64;                // tokens per workgroup
@@ -90,22 +109,29 @@ __global__ __launch_bounds__(256) void bwd_prep(const typename E::T* __restrict_
   const int w = tid >> 6;
   const int h = lane >> 5;
   const int r = lane & 31;
-  const int nrb = N / R;
+  const int nrb = Np / R;
   const int bh = (int)(blockIdx.x / nrb);
   const int rb = (int)(blockIdx.x % nrb);
-  const size_t head = (size_t)bh * N * D;
-  const size_t row0 = (size_t)rb * R;
+  const size_t head = (size_t)bh * N * D;     // inputs [B*H][N][d]
+  const size_t headp = (size_t)bh * Np * D;   // transposed copies [B*H][d][Np]
+  const int row0 = rb * R;
+  const bool tail = TAIL && row0 + R > N;     // the block holding the last tokens of a ragged N
 
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
     const int idx = tid + c * 256;
     const int row = idx / CPR;
     const int col = (idx % CPR) * 8;
-    const size_t g = head + (row0 + row) * D + col;
-    const v8 qv = *(const v8*)(Q + g);
-    const v8 kv = *(const v8*)(K + g);
-    const v8 dov = *(const v8*)(dO + g);
-    const v8 ov = *(const v8*)(O + g);
+    const int tok = row0 + row;
+    const bool in = !TAIL || tok < N;
+    const size_t g = head + (size_t)tok * D + col;
+    v8 qv = {}, kv = {}, dov = {}, ov = {};
+    if (in) {
+      qv = *(const v8*)(Q + g);
+      kv = *(const v8*)(K + g);
+      dov = *(const v8*)(dO + g);
+      ov = *(const v8*)(O + g);
+    }
     *(v8*)(&tile[0][swz<D>(row, col)]) = qv;
     *(v8*)(&tile[1][swz<D>(row, col)]) = kv;
     *(v8*)(&tile[2][swz<D>(row, col)]) = dov;
@@ -116,9 +142,18 @@ __global__ __launch_bounds__(256) void bwd_prep(const typename E::T* __restrict_
 #pragma unroll
     for (int off = CPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, CPR);
     if ((idx % CPR) == 0) {
-      const size_t i = (size_t)bh * N + row0 + row;
+      const size_t i = (size_t)bh * Np + tok;
       Dvec[i] = -acc;
-      LSE2[i] = -LSE[i] * kLog2e;
+      NLSE[i] = in ? -LSE[(size_t)bh * N + tok] * inv_scale : -__builtin_inff();
+    }
+    if (tail) {
+      const size_t gt = (size_t)bh * R * D + (size_t)row * D + col;
+      v8 vv = {};
+      if (in) vv = *(const v8*)(V + g);
+      *(v8*)(QTail + gt) = qv;
+      *(v8*)(dOTail + gt) = dov;
+      *(v8*)(KTail + gt) = kv;
+      *(v8*)(VTail + gt) = vv;
     }
   }
   __syncthreads();
@@ -136,7 +171,7 @@ __global__ __launch_bounds__(256) void bwd_prep(const typename E::T* __restrict_
       const int rr = pg * 16 + tr_row;
       const v8 val = concat44<E>(E::tr_read(&tile[t][swz<D>(rr, db * 32 + tr_col)]),
                                  E::tr_read(&tile[t][swz<D>(rr + 8, db * 32 + tr_col)]));
-      *(v8*)(outs[t] + head + (size_t)(db * 32 + r) * N + row0 + pg * 16 + 8 * h) = val;
+      *(v8*)(outs[t] + headp + (size_t)(db * 32 + r) * Np + row0 + pg * 16 + 8 * h) = val;
     }
   }
 }
@@ -163,8 +198,8 @@ __global__ __launch_bounds__(256) void bwd_prep(const typename E::T* __restrict_
 // Each 32-query sub-tile runs as four groups of MFMAs, and every group has
 // the LDS reads or the softmax work of a later group interleaved with it,
 // so that each read has a whole group of MFMAs to arrive in:
-//   X  S' = -lse log2e + Q (scale log2e K)^T   | dO^T fragments (B operands of Z)
-//   Y  dP' = -D + dO V^T  | P = exp2(S'); Q^T fragments (W)
+//   X  S' = -lse / scale + Q K^T   | dO^T fragments (B operands of Z)
+//   Y  dP' = -D + dO V^T  | P = exp2(scale log2e S'); Q^T fragments (W)
 //   Z  dV += P^T dO       | dS = P dP'; next sub-tile's Q fragments (X)
 //   W  dK += dS^T Q       | next sub-tile's dO fragments (Y) and lse, D (X, Y)
 // (S, dP with one key per lane: P and dS are directly the A operands of the
@@ -174,15 +209,17 @@ __global__ __launch_bounds__(256) void bwd_prep(const typename E::T* __restrict_
 // tile after it starts into the buffer just released.  Tiles that reach the
 // causal diagonal come first and run the same pipeline with the mask applied
 // (sub-tiles entirely above the diagonal come out as P = 0).
-template <typename E, int D, bool CAUSAL, int NW, int BMQ>
+template <typename E, int D, bool CAUSAL, int NW, int BMQ, bool TAIL>
 __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv(
     const typename E::T* __restrict__ Q, const typename E::T* __restrict__ K,
     const typename E::T* __restrict__ V, const typename E::T* __restrict__ dO,
     const typename E::T* __restrict__ QT, const typename E::T* __restrict__ dOT,
-    const float* __restrict__ LSE2, const float* __restrict__ Dvec, typename E::T* __restrict__ dK,
-    typename E::T* __restrict__ dV, int BH, int N, int nkb, float scale, float scale_log2) {
+    const typename E::T* __restrict__ QTail, const typename E::T* __restrict__ dOTail,
+    const float* __restrict__ NLSE, const float* __restrict__ Dvec, typename E::T* __restrict__ dK,
+    typename E::T* __restrict__ dV, int BH, int N, int Np_arg, int nkb, float scale, float scale_log2) {
   using T = typename E::T;
   using v8 = typename E::v8;
+  const int Np = TAIL ? Np_arg : N;     // padded length: N itself unless TAIL
   static_assert(BMQ == 64, "the pipeline handles two 32-query sub-tiles per tile");
   static_assert(!CAUSAL || NW * 32 == 2 * BMQ, "causal: exactly two diagonal tiles per workgroup");
   static_assert((NW & (NW - 1)) == 0, "power-of-two wave count");
@@ -217,22 +254,26 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv(
   int round = 0;
   int unit = xcd_snake_unit((int)blockIdx.x, (int)gridDim.x, BH * nkb, 0);
   if (unit < 0) return;
-  const int nqt = N / BMQ;
+  const int nqt = Np / BMQ;             // query tiles (the last may be padded)
+  const int nfull = N / BMQ;            // tiles wholly inside the sequence
   int kb0, kw0, it0, ntile, nmask;
   size_t head;
-  const T *Qh, *dOh, *QTh, *dOTh;
+  const T *Qh, *dOh, *QTh, *dOTh, *Qtl, *dOtl;
   const float *lse_h, *dd_h;
   auto set_unit = [&](const int u) {
     const int bh = u / nkb;
     kb0 = (u % nkb) * BN;
     kw0 = kb0 + wu * 32;                 // first key of this wave
     head = (size_t)bh * (size_t)N * D;
+    const size_t headp = (size_t)bh * (size_t)Np * D;
     Qh = Q + head;
     dOh = dO + head;
-    QTh = QT + head;
-    dOTh = dOT + head;
-    lse_h = LSE2 + (size_t)bh * N;
-    dd_h = Dvec + (size_t)bh * N;
+    QTh = QT + headp;
+    dOTh = dOT + headp;
+    Qtl = QTail + (size_t)bh * BMQ * D;
+    dOtl = dOTail + (size_t)bh * BMQ * D;
+    lse_h = NLSE + (size_t)bh * Np;
+    dd_h = Dvec + (size_t)bh * Np;
     it0 = CAUSAL ? kb0 / BMQ : 0;        // earlier tiles lie entirely above the diagonal
     ntile = nqt - it0;                   // visited in order it0, it0 + 1, ...; the first two are on the diagonal
     nmask = CAUSAL ? min(2, ntile) : 0;
@@ -260,17 +301,20 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv(
     const int s = 64 * (wu + NW * c) + lane;
     const int row = min(s / TSL, D - 1);
     const int col = min(s % TSL, TSL - 2);
-    toff[c] = ((unsigned)row * (unsigned)N + (unsigned)(col * 8)) * 2u;
+    toff[c] = ((unsigned)row * (unsigned)Np + (unsigned)(col * 8)) * 2u;
   }
   // A tile's copies in four parts (Q, dO, Q^T, dO^T with the statistics),
   // so that they can be spread over the MFMA groups instead of filling the
-  // wave's memory queue at once.
+  // wave's memory queue at once.  A padded last tile takes its Q and dO rows
+  // from the zero-padded tail tiles (a scalar choice of base address).
   auto copy_part = [&](const int it, auto bufc, auto partc) {
     constexpr int b = decltype(bufc)::value;
     constexpr int part = decltype(partc)::value;
     if constexpr (part < 2) {
       T* const dst = part == 0 ? (b ? lq1 : lq0) : (b ? ldo1 : ldo0);
-      const char* g = (const char*)((part == 0 ? Qh : dOh) + (size_t)it * BMQ * D);
+      const T* const src =
+          !TAIL || it < nfull ? (part == 0 ? Qh : dOh) + (size_t)it * BMQ * D : (part == 0 ? Qtl : dOtl);
+      const char* g = (const char*)src;
 #pragma unroll
       for (int c = 0; c < RC; ++c)
         if (wu + NW * c < RI) lds_copy16(g, roff[c], dst + (wu + NW * c) * 512);
@@ -336,7 +380,6 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv(
   f32x4 l4[4], d4[4];
 
   // this wave's K and V as B operands: lane holds row kw0 + r, d = 16ks + 8h .. +7
-  // (K is scaled by scale log2e once it has arrived)
   v8 kB[KS], vB[KS];
   auto load_kv = [&]() {
     const int key = min(kw0 + r, N - 1);
@@ -388,7 +431,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv(
     }
     float p[16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) p[j] = fast_exp2(sacc[j]);
+    for (int j = 0; j < 16; ++j) p[j] = fast_exp2(sacc[j] * scale_log2);
     if constexpr (decltype(maskc)::value) {  // key > query -> P = 0
 #pragma unroll
       for (int j = 0; j < 16; ++j)
@@ -464,7 +507,6 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv(
     __syncthreads();
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {  // MFMA operands only: keep them in AGPRs
-      kB[ks] = scaled8<E>(kB[ks], scale_log2);
       asm volatile("" : "+a"(kB[ks]));
       asm volatile("" : "+a"(vB[ks]));
     }
@@ -487,7 +529,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv(
     // start the next unit, then store this one's dK = scale * acc, dV = acc
     // (lane holds key kw0 + acc_row(j, h), d = 32db + r)
     const size_t out = head + (size_t)kw0 * D;
-    const bool valid = kw0 < N;
+    const int nvalid = N - kw0;          // keys of this wave inside the sequence
     unit = xcd_snake_unit((int)blockIdx.x, (int)gridDim.x, BH * nkb, ++round);
     __syncthreads();  // every wave is done with this unit's tiles
     if (unit >= 0) {
@@ -495,7 +537,9 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv(
       copy_tile(it0, B0{});
       load_kv();
     }
-    if (valid) {
+    // (a unit holds 4 * 32 keys and N is only a multiple of 64 without TAIL,
+    // so whole waves can lie past the end: nvalid <= 0)
+    if (nvalid >= 32) {
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -504,6 +548,16 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv(
           dK[off] = (T)(dk_acc[db][j] * scale);
           dV[off] = (T)dv_acc[db][j];
         }
+    } else if (TAIL && nvalid > 0) {  // the sequence ends inside this wave's keys
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if (acc_row(j, h) < nvalid) {
+            const size_t off = out + (size_t)acc_row(j, h) * D + db * 32 + r;
+            dK[off] = (T)(dk_acc[db][j] * scale);
+            dV[off] = (T)dv_acc[db][j];
+          }
     }
     if (unit < 0) break;
 #pragma unroll
@@ -515,8 +569,8 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv(
 }
 
 // ---------------------------------------------------------------- dQ
-// Shaped like the forward: each wave keeps 32 queries' Q (times scale
-// log2e) and dO rows as B operands and dQ^T in accumulators, computes
+// Shaped like the forward: each wave keeps 32 queries' Q and dO rows as B
+// operands and dQ^T in accumulators, computes
 // S^T = K Q^T and dP^T = V dO^T (one query per lane: lse and D are per-lane
 // scalars), and adds dQ^T += K^T dS^T (A operands from the K^T tile).  A
 // persistent grid, like the dK/dV kernel's: workgroups walk their units
@@ -528,13 +582,15 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv(
 // buffers, two tiles ahead of their use; a copy instruction fills 64
 // consecutive 16-byte slots, so the padding slot of each row gets a
 // duplicate of the row's last chunk and a tile is a whole number of blocks.
-template <typename E, int D, bool CAUSAL, int NW, int BN>
+template <typename E, int D, bool CAUSAL, int NW, int BN, bool TAIL>
 __global__ __launch_bounds__(NW * 64, ATTN_DQ_MINW) void bwd_dq(
     const typename E::T* __restrict__ Q, const typename E::T* __restrict__ K,
     const typename E::T* __restrict__ V, const typename E::T* __restrict__ dO,
-    const typename E::T* __restrict__ KT, const float* __restrict__ NLSE2, const float* __restrict__ ND,
-    typename E::T* __restrict__ dQ, int BH, int N, int nqb, float scale, float scale_log2) {
+    const typename E::T* __restrict__ KT, const typename E::T* __restrict__ KTail,
+    const typename E::T* __restrict__ VTail, const float* __restrict__ NLSE, const float* __restrict__ ND,
+    typename E::T* __restrict__ dQ, int BH, int N, int Np_arg, int nqb, float scale, float scale_log2) {
   using T = typename E::T;
+  const int Np = TAIL ? Np_arg : N;     // padded length: N itself unless TAIL
   using v8 = typename E::v8;
   using v4 = typename E::v4;
   constexpr int BM = NW * 32;        // queries per workgroup
@@ -571,10 +627,11 @@ __global__ __launch_bounds__(NW * 64, ATTN_DQ_MINW) void bwd_dq(
   int round = 0;
   int unit = xcd_snake_unit((int)blockIdx.x, (int)gridDim.x, BH * nqb, 0);
   if (unit < 0) return;
+  const int nfull = N / BN;   // key tiles wholly inside the sequence
   int bh, q0, qw0, kv_end, ntiles, q_last;
   bool wave_valid;
   size_t head;
-  const T *Kh, *Vh, *KTh;
+  const T *Kh, *Vh, *KTh, *Ktl, *Vtl;
   auto set_unit = [&](const int u) {
     bh = u / nqb;
     const int qblk = CAUSAL ? nqb - 1 - u % nqb : u % nqb;
@@ -584,15 +641,17 @@ __global__ __launch_bounds__(NW * 64, ATTN_DQ_MINW) void bwd_dq(
     head = (size_t)bh * (size_t)N * D;
     Kh = K + head;
     Vh = V + head;
-    KTh = KT + head;
+    KTh = KT + (size_t)bh * (size_t)Np * D;
+    Ktl = KTail + (size_t)bh * BN * D;
+    Vtl = VTail + (size_t)bh * BN * D;
     kv_end = CAUSAL ? min(N, q0 + BM) : N;
     ntiles = (kv_end + BN - 1) / BN;
     q_last = qw0 + 31;
   };
   set_unit(unit);
 
-  // this wave's Q (times scale log2e) and dO rows and the accumulator
-  // starting values; filled in once the first tile copies are issued
+  // this wave's Q and dO rows and the accumulator starting values; filled
+  // in once the first tile copies are issued
   v8 qf[KS], dof[KS];
   f32x16 s_init, dp_init;
   f32x16 acc[DB];
@@ -616,13 +675,15 @@ __global__ __launch_bounds__(NW * 64, ATTN_DQ_MINW) void bwd_dq(
     const int sl = 64 * (wu + NW * c) + lane;
     const int row = min(sl / TSL, D - 1);
     const int col = min(sl % TSL, BN / 8 - 1);
-    toff[c] = ((unsigned)row * (unsigned)N + (unsigned)(col * 8)) * 2u;
+    toff[c] = ((unsigned)row * (unsigned)Np + (unsigned)(col * 8)) * 2u;
   }
   // a tile's copies in three parts (K, V, K^T), so that they can be spread
-  // over the tile instead of filling the wave's memory queue at once
+  // over the tile instead of filling the wave's memory queue at once; a
+  // padded last tile takes its K and V rows from the zero-padded tail tiles
   auto copy_part = [&](const int t, const int b, const int part) {
     if (part < 2) {
-      const char* g = (const char*)((part == 0 ? Kh : Vh) + (size_t)t * BN * D);
+      const T* const src = !TAIL || t < nfull ? (part == 0 ? Kh : Vh) + (size_t)t * BN * D : (part == 0 ? Ktl : Vtl);
+      const char* g = (const char*)src;
       T* const dst = part == 0 ? lds_k[b] : lds_v[b];
 #pragma unroll
       for (int c = 0; c < RC; ++c)
@@ -696,7 +757,12 @@ __global__ __launch_bounds__(NW * 64, ATTN_DQ_MINW) void bwd_dq(
 #endif
     float ds[16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) ds[j] = fast_exp2(sacc[j]);
+    for (int j = 0; j < 16; ++j) ds[j] = fast_exp2(sacc[j] * scale_log2);
+    if (TAIL && !CAUSAL && kbk0 + 32 > N) {   // keys past the end of the sequence -> P = 0
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (kbk0 + acc_row(j, h) >= N) ds[j] = 0.f;
+    }
     if (CAUSAL && kbk0 + 31 > qw0) {   // block crosses the diagonal: key > query -> P = 0
 #pragma unroll
       for (int j = 0; j < 16; ++j)
@@ -722,8 +788,8 @@ __global__ __launch_bounds__(NW * 64, ATTN_DQ_MINW) void bwd_dq(
   };
 
   // Q and dO rows as B operands of S^T = K Q^T and dP^T = V dO^T, and the
-  // statistics (raw; scaled and spread once they have arrived)
-  float nlse2, ndd;
+  // statistics (spread over the accumulator starting values once they have arrived)
+  float nlse, ndd;
   auto load_q = [&]() {
     const int qrow = min(qw0 + r, N - 1);
 #pragma unroll
@@ -731,8 +797,8 @@ __global__ __launch_bounds__(NW * 64, ATTN_DQ_MINW) void bwd_dq(
       qf[ks] = *(const v8*)(Q + head + (size_t)qrow * D + ks * 16 + 8 * h);
       dof[ks] = *(const v8*)(dO + head + (size_t)qrow * D + ks * 16 + 8 * h);
     }
-    nlse2 = NLSE2[(size_t)bh * N + qrow];
-    ndd = ND[(size_t)bh * N + qrow];
+    nlse = NLSE[(size_t)bh * Np + qrow];
+    ndd = ND[(size_t)bh * Np + qrow];
   };
 
   auto k_tile = [&](const int t, auto bufc) {
@@ -749,7 +815,7 @@ __global__ __launch_bounds__(NW * 64, ATTN_DQ_MINW) void bwd_dq(
     for (int kb = 0; kb < KB; ++kb) {
       if (kb == KB / 2 && more) copy_part(t + 2, NB, 1);
       const int kbk0 = k0 + kb * 32;
-      if (run && (!CAUSAL || kbk0 <= q_last)) key_block(buf, kb, kbk0);
+      if (run && (!CAUSAL || kbk0 <= q_last) && (!TAIL || kbk0 < N)) key_block(buf, kb, kbk0);
     }
     if (more) copy_part(t + 2, NB, 2);
     mfma_drain();
@@ -769,13 +835,12 @@ __global__ __launch_bounds__(NW * 64, ATTN_DQ_MINW) void bwd_dq(
     wait_all_vmem_loads();
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      qf[ks] = scaled8<E>(qf[ks], scale_log2);
       materialize(qf[ks]);
       materialize(dof[ks]);
     }
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      s_init[j] = nlse2;
+      s_init[j] = nlse;
       dp_init[j] = ndd;
     }
     __syncthreads();
@@ -792,7 +857,7 @@ __global__ __launch_bounds__(NW * 64, ATTN_DQ_MINW) void bwd_dq(
     // every wave has passed the last tile's barrier: start the next unit,
     // then store this one's dQ = scale * dQ^T (lane holds query qw0 + r,
     // d = 32db + acc_row(j, h))
-    const bool valid = wave_valid;
+    const bool valid = wave_valid && (!TAIL || qw0 + r < N);   // rows past the end are not stored
     T* const qrow_out = dQ + head + (size_t)(qw0 + r) * D;
     unit = xcd_snake_unit((int)blockIdx.x, (int)gridDim.x, BH * nqb, ++round);
     if (unit >= 0) {
@@ -820,13 +885,14 @@ __global__ __launch_bounds__(NW * 64, ATTN_DQ_MINW) void bwd_dq(
   }
 }
 
-template <typename E, int D, bool CAUSAL>
+template <typename E, int D, bool CAUSAL, bool TAIL>
 hipError_t launch_bwd_cfg(const BwdArgs& a) {
   constexpr int NWK = 4;            // dK/dV: waves per workgroup (32 keys each)
   constexpr int NWQ = ATTN_DQ_NW;
   constexpr int BNQ = ATTN_DQ_BN;
   const int BH = (int)(a.B * a.H);
   const int N = (int)a.N;
+  const int Np = (int)bwd_padded_n(a.N);
   using T = typename E::T;
   const T* q = (const T*)a.q;
   const T* k = (const T*)a.k;
@@ -838,35 +904,42 @@ hipError_t launch_bwd_cfg(const BwdArgs& a) {
   T* dk = (T*)a.dk;
   T* dv = (T*)a.dv;
   float* delta = a.delta;
-  float* lse2 = a.lse2;
+  float* nlse = a.nlse;
   T* qt = (T*)a.qt;
   T* kt = (T*)a.kt;
   T* dot = (T*)a.dot;
+  T* qtail = (T*)a.qtail;
+  T* dotail = (T*)a.dotail;
+  T* ktail = (T*)a.ktail;
+  T* vtail = (T*)a.vtail;
   float scale = a.scale;
   float scale_log2 = a.scale * kLog2e;
+  float inv_scale = (float)(1.0 / (double)a.scale);
 
   {
-    void* args[] = {(void*)&q, (void*)&k, (void*)&o, (void*)&dO, (void*)&lse, (void*)&delta, (void*)&lse2,
-                    (void*)&qt, (void*)&kt, (void*)&dot, (void*)&N};
-    hipError_t e = launch_kernel((const void*)bwd_prep<E, D>, dim3((unsigned)(BH * (N / 64))), dim3(256), args,
+    void* args[] = {(void*)&q,   (void*)&k,     (void*)&v,    (void*)&o,     (void*)&dO,    (void*)&lse,
+                    (void*)&delta, (void*)&nlse, (void*)&qt, (void*)&kt, (void*)&dot, (void*)&qtail,
+                    (void*)&dotail, (void*)&ktail, (void*)&vtail, (void*)&N, (void*)&Np, (void*)&inv_scale};
+    hipError_t e = launch_kernel((const void*)bwd_prep<E, D, TAIL>, dim3((unsigned)(BH * (Np / 64))), dim3(256), args,
                                  a.stream, 1);
     if (e != hipSuccess) return e;
   }
   {
     const int nkb = (N + NWK * 32 - 1) / (NWK * 32);
-    void* args[] = {(void*)&q, (void*)&k, (void*)&v, (void*)&dO, (void*)&qt, (void*)&dot, (void*)&lse2,
-                    (void*)&delta, (void*)&dk, (void*)&dv, (void*)&BH, (void*)&N, (void*)&nkb,
-                    (void*)&scale, (void*)&scale_log2};
-    const void* fn = (const void*)bwd_dkdv<E, D, CAUSAL, NWK, 64>;
+    void* args[] = {(void*)&q,     (void*)&k,  (void*)&v,  (void*)&dO, (void*)&qt,  (void*)&dot,
+                    (void*)&qtail, (void*)&dotail, (void*)&nlse, (void*)&delta, (void*)&dk, (void*)&dv,
+                    (void*)&BH, (void*)&N, (void*)&Np, (void*)&nkb, (void*)&scale, (void*)&scale_log2};
+    const void* fn = (const void*)bwd_dkdv<E, D, CAUSAL, NWK, 64, TAIL>;
     hipError_t e = launch_kernel(fn, dim3((unsigned)persistent_grid(fn, NWK * 64, nkb * BH)), dim3(NWK * 64), args,
                                  a.stream, 2);
     if (e != hipSuccess) return e;
   }
   {
     const int nqb = (N + NWQ * 32 - 1) / (NWQ * 32);
-    void* args[] = {(void*)&q, (void*)&k, (void*)&v, (void*)&dO, (void*)&kt, (void*)&lse2, (void*)&delta,
-                    (void*)&dq, (void*)&BH, (void*)&N, (void*)&nqb, (void*)&scale, (void*)&scale_log2};
-    const void* fn = (const void*)bwd_dq<E, D, CAUSAL, NWQ, BNQ>;
+    void* args[] = {(void*)&q,    (void*)&k,  (void*)&v,  (void*)&dO, (void*)&kt, (void*)&ktail, (void*)&vtail,
+                    (void*)&nlse, (void*)&delta, (void*)&dq, (void*)&BH, (void*)&N, (void*)&Np, (void*)&nqb,
+                    (void*)&scale, (void*)&scale_log2};
+    const void* fn = (const void*)bwd_dq<E, D, CAUSAL, NWQ, BNQ, TAIL>;
     return launch_kernel(fn, dim3((unsigned)persistent_grid(fn, NWQ * 64, nqb * BH)), dim3(NWQ * 64), args,
                          a.stream, 3);
   }
@@ -874,8 +947,12 @@ hipError_t launch_bwd_cfg(const BwdArgs& a) {
 
 template <typename E, int D>
 hipError_t launch_bwd_d(const BwdArgs& a) {
-  if (a.causal) return launch_bwd_cfg<E, D, true>(a);
-  return launch_bwd_cfg<E, D, false>(a);
+  if (a.N % 64 == 0) {
+    if (a.causal) return launch_bwd_cfg<E, D, true, false>(a);
+    return launch_bwd_cfg<E, D, false, false>(a);
+  }
+  if (a.causal) return launch_bwd_cfg<E, D, true, true>(a);
+  return launch_bwd_cfg<E, D, false, true>(a);
 }
 
 }  // namespace

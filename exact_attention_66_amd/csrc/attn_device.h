@@ -255,13 +255,6 @@ __device__ __forceinline__ typename E::v8 pack8(float a0, float a1, float a2, fl
   return r;
 }
 
-// Eight operand elements times c, rounded back to the element type.
-template <typename E>
-__device__ __forceinline__ typename E::v8 scaled8(typename E::v8 x, float c) {
-  return pack8<E>((float)x[0] * c, (float)x[1] * c, (float)x[2] * c, (float)x[3] * c, (float)x[4] * c,
-                  (float)x[5] * c, (float)x[6] * c, (float)x[7] * c);
-}
-
 // acc + sum of the 8 packed 16-bit values (exact products by 1.0, fp32 sums).
 template <typename E>
 __device__ __forceinline__ float sum8(typename E::v8 x, float acc) {

@@ -27,7 +27,10 @@
 //    O rescale is skipped while the running max grows by less than 2^8
 //    (exact: the same stale max is used for O, l and lse); row max and sums
 //    are trees rather than dependent chains;
-//  * causal launches order work units heaviest query block first.
+//  * causal launches order work units heaviest query block first;
+//  * any N: rows past the end are neither read nor stored, and the last
+//    tile's keys past the end are masked (the TAIL instantiation, chosen
+//    when N is not a multiple of 64, so that other launches pay nothing).
 #include "attn_device.h"
 #include "attn_launch.h"
 
@@ -61,7 +64,7 @@ constexpr float kRescaleSlack = 8.0f;
 // with ds_read_b64_tr_b16 by 32 lanes covering 4 rows x 64 bytes (rows 16
 // banks apart: the 4 rows land on 4 disjoint 16-bank groups).  Both are
 // affine, so every read is one per-lane base plus an immediate offset.
-template <typename E, int D, bool CAUSAL, int QB, int NW, int BN>
+template <typename E, int D, bool CAUSAL, int QB, int NW, int BN, bool TAIL>
 __global__ __launch_bounds__(NW * 64, ATTN_FWD_MINW) void fwd_kernel(const typename E::T* __restrict__ Q,
                                                                      const typename E::T* __restrict__ K,
                                                                      const typename E::T* __restrict__ V,
@@ -167,22 +170,41 @@ __global__ __launch_bounds__(NW * 64, ATTN_FWD_MINW) void fwd_kernel(const typen
     const int col = min(sl % VSL, D / 8 - 1);
     voff[c] = (unsigned)(row * D + col * 8) * 2u;
   }
-  // A tile past the end of the sequence (N is a multiple of 64, so only a
-  // 128-key tile can be cut) holds 64 keys: exactly the first half of its
-  // copy blocks, since 64 rows of either layout fill whole 64-slot blocks.
+  // Without TAIL (N a multiple of 64) only a 128-key tile can run past the
+  // end of the sequence, by exactly 64 keys: it is copied as its first half,
+  // since 64 rows of either layout fill whole 64-slot blocks, and its second
+  // half is never read.  With TAIL (any other N) the last tile's copies clamp
+  // every row to the last key, N - 1, so the rows past the end hold finite
+  // duplicates that are read only under the key mask, and no copy reads
+  // beyond the input.  A copy offset is row * 2D + column bytes with 2D a
+  // power of two, so the clamp is one shift, min and or per lane.
   static_assert((64 * KSL) % 64 == 0 && (64 * VSL) % 64 == 0, "half tiles are whole blocks");
+  constexpr int RSH = D == 128 ? 8 : 7;   // log2 of a row's bytes
+  auto clamp_row = [](unsigned off, int lim) {
+    return ((unsigned)min((int)(off >> RSH), lim) << RSH) | (off & ((1u << RSH) - 1u));
+  };
   auto copy_tile = [&](const int t, const int b) {
     const char* gk = (const char*)(Kh + (size_t)t * BN * D);
     const char* gv = (const char*)(Vh + (size_t)t * BN * D);
-    const bool half = t * BN + BN > N;
-    const int ki = half ? 64 * KSL / 64 : KI;
-    const int vi = half ? 64 * VSL / 64 : VI;
+    if constexpr (!TAIL) {
+      const bool half = t * BN + BN > N;
+      const int ki = half ? 64 * KSL / 64 : KI;
+      const int vi = half ? 64 * VSL / 64 : VI;
 #pragma unroll
-    for (int c = 0; c < KC; ++c)
-      if (wu + NW * c < ki) lds_copy16(gk, koff[c], &lds_k[b][(wu + NW * c) * 512]);
+      for (int c = 0; c < KC; ++c)
+        if (wu + NW * c < ki) lds_copy16(gk, koff[c], &lds_k[b][(wu + NW * c) * 512]);
 #pragma unroll
-    for (int c = 0; c < VC; ++c)
-      if (wu + NW * c < vi) lds_copy16(gv, voff[c], &lds_v[b][(wu + NW * c) * 512]);
+      for (int c = 0; c < VC; ++c)
+        if (wu + NW * c < vi) lds_copy16(gv, voff[c], &lds_v[b][(wu + NW * c) * 512]);
+    } else {
+      const int lim = min(N - 1 - t * BN, BN - 1);   // last row of tile t inside the sequence
+#pragma unroll
+      for (int c = 0; c < KC; ++c)
+        if (wu + NW * c < KI) lds_copy16(gk, clamp_row(koff[c], lim), &lds_k[b][(wu + NW * c) * 512]);
+#pragma unroll
+      for (int c = 0; c < VC; ++c)
+        if (wu + NW * c < VI) lds_copy16(gv, clamp_row(voff[c], lim), &lds_v[b][(wu + NW * c) * 512]);
+    }
   };
   // Wait until at most one tile's copies (the most recent) are outstanding:
   // vmcnt counts this wave's copies in issue order.
@@ -235,7 +257,16 @@ __global__ __launch_bounds__(NW * 64, ATTN_FWD_MINW) void fwd_kernel(const typen
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) s[qb] = E::mfma32(kf[ks], qf[qb][ks], s[qb]);
     sched_fence();
-    // ---- causal mask (key > query -> -inf) on blocks that cross the diagonal
+    // ---- causal mask (key > query -> -inf) on blocks that cross the
+    // diagonal; without it, keys past the end of the sequence are masked
+    // (with it they lie above the diagonal of every stored row)
+    if (TAIL && !CAUSAL && kbk0 + 32 > N) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if (kbk0 + acc_row(j, h) >= N) s[qb][j] = -__builtin_inff();
+    }
     if (CAUSAL && kbk0 + 31 > qw0) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
@@ -354,6 +385,7 @@ __global__ __launch_bounds__(NW * 64, ATTN_FWD_MINW) void fwd_kernel(const typen
     const float l = xhalf_sum(l_run[qb]);
     const float inv = 1.0f / xhalf_sum(lr_run[qb]);
     const int q = qw0 + qb * 32 + r;
+    if (TAIL && q >= N) continue;   // rows past the end of the sequence
     T* orow = O + head + (size_t)q * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -370,7 +402,7 @@ __global__ __launch_bounds__(NW * 64, ATTN_FWD_MINW) void fwd_kernel(const typen
   }
 }
 
-template <typename E, int D, bool CAUSAL, int QB, int NW, int BN>
+template <typename E, int D, bool CAUSAL, int QB, int NW, int BN, bool TAIL>
 hipError_t launch_fwd_cfg(const FwdArgs& a) {
   constexpr int BM = NW * 32 * QB;
   const int BH = (int)(a.B * a.H);
@@ -385,14 +417,19 @@ hipError_t launch_fwd_cfg(const FwdArgs& a) {
   float* lse = a.lse;
   void* args[] = {(void*)&q, (void*)&k, (void*)&v, (void*)&o, (void*)&lse,
                   (void*)&BH, (void*)&N, (void*)&nqb, (void*)&scale_log2};
-  return launch_kernel((const void*)fwd_kernel<E, D, CAUSAL, QB, NW, BN>, grid, block, args, a.stream, 0);
+  return launch_kernel((const void*)fwd_kernel<E, D, CAUSAL, QB, NW, BN, TAIL>, grid, block, args, a.stream, 0);
 }
 
 template <typename E, int D>
 hipError_t launch_fwd_d(const FwdArgs& a) {
   constexpr int BN = ATTN_FWD_BN ? ATTN_FWD_BN : (D == 128 ? 128 : 64);
-  if (a.causal) return launch_fwd_cfg<E, D, true, ATTN_FWD_QB, ATTN_FWD_NW, BN>(a);
-  return launch_fwd_cfg<E, D, false, ATTN_FWD_QB, ATTN_FWD_NW, BN>(a);
+  constexpr int QB = ATTN_FWD_QB, NW = ATTN_FWD_NW;
+  if (a.N % 64 == 0) {
+    if (a.causal) return launch_fwd_cfg<E, D, true, QB, NW, BN, false>(a);
+    return launch_fwd_cfg<E, D, false, QB, NW, BN, false>(a);
+  }
+  if (a.causal) return launch_fwd_cfg<E, D, true, QB, NW, BN, true>(a);
+  return launch_fwd_cfg<E, D, false, QB, NW, BN, true>(a);
 }
 
 }  // namespace

@@ -35,12 +35,19 @@ struct BwdArgs {
   float scale;
   bool causal;
   int dtype;
-  // workspace parts
-  float* delta;   // [B,H,N] fp32: -D_i = -dO_i . O_i
-  float* lse2;    // [B,H,N] fp32: -lse_i * log2(e)
-  void* qt;       // [B,H,d,N] 16-bit: Q transposed (tokens in slot order per 16)
-  void* kt;       // [B,H,d,N] 16-bit: K transposed
-  void* dot;      // [B,H,d,N] 16-bit: dO transposed
+  // workspace parts; Np = N rounded up to a multiple of 64, entries for
+  // tokens N .. Np-1 are padding
+  float* delta;   // [B,H,Np] fp32: -D_i = -dO_i . O_i (0 for padding)
+  float* nlse;    // [B,H,Np] fp32: -lse_i / scale (-inf for padding)
+  void* qt;       // [B,H,d,Np] 16-bit: Q transposed (tokens in slot order per 16, padding 0)
+  void* kt;       // [B,H,d,Np] 16-bit: K transposed
+  void* dot;      // [B,H,d,Np] 16-bit: dO transposed
+  // [B,H,64,d] 16-bit: the last 64-token tile of Q, dO, K, V, zero past N;
+  // only when N is not a multiple of 64 (else NULL and never read)
+  void* qtail;
+  void* dotail;
+  void* ktail;
+  void* vtail;
   hipStream_t stream;
 };
 
@@ -56,10 +63,19 @@ int persistent_grid(const void* fn, int block, int units);
 hipError_t launch_fwd(const FwdArgs& a);
 hipError_t launch_bwd(const BwdArgs& a);
 
-// Workspace split used by attn_bwd: delta, lse2, then Q^T, K^T, dO^T, each
-// part starting on a 256-byte boundary.
+// Workspace split used by attn_bwd: delta, nlse, then Q^T, K^T, dO^T, then
+// (N not a multiple of 64) the tail tiles of Q, dO, K, V, each part starting
+// on a 256-byte boundary.
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-inline size_t bwd_delta_bytes(int64_t B, int64_t H, int64_t N) { return align256((size_t)(B * H * N) * 4); }
-inline size_t bwd_tcopy_bytes(int64_t B, int64_t H, int64_t N, int64_t d) { return align256((size_t)(B * H * N * d) * 2); }
+inline int64_t bwd_padded_n(int64_t N) { return (N + 63) / 64 * 64; }
+inline size_t bwd_delta_bytes(int64_t B, int64_t H, int64_t N) {
+  return align256((size_t)(B * H * bwd_padded_n(N)) * 4);
+}
+inline size_t bwd_tcopy_bytes(int64_t B, int64_t H, int64_t N, int64_t d) {
+  return align256((size_t)(B * H * bwd_padded_n(N) * d) * 2);
+}
+inline size_t bwd_tail_bytes(int64_t B, int64_t H, int64_t N, int64_t d) {
+  return N % 64 ? align256((size_t)(B * H * 64 * d) * 2) : 0;
+}
 
 }  // namespace attn

@@ -31,7 +31,9 @@
  *            calls (apart from the opt-in profiling window below and a
  *            per-device cache of the compute-unit count, read once and used
  *            to size the persistent backward grids).
- * Sizes:     B, H, N >= 1; d in {64, 128}; N a multiple of 64.
+ * Sizes:     B, H, N >= 1 (any N: a last tile that runs past the end of the
+ *            sequence is masked, never read past the inputs' end and never
+ *            stored past row N - 1); d in {64, 128}; N <= 2^24.
  * Streams:   work is enqueued on `stream` (a hipStream_t; NULL = the null
  *            stream) and the call returns without synchronising.
  * Errors:    every argument check runs before any HIP call: an argument
@@ -63,7 +65,7 @@ enum attn_status {
   ATTN_ERR_UNSUPPORTED_HEAD_DIM = 3,  /* d not in {64, 128} */
   ATTN_ERR_BAD_DTYPE = 4,             /* dtype not an attn_dtype value */
   ATTN_ERR_MISALIGNED = 5,            /* a pointer is not 16-byte aligned */
-  ATTN_ERR_UNSUPPORTED_SEQLEN = 6,    /* N not a multiple of 64 */
+  ATTN_ERR_UNSUPPORTED_SEQLEN = 6,    /* reserved; no longer returned (any N >= 1 is accepted) */
   ATTN_ERR_BAD_SCALE = 7,             /* scale NaN, infinite or <= 0 */
   ATTN_ERR_WORKSPACE_TOO_SMALL = 8,   /* workspace NULL or below attn_bwd_workspace_bytes() */
   ATTN_ERR_ALIASING = 9,              /* an output overlaps an input or another output */
@@ -85,12 +87,15 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int dtype, void* stream);
 
 /*
- * attn_bwd_workspace_bytes - size of the scratch buffer attn_bwd needs:
- * two fp32 per query row (-D_i = -dO_i . O_i and -lse_i * log2(e)) plus three
- * 16-bit [B,H,d,N] transposed copies of Q, K and dO, each part rounded up to
- * 256 bytes: 8*B*H*N + 6*B*H*N*d bytes.  It grows as O(B*H*N*d), never with N^2 (the
- * memory bound of page "突破单卡显存极限…" §2.2).  Returns 0 when the sizes
- * are invalid (B, H, N < 1, d not in {64,128}, or overflow).
+ * attn_bwd_workspace_bytes - size of the scratch buffer attn_bwd needs.  With
+ * Np = N rounded up to a multiple of 64: two fp32 per padded query row
+ * (-D_i = -dO_i . O_i and -lse_i / scale) plus three 16-bit [B,H,d,Np]
+ * transposed copies of Q, K and dO; when N is not a multiple of 64, also four
+ * 16-bit [B,H,64,d] copies of the last, zero-padded 64-token tile of Q, dO,
+ * K and V.  Each part is rounded up to 256 bytes: about 8*B*H*Np +
+ * 6*B*H*Np*d (+ 512*B*H*d) bytes.  It grows as O(B*H*N*d), never with N^2
+ * (the memory bound of page "突破单卡显存极限…" §2.2).  Returns 0 when the
+ * sizes are invalid (B, H, N < 1, d not in {64,128}, or overflow).
  */
 size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d);
 

@@ -55,6 +55,13 @@ def test_workspace_bytes():
     assert ea.attn_bwd_workspace_bytes(4, 32, 4096, 128) == 2 * 4 * 32 * 4096 * 4 + 3 * 4 * 32 * 4096 * 128 * 2
     n = 32768
     assert ea.attn_bwd_workspace_bytes(1, 16, n, 128) < 16 * n * (8 + 6 * 128) + 1024  # O(N d), never N^2
+    # any N: [B,H,Np] and [B,H,d,Np] with Np = N rounded up to 64, plus, when
+    # N is not a multiple of 64, four 16-bit [B,H,64,d] tail tiles
+    assert ea.attn_bwd_workspace_bytes(1, 1, 100, 64) == 2 * 512 + 3 * 128 * 64 * 2 + 4 * 64 * 64 * 2
+    assert ea.attn_bwd_workspace_bytes(1, 1, 1, 128) == 2 * 256 + 3 * 64 * 128 * 2 + 4 * 64 * 128 * 2
+    assert ea.attn_bwd_workspace_bytes(3, 5, 4095, 128) == (2 * 3 * 5 * 4096 * 4 + 3 * 3 * 5 * 4096 * 128 * 2
+                                                            + 4 * 3 * 5 * 64 * 128 * 2)
+    assert ea.attn_bwd_workspace_bytes(1, 3, 1, 64) == 2 * 768 + 3 * 3 * 64 * 64 * 2 + 4 * 3 * 64 * 64 * 2
     for bad in [(0, 1, 64, 64), (1, 0, 64, 64), (1, 1, 0, 64), (1, 1, 64, 96), (1, 1, 64, -1),
                 (1 << 40, 1 << 20, 1 << 20, 128)]:
         assert ea.attn_bwd_workspace_bytes(*bad) == 0, bad
@@ -80,7 +87,7 @@ def test_fwd_null(lib, which):
     (dict(B=0), SHAPE), (dict(H=-1), SHAPE), (dict(N=0), SHAPE), (dict(B=1 << 40, H=1 << 20), SHAPE),
     (dict(d=96), HEADDIM), (dict(d=256), HEADDIM), (dict(d=32), HEADDIM),
     (dict(dtype=2), DTYPE), (dict(dtype=-1), DTYPE),
-    (dict(N=100), SEQ), (dict(N=65), SEQ),
+    (dict(N=(1 << 24) + 1), SHAPE), (dict(N=-5), SHAPE),
     (dict(scale=float("nan")), SCALE), (dict(scale=float("inf")), SCALE), (dict(scale=0.0), SCALE),
     (dict(scale=-0.1), SCALE),
     (dict(q=P[0] + 8), ALIGN), (dict(lse=P[4] + 4), ALIGN), (dict(o=P[3] + 2), ALIGN),
@@ -96,9 +103,10 @@ def test_bwd_null(lib, which):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(B=0), SHAPE), (dict(d=80), HEADDIM), (dict(dtype=7), DTYPE), (dict(N=96), SEQ),
+    (dict(B=0), SHAPE), (dict(d=80), HEADDIM), (dict(dtype=7), DTYPE), (dict(N=0), SHAPE),
     (dict(scale=float("-inf")), SCALE),
     (dict(ws=None), WS), (dict(ws_bytes=100), WS),
+    (dict(N=100, ws_bytes=2 * 1024 + 3 * 2 * 128 * 64 * 2), WS),   # ragged N without room for the tail tiles
     (dict(dq=P[6] + 8), ALIGN), (dict(ws=P[9] + 16), ALIGN),
     (dict(dq=P[0]), ALIAS), (dict(dk=P[6]), ALIAS), (dict(ws=P[8]), ALIAS), (dict(dv=P[5]), ALIAS),
 ])
