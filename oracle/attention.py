@@ -34,6 +34,16 @@ plain definition.
 Readings where the pages are silent: the causal mask is top-left aligned
 with the diagonal kept; lse is in natural log; dropout is 0; the backward pass
 differentiates O only (lse receives no gradient).
+
+Query and key counts may differ (``Nq`` rows of Q against ``Nk`` rows of K and
+V), the shape of decoding against a KV cache [page "FlashAttention技术解析
+如何让GPT训练速度提升5-9倍", §4.1: the keys and values of earlier positions
+are kept and reused].  The pages give no mask for that case; the reading
+here is that the ``Nq`` queries are the last ``Nq`` positions of the
+sequence whose ``Nk`` keys are cached, so causal query ``i`` sees keys
+``j <= i + (Nk - Nq)`` (bottom-right alignment).  With ``Nq == Nk`` this is
+the top-left mask above.  Causal with ``Nk < Nq`` leaves rows with no
+visible key and is not defined.
 """
 from __future__ import annotations
 
@@ -61,8 +71,9 @@ def _f64(x) -> np.ndarray:
 def masked_scores(q, k, scale: float, causal: bool, rows: Optional[np.ndarray] = None) -> np.ndarray:
     """S = scale * Q K^T for the given query rows (all rows by default).
 
-    Causal reading: query i sees keys j <= i (top-left alignment, diagonal
-    kept); every other entry is -inf.
+    Causal reading: query i sees keys j <= i + (Nk - Nq), i.e. j <= i
+    (top-left, diagonal kept) when Q and K have the same number of rows, and
+    the queries are the last Nq positions otherwise; every other entry is -inf.
     """
     q = _f64(q)
     k = _f64(k)
@@ -73,7 +84,7 @@ def masked_scores(q, k, scale: float, causal: bool, rows: Optional[np.ndarray] =
     s = float(scale) * (q[rows] @ k.T)
     if causal:
         cols = np.arange(k.shape[0])
-        s[cols[None, :] > rows[:, None]] = -np.inf
+        s[cols[None, :] > rows[:, None] + (k.shape[0] - n)] = -np.inf
     return s
 
 
@@ -148,7 +159,7 @@ def _heads(x) -> Iterable[Tuple[int, int]]:
 
 
 def forward(q, k, v, scale: float, causal: bool, row_block: Optional[int] = None):
-    """O [B,H,N,d] and lse [B,H,N] over all heads."""
+    """O [B,H,Nq,d] and lse [B,H,Nq] over all heads (K, V: [B,H,Nk,d])."""
     q = _f64(q)
     b, h, n, d = q.shape
     o = np.empty((b, h, n, np.shape(v)[3]))
@@ -196,7 +207,7 @@ def online_softmax_forward_head(q, k, v, scale: float, causal: bool, block: int)
         cols = np.arange(c0, min(nk, c0 + block))
         x = float(scale) * (q @ k[cols].T)
         if causal:
-            x[cols[None, :] > np.arange(n)[:, None]] = -np.inf
+            x[cols[None, :] > np.arange(n)[:, None] + (nk - n)] = -np.inf
         m_j = x.max(axis=1)
         seen = m_j > -np.inf                      # rows with at least one visible key
         f_j = np.zeros_like(x)
@@ -222,7 +233,7 @@ def scalar_forward_head(q, k, v, scale: float, causal: bool):
     o = [[0.0] * dv for _ in range(n)]
     lse = [0.0] * n
     for i in range(n):
-        js = [j for j in range(len(k)) if (not causal or j <= i)]
+        js = [j for j in range(len(k)) if (not causal or j <= i + len(k) - n)]
         s = [float(scale) * math.fsum(float(q[i][c]) * float(k[j][c]) for c in range(d)) for j in js]
         mx = max(s)
         e = [math.exp(x - mx) for x in s]

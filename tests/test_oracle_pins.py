@@ -310,3 +310,110 @@ def test_planted_backward_mistake_is_caught(kind):
         except (AssertionError, FloatingPointError, ValueError, IndexError):
             caught.append(pin.__name__)
     assert caught, f"planted backward mistake {kind!r} passed every pin"
+
+
+# ---------------------------------------------------------------- KV-cache shapes (Nq != Nk)
+# Reading (the pages are silent on the mask when Q has fewer rows than K):
+# the Nq queries are the last Nq positions of the sequence whose Nk keys are
+# cached, so causal query i sees keys j <= i + Nk - Nq.  The pins tie that
+# reading to the square case (pinned above) and to closed forms.
+
+def pin_kv_suffix_of_square(fwd):
+    """Decoding the last Nq positions gives the last Nq rows of the square causal result."""
+    rng = np.random.default_rng(21)
+    nk, d = 13, 5
+    q, k, v = _rand(rng, nk, d)
+    o_full, lse_full = oracle.forward_head(q, k, v, 0.6, True)
+    for nq in (1, 2, 5, 13):
+        o, lse = fwd(q[nk - nq:], k, v, 0.6, True)
+        np.testing.assert_allclose(o, o_full[nk - nq:], rtol=0, atol=1e-13)
+        np.testing.assert_allclose(lse, lse_full[nk - nq:], rtol=0, atol=1e-13)
+
+
+def pin_kv_last_position_sees_all(fwd):
+    """A single causal query (the newest position) attends to every cached key."""
+    rng = np.random.default_rng(22)
+    q, k, v = _rand(rng, 9, 4)
+    o_c, lse_c = fwd(q[:1], k, v, 0.9, True)
+    o_n, lse_n = fwd(q[:1], k, v, 0.9, False)
+    np.testing.assert_allclose(o_c, o_n, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse_c, lse_n, rtol=0, atol=1e-13)
+
+
+def pin_kv_uniform_prefix_mean(fwd):
+    """Q = 0: query i of Nq sees keys 0 .. i + Nk - Nq, so O_i is their V mean and lse_i = ln(count)."""
+    rng = np.random.default_rng(23)
+    nq, nk, d = 3, 8, 4
+    _, k, v = _rand(rng, nk, d)
+    q = np.zeros((nq, d))
+    o, lse = fwd(q, k, v, 1.3, True)
+    cnt = np.arange(nq) + nk - nq + 1
+    mean = np.stack([v[:c].mean(0) for c in cnt])
+    np.testing.assert_allclose(o, mean, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse, np.log(cnt), rtol=0, atol=1e-13)
+
+
+KV_PINS = [pin_kv_suffix_of_square, pin_kv_last_position_sees_all, pin_kv_uniform_prefix_mean]
+
+
+@pytest.mark.parametrize("pin", KV_PINS, ids=[p.__name__ for p in KV_PINS])
+def test_oracle_kv_pin(pin):
+    pin(oracle.forward_head)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_kv_scalar_and_recurrence_agree(causal):
+    """Scalar brute force and the blockwise recurrence agree with the vectorised oracle for Nq != Nk."""
+    rng = np.random.default_rng(24)
+    for nq, nk in ((1, 1), (1, 6), (3, 7), (4, 4), (2, 9)):
+        q = rng.standard_normal((nq, 3))
+        k = rng.standard_normal((nk, 3))
+        v = rng.standard_normal((nk, 2))
+        o, lse = oracle.forward_head(q, k, v, 0.7, causal)
+        o_s, lse_s = oracle.scalar_forward_head(q.tolist(), k.tolist(), v.tolist(), 0.7, causal)
+        np.testing.assert_allclose(o, o_s, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse, lse_s, rtol=0, atol=1e-12)
+        for block in (1, 2, 5):
+            o_b, lse_b = oracle.online_softmax_forward_head(q, k, v, 0.7, causal, block)
+            np.testing.assert_allclose(o_b, o, rtol=0, atol=1e-12)
+            np.testing.assert_allclose(lse_b, lse, rtol=0, atol=1e-12)
+
+
+def test_key_split_partials_merge_by_lse():
+    """Attention over disjoint key ranges merges exactly: O = sum_s e^(lse_s - lse) O_s,
+    lse = ln sum_s e^(lse_s).  This is what makes a split over keys exact."""
+    rng = np.random.default_rng(25)
+    q = rng.standard_normal((4, 6)) * 2
+    k = rng.standard_normal((23, 6)) * 2
+    v = rng.standard_normal((23, 5))
+    o_ref, lse_ref = oracle.forward_head(q, k, v, 0.5, False)
+    parts = [oracle.forward_head(q, k[a:b], v[a:b], 0.5, False) for a, b in ((0, 5), (5, 6), (6, 23))]
+    lse = np.logaddexp.reduce(np.stack([p[1] for p in parts]), axis=0)
+    o = sum(np.exp(p[1] - lse)[:, None] * p[0] for p in parts)
+    np.testing.assert_allclose(o, o_ref, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse, lse_ref, rtol=0, atol=1e-13)
+
+
+def _mut_kv_fwd(kind):
+    def fwd(q, k, v, scale, causal):
+        s = float(scale) * (q @ k.T)
+        nq, nk = q.shape[0], k.shape[0]
+        if causal:
+            j, i = np.meshgrid(np.arange(nk), np.arange(nq))
+            off = {"top_left": 0, "offset_sign": -(nk - nq), "off_by_one": nk - nq - 1}[kind]
+            s[j > i + off] = -np.inf
+        with np.errstate(invalid="ignore"):
+            p, m, l = A.row_softmax(s)
+        return p @ v, m + np.log(l)
+    return fwd
+
+
+@pytest.mark.parametrize("kind", ["top_left", "offset_sign", "off_by_one"])
+def test_planted_kv_mask_mistake_is_caught(kind):
+    caught = []
+    for pin in KV_PINS:
+        try:
+            pin(_mut_kv_fwd(kind))
+        except (AssertionError, FloatingPointError, ValueError, IndexError):
+            caught.append(pin.__name__)
+    assert caught, f"planted KV-cache mask mistake {kind!r} passed every pin"
