@@ -16,6 +16,9 @@ from ._binding import (  # noqa: F401
     attn_bwd,
     attn_bwd_workspace_bytes,
     attn_fwd,
+    attn_fwd_kvcache,
+    attn_fwd_kvcache_splits,
+    attn_fwd_kvcache_workspace_bytes,
     attn_last_hip_error,
     attn_profile_start,
     attn_profile_stop,
@@ -23,5 +26,6 @@ from ._binding import (  # noqa: F401
     backward,
     default_scale,
     forward,
+    forward_kvcache,
     load,
 )

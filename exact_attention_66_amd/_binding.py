@@ -24,10 +24,11 @@ STATUS_NAMES = {
     4: "ATTN_ERR_BAD_DTYPE", 5: "ATTN_ERR_MISALIGNED", 6: "ATTN_ERR_UNSUPPORTED_SEQLEN",
     7: "ATTN_ERR_BAD_SCALE", 8: "ATTN_ERR_WORKSPACE_TOO_SMALL", 9: "ATTN_ERR_ALIASING", 10: "ATTN_ERR_HIP",
 }
-EXPORTED = ["attn_fwd", "attn_bwd_workspace_bytes", "attn_bwd", "attn_profile_start", "attn_profile_stop",
-            "attn_status_string", "attn_last_hip_error"]
+EXPORTED = ["attn_fwd", "attn_bwd_workspace_bytes", "attn_bwd", "attn_fwd_kvcache",
+            "attn_fwd_kvcache_workspace_bytes", "attn_fwd_kvcache_splits", "attn_profile_start",
+            "attn_profile_stop", "attn_status_string", "attn_last_hip_error"]
 # attn_kernel_kind values
-KERNEL_KINDS = ["fwd", "bwd_prep", "bwd_dkdv", "bwd_dq"]
+KERNEL_KINDS = ["fwd", "bwd_prep", "bwd_dkdv", "bwd_dq", "kv_split", "kv_merge"]
 
 _lib = None
 
@@ -58,6 +59,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_bwd_workspace_bytes.restype = sz
     lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, f32, i32, i32, vp, sz, vp]
     lib.attn_bwd.restype = i32
+    lib.attn_fwd_kvcache.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, f32, i32, i32, i32, vp, sz, vp]
+    lib.attn_fwd_kvcache.restype = i32
+    lib.attn_fwd_kvcache_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i32]
+    lib.attn_fwd_kvcache_workspace_bytes.restype = sz
+    lib.attn_fwd_kvcache_splits.argtypes = [i64, i64, i64, i64, i64, i32]
+    lib.attn_fwd_kvcache_splits.restype = i32
     lib.attn_profile_start.argtypes = []
     lib.attn_profile_start.restype = i32
     lib.attn_profile_stop.argtypes = [ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double)]
@@ -97,6 +104,14 @@ def attn_profile_stop() -> dict:
 
 def attn_bwd_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
     return int(load().attn_bwd_workspace_bytes(B, H, N, d))
+
+
+def attn_fwd_kvcache_workspace_bytes(B: int, H: int, Nq: int, Nk: int, d: int, num_splits: int = 0) -> int:
+    return int(load().attn_fwd_kvcache_workspace_bytes(B, H, Nq, Nk, d, int(num_splits)))
+
+
+def attn_fwd_kvcache_splits(B: int, H: int, Nq: int, Nk: int, d: int, num_splits: int = 0) -> int:
+    return int(load().attn_fwd_kvcache_splits(B, H, Nq, Nk, d, int(num_splits)))
 
 
 def _dtype_code(t: torch.Tensor) -> int:
@@ -159,6 +174,25 @@ def attn_bwd(q, k, v, o, dO, lse, dq, dk, dv, scale: float, causal: bool, worksp
         raise AttnError(st, "attn_bwd")
 
 
+def attn_fwd_kvcache(q, k, v, o, lse, scale: float, causal: bool, workspace, num_splits: int = 0,
+                     stream=None) -> None:
+    """Enqueue the KV-cache forward: q, o [B,H,Nq,d], k, v [B,H,Nk,d], lse [B,H,Nq] fp32."""
+    B, H, Nq, d = _shape4(q)
+    Nk = int(k.shape[2]) if k.dim() == 4 else -1
+    if tuple(k.shape) != (B, H, Nk, d) or tuple(v.shape) != (B, H, Nk, d) or tuple(o.shape) != (B, H, Nq, d):
+        raise ValueError("q, o must be [B,H,Nq,d] and k, v [B,H,Nk,d]")
+    if any(t.dtype != q.dtype for t in (k, v, o)):
+        raise ValueError("q, k, v and o must share the dtype")
+    if tuple(lse.shape) != (B, H, Nq) or lse.dtype != torch.float32:
+        raise ValueError("lse must be a float32 [B, H, Nq] tensor")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = load().attn_fwd_kvcache(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk, d, float(scale),
+                                 int(bool(causal)), _dtype_code(q), int(num_splits), _ptr(workspace), ws_bytes,
+                                 _stream(stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fwd_kvcache")
+
+
 # ------------------------------------------------------------------ conveniences
 def default_scale(d: int) -> float:
     """fp32(1/sqrt(d)), the default softmax scale."""
@@ -185,3 +219,18 @@ def backward(q, k, v, o, lse, dO, scale: Optional[float] = None, causal: bool = 
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     attn_bwd(q, k, v, o, dO, lse, dq, dk, dv, scale, causal, workspace, stream)
     return dq, dk, dv
+
+
+def forward_kvcache(q, k, v, scale: Optional[float] = None, causal: bool = False, num_splits: int = 0,
+                    workspace=None, stream=None):
+    """Allocate (o, lse) and, if not given, the workspace; run attn_fwd_kvcache."""
+    B, H, Nq, d = _shape4(q)
+    Nk = int(k.shape[2])
+    scale = default_scale(d) if scale is None else scale
+    if workspace is None:
+        workspace = torch.empty(attn_fwd_kvcache_workspace_bytes(B, H, Nq, Nk, d, num_splits), dtype=torch.uint8,
+                                device=q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    attn_fwd_kvcache(q, k, v, o, lse, scale, causal, workspace, num_splits, stream)
+    return o, lse

@@ -113,6 +113,67 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
   return launch_status(attn::launch_bwd(a));
 }
 
+// Sizes of a KV-cache call: both lengths as in check_common (B*H*ceil(len/64)
+// units fit a launch), plus the split grid and the merge rows.
+int check_kvcache(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale, int causal, int dtype,
+                  int num_splits) {
+  int st = check_common(B, H, Nq, d, scale, dtype);
+  if (st != ATTN_OK) return st;
+  st = check_common(B, H, Nk, d, scale, dtype);
+  if (st != ATTN_OK) return st;
+  if (causal && Nk < Nq) return ATTN_ERR_BAD_SHAPE;   // rows with no visible key
+  if (num_splits < 0 || num_splits > 4096) return ATTN_ERR_BAD_SHAPE;
+  int P = 1, chunk = 32;
+  attn::kv_split_plan(B * H, Nq, Nk, num_splits, &P, &chunk);
+  if (B * H * ((Nq + 31) / 32) * P > (int64_t)INT32_MAX || B * H * Nq > (int64_t)INT32_MAX - 3) return ATTN_ERR_BAD_SHAPE;
+  if (checked_elems(B * H, Nq, P, d) < 0) return ATTN_ERR_BAD_SHAPE;
+  return ATTN_OK;
+}
+
+size_t attn_fwd_kvcache_workspace_bytes(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int num_splits) {
+  if (check_kvcache(B, H, Nq, Nk, d, 1.0f, 0, ATTN_DTYPE_BF16, num_splits) != ATTN_OK) return 0;
+  int P = 1, chunk = 32;
+  attn::kv_split_plan(B * H, Nq, Nk, num_splits, &P, &chunk);
+  return attn::kv_acc_bytes(B * H, Nq, P, d) + attn::kv_stat_bytes(B * H, Nq, P);
+}
+
+int attn_fwd_kvcache_splits(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int num_splits) {
+  if (check_kvcache(B, H, Nq, Nk, d, 1.0f, 0, ATTN_DTYPE_BF16, num_splits) != ATTN_OK) return 0;
+  int P = 1, chunk = 32;
+  attn::kv_split_plan(B * H, Nq, Nk, num_splits, &P, &chunk);
+  return P;
+}
+
+int attn_fwd_kvcache(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                     int64_t Nq, int64_t Nk, int64_t d, float scale, int causal, int dtype, int num_splits,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL_PTR;
+  int st = check_kvcache(B, H, Nq, Nk, d, scale, causal, dtype, num_splits);
+  if (st != ATTN_OK) return st;
+  const size_t need = attn_fwd_kvcache_workspace_bytes(B, H, Nq, Nk, d, num_splits);
+  if (need == 0) return ATTN_ERR_BAD_SHAPE;
+  if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE_TOO_SMALL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return ATTN_ERR_MISALIGNED;
+  const size_t qb = (size_t)(B * H * Nq * d) * 2, kb = (size_t)(B * H * Nk * d) * 2, lb = (size_t)(B * H * Nq) * 4;
+  struct R { const void* p; size_t n; };
+  const R ins[] = {{q, qb}, {k, kb}, {v, kb}};
+  const R outs[] = {{o, qb}, {lse, lb}, {workspace, need}};
+  for (const R& x : outs) {
+    for (const R& y : ins)
+      if (overlaps(x.p, x.n, y.p, y.n)) return ATTN_ERR_ALIASING;
+    for (const R& y : outs)
+      if (&x != &y && overlaps(x.p, x.n, y.p, y.n)) return ATTN_ERR_ALIASING;
+  }
+  int P = 1, chunk = 32;
+  attn::kv_split_plan(B * H, Nq, Nk, num_splits, &P, &chunk);
+  char* ws = (char*)workspace;
+  attn::KvArgs a{q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal != 0, dtype, P, chunk,
+                 (float*)ws, (float*)(ws + attn::kv_acc_bytes(B * H, Nq, P, d)), (hipStream_t)stream};
+  return launch_status(attn::launch_kvcache(a));
+}
+
 const char* attn_status_string(int status) {
   switch (status) {
     case ATTN_OK: return "ok";

@@ -51,6 +51,47 @@ struct BwdArgs {
   hipStream_t stream;
 };
 
+// Forward for KV-cache shapes: Nq queries against Nk keys, the key axis cut
+// into `splits` ranges of `chunk` keys (a multiple of 32), each computed by
+// its own wave, then merged.
+struct KvArgs {
+  const void* q;   // [B,H,Nq,d]
+  const void* k;   // [B,H,Nk,d]
+  const void* v;   // [B,H,Nk,d]
+  void* o;         // [B,H,Nq,d]
+  float* lse;      // [B,H,Nq]
+  int64_t B, H, Nq, Nk, d;
+  float scale;
+  bool causal;     // query i sees keys j <= i + Nk - Nq
+  int dtype;
+  int splits;
+  int chunk;
+  float* part_acc;   // workspace [B,H,Nq,splits,d] fp32: unnormalised O of each split
+  float* part_stat;  // workspace [B,H,Nq,splits,4] fp32: m (log2 units), l, rounded l, unused
+  hipStream_t stream;
+};
+
+// Split plan: `requested` splits (0: about 2048 waves in all, at least 128
+// keys per split), then the keys per split rounded up to a multiple of 32
+// and the split count recomputed from it, so that no split is empty unless
+// the causal mask empties it.  A pure function of the sizes: the workspace
+// size and the launch agree on it.
+inline void kv_split_plan(int64_t BH, int64_t Nq, int64_t Nk, int requested, int* splits, int* chunk) {
+  const int64_t units = BH * ((Nq + 31) / 32);
+  int64_t P = requested;
+  if (P <= 0) {
+    P = (2048 + units - 1) / units;
+    const int64_t cap = (Nk + 127) / 128;
+    if (P > cap) P = cap;
+  }
+  if (P < 1) P = 1;
+  if (P > 4096) P = 4096;
+  int64_t c = (Nk + P - 1) / P;
+  c = (c + 31) / 32 * 32;
+  *chunk = (int)c;
+  *splits = (int)((Nk + c - 1) / c);
+}
+
 // hipLaunchKernel, or an event-timed launch while a profiling window is open;
 // kind is an attn_kernel_kind value.
 hipError_t launch_kernel(const void* fn, dim3 grid, dim3 block, void** args, hipStream_t stream, int kind);
@@ -62,6 +103,7 @@ int persistent_grid(const void* fn, int block, int units);
 
 hipError_t launch_fwd(const FwdArgs& a);
 hipError_t launch_bwd(const BwdArgs& a);
+hipError_t launch_kvcache(const KvArgs& a);
 
 // Workspace split used by attn_bwd: delta, nlse, then Q^T, K^T, dO^T, then
 // (N not a multiple of 64) the tail tiles of Q, dO, K, V, each part starting
@@ -73,6 +115,12 @@ inline size_t bwd_delta_bytes(int64_t B, int64_t H, int64_t N) {
 }
 inline size_t bwd_tcopy_bytes(int64_t B, int64_t H, int64_t N, int64_t d) {
   return align256((size_t)(B * H * bwd_padded_n(N) * d) * 2);
+}
+inline size_t kv_acc_bytes(int64_t BH, int64_t Nq, int splits, int64_t d) {
+  return align256((size_t)(BH * Nq * splits * d) * 4);
+}
+inline size_t kv_stat_bytes(int64_t BH, int64_t Nq, int splits) {
+  return align256((size_t)(BH * Nq * splits) * 16);
 }
 inline size_t bwd_tail_bytes(int64_t B, int64_t H, int64_t N, int64_t d) {
   return N % 64 ? align256((size_t)(B * H * 64 * d) * 2) : 0;

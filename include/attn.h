@@ -118,13 +118,61 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o,
              int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal,
              int dtype, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * KV-cache forward: Nq new queries against Nk cached keys and values
+ * (decoding one or a few tokens), the reuse of earlier positions' keys and
+ * values described on page "FlashAttention技术解析 如何让GPT训练速度提升5-9倍"
+ * §4.1, computed exactly as attn_fwd computes the square case.
+ *
+ * attn_fwd_kvcache - forward pass with Q shorter than K.
+ *   q        [B,H,Nq,d] queries.
+ *   k, v     [B,H,Nk,d] cached keys and values (read only).
+ *   o        [B,H,Nq,d] output, same dtype; lse [B,H,Nq] fp32 (natural log).
+ *   causal   nonzero = the queries are the last Nq positions of the
+ *            sequence: query i sees keys j <= i + Nk - Nq (bottom-right;
+ *            for Nq == Nk the same mask as attn_fwd).  Requires Nk >= Nq.
+ *   num_splits  key splits: the key axis is cut into about this many ranges,
+ *            each computed by its own wave and merged afterwards (the merge
+ *            by per-range maxima and sums is exact).  0 = chosen by the
+ *            library from the sizes; at most 4096; ranges are whole 32-key
+ *            blocks, so fewer are used when Nk is short.
+ *   workspace  device buffer of at least attn_fwd_kvcache_workspace_bytes()
+ *            bytes for the same sizes and num_splits, 256-byte aligned;
+ *            overwritten.  Concurrent calls need distinct workspaces.
+ * Other conventions as above (16-byte aligned pointers, no overlap between
+ * outputs, workspace and inputs, checks before any HIP call, asynchronous).
+ * Any Nq, Nk >= 1; the kernels are built for Nq much smaller than Nk
+ * (their cost is one pass over K and V per 32 queries).
+ * Returns ATTN_OK or an attn_status error code (ATTN_ERR_BAD_SHAPE also for
+ * causal with Nk < Nq and for num_splits outside 0..4096).
+ */
+int attn_fwd_kvcache(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale,
+                     int causal, int dtype, int num_splits, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/*
+ * attn_fwd_kvcache_workspace_bytes - workspace of attn_fwd_kvcache: per
+ * query row and split, d fp32 partial sums plus 4 fp32 statistics, each part
+ * rounded up to 256 bytes (about 4*B*H*Nq*P*(d+4) bytes for P splits).
+ * Returns 0 for invalid sizes.
+ */
+size_t attn_fwd_kvcache_workspace_bytes(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                                        int num_splits);
+
+/* attn_fwd_kvcache_splits - the number of key splits a call with these sizes
+ * uses (0 for invalid sizes). */
+int attn_fwd_kvcache_splits(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int num_splits);
+
 /* Kernels the library launches, as counted by the profiling window below. */
 enum attn_kernel_kind {
   ATTN_KERNEL_FWD = 0,         /* forward: O and lse */
   ATTN_KERNEL_BWD_PREP = 1,    /* backward: D = rowsum(dO * O), transposed Q, K, dO */
   ATTN_KERNEL_BWD_DKDV = 2,    /* backward: recompute per key block, dK and dV */
   ATTN_KERNEL_BWD_DQ = 3,      /* backward: recompute per query block, dQ */
-  ATTN_KERNEL_KINDS = 4,
+  ATTN_KERNEL_KV_SPLIT = 4,    /* KV-cache forward: one key range per wave */
+  ATTN_KERNEL_KV_MERGE = 5,    /* KV-cache forward: merge of the ranges, O and lse */
+  ATTN_KERNEL_KINDS = 6,
 };
 
 /*

@@ -119,3 +119,53 @@ def test_python_binding_rejects_noncontiguous():
     q = torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16).transpose(2, 3)
     with pytest.raises(ValueError):
         ea._binding._ptr(q)
+
+
+# ---------------------------------------------------------------- KV-cache forward
+
+def test_kvcache_split_plan_and_workspace():
+    # decode, 128 heads, 4096 keys: about 2048 waves -> 16 splits of 256 keys
+    assert ea.attn_fwd_kvcache_splits(4, 32, 1, 4096, 128) == 16
+    assert ea.attn_fwd_kvcache_workspace_bytes(4, 32, 1, 4096, 128) == 128 * 16 * 128 * 4 + 128 * 16 * 16
+    # at least 128 keys per automatic split; a requested count is cut to whole 32-key blocks
+    assert ea.attn_fwd_kvcache_splits(1, 1, 1, 300, 64) == 3
+    assert ea.attn_fwd_kvcache_splits(1, 1, 1, 100, 64, 1000) == 4
+    assert ea.attn_fwd_kvcache_splits(1, 1, 1, 100, 64, 3) == 2      # 34 keys per split -> 64: 2 splits
+    assert ea.attn_fwd_kvcache_splits(1, 1, 1, 1, 128) == 1
+    assert ea.attn_fwd_kvcache_workspace_bytes(1, 1, 1, 1, 64, 1) == 256 + 256
+    # 40 queries = 2 query blocks of 32
+    assert ea.attn_fwd_kvcache_splits(2, 2, 40, 8192, 128) == 64
+    for bad in [(0, 1, 1, 64, 64, 0), (1, 1, 0, 64, 64, 0), (1, 1, 1, 0, 64, 0), (1, 1, 1, 64, 96, 0),
+                (1, 1, 1, 64, 64, -1), (1, 1, 1, 64, 64, 4097)]:
+        assert ea.attn_fwd_kvcache_workspace_bytes(*bad) == 0, bad
+        assert ea.attn_fwd_kvcache_splits(*bad) == 0, bad
+
+
+def kvf(lib, q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=1, H=2, Nq=4, Nk=300, d=64, scale=0.125, causal=1,
+        dtype=0, splits=0, ws=P[5], ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = 1 << 24
+    return lib.attn_fwd_kvcache(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, dtype, splits, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "o", "lse"])
+def test_kvcache_null(lib, which):
+    assert kvf(lib, **{which: None}) == NULL
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), SHAPE), (dict(Nq=0), SHAPE), (dict(Nk=0), SHAPE), (dict(Nq=301, Nk=300), SHAPE),
+    (dict(splits=-2), SHAPE), (dict(splits=5000), SHAPE), (dict(Nk=(1 << 24) + 1), SHAPE),
+    (dict(d=32), HEADDIM), (dict(dtype=3), DTYPE), (dict(scale=float("nan")), SCALE),
+    (dict(ws=None), WS), (dict(ws_bytes=100), WS),
+    (dict(q=P[0] + 2), ALIGN), (dict(ws=P[5] + 16), ALIGN),
+    (dict(o=P[0]), ALIAS), (dict(lse=P[2] + 32), ALIAS), (dict(ws=P[3]), ALIAS), (dict(o=P[4]), ALIAS),
+])
+def test_kvcache_rejects(lib, kw, code):
+    assert kvf(lib, **kw) == code
+
+
+def test_kvcache_noncausal_allows_more_queries_than_keys(lib):
+    # non-causal with Nq > Nk is defined (every query sees every key); the
+    # call still fails here, but only at the (fake) workspace size check
+    assert kvf(lib, Nq=500, Nk=300, causal=0, ws_bytes=16) == WS

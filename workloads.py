@@ -112,6 +112,71 @@ def make_inputs(w: Workload, *, with_grad: Optional[bool] = None):
     return out
 
 
+@dataclasses.dataclass(frozen=True)
+class KvWorkload:
+    """Decoding against a KV cache: Nq new queries per head, Nk cached keys and values."""
+    name: str
+    B: int
+    H: int
+    Nq: int
+    Nk: int
+    d: int
+    dtype: str
+    causal: bool        # the queries are the last Nq positions (query i sees keys <= i + Nk - Nq)
+    seed: int
+    qk_gain: float = 1.0
+    description: str = ""
+
+    @property
+    def scale(self) -> float:
+        return float(torch.tensor(1.0 / math.sqrt(self.d), dtype=torch.float32).item())
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return {"bf16": torch.bfloat16, "fp16": torch.float16}[self.dtype]
+
+    def kv_bytes(self) -> int:
+        """K and V bytes: the one pass over the cache that bounds the call."""
+        return 2 * self.B * self.H * self.Nk * self.d * 2
+
+    def io_bytes(self) -> int:
+        """All algorithmic HBM bytes: K, V and Q read, O written (16-bit), lse written (fp32)."""
+        return self.kv_bytes() + 2 * self.B * self.H * self.Nq * self.d * 2 + 4 * self.B * self.H * self.Nq
+
+    def with_size(self, **kw) -> "KvWorkload":
+        return dataclasses.replace(self, **kw)
+
+
+# The head shapes of the training workloads above, one or a few new tokens
+# against the cache of their context length.
+KV_WORKLOADS: Dict[str, KvWorkload] = {
+    w.name: w
+    for w in [
+        KvWorkload("decode_b4h32q1k4096d128", 4, 32, 1, 4096, 128, "bf16", True, 2001,
+                   description="one new token per sequence, Llama-7B-shaped heads, 4K cache"),
+        KvWorkload("decode_fp16_b1h16q1k32768d128", 1, 16, 1, 32768, 128, "fp16", True, 2002,
+                   description="one new token, 32K fp16 cache"),
+        KvWorkload("spec_b4h32q8k4096d128", 4, 32, 8, 4096, 128, "bf16", True, 2003,
+                   description="eight speculative tokens, causal within the block, 4K cache"),
+    ]
+}
+
+
+def make_kv_inputs(w: KvWorkload):
+    """CPU tensors q [B,H,Nq,d], k and v [B,H,Nk,d] (I/O dtype): fp32 randn drawn
+    in the order Q, K, V from the workload's seed, Q and K times qk_gain,
+    rounded to nearest-even."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(w.seed)
+    q = torch.randn((w.B, w.H, w.Nq, w.d), generator=g, dtype=torch.float32)
+    k = torch.randn((w.B, w.H, w.Nk, w.d), generator=g, dtype=torch.float32)
+    v = torch.randn((w.B, w.H, w.Nk, w.d), generator=g, dtype=torch.float32)
+    if w.qk_gain != 1.0:
+        q.mul_(w.qk_gain)
+        k.mul_(w.qk_gain)
+    return {"q": q.to(w.torch_dtype), "k": k.to(w.torch_dtype), "v": v.to(w.torch_dtype)}
+
+
 def to_f64_numpy(t: torch.Tensor):
     """Upcast a rounded I/O tensor to an fp64 numpy array (exact)."""
     return t.to(torch.float64).numpy()
