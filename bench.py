@@ -32,11 +32,15 @@ import workloads  # noqa: E402
 
 METRIC = "attention fwd+bwd TFLOP/s at d=128, N=4096 causal; % of bf16 MFMA peak"
 PEAK_TFLOPS = 2516.6   # MI355X dense bf16/fp16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 KERNEL_SOURCES = {
     "fwd": "exact_attention_66_amd/csrc/attn_fwd.hip",
     "bwd_dkdv": "exact_attention_66_amd/csrc/attn_bwd.hip",
     "bwd_dq": "exact_attention_66_amd/csrc/attn_bwd.hip",
+    "kv_split": "exact_attention_66_amd/csrc/attn_kvcache.hip",
+    "kv_merge": "exact_attention_66_amd/csrc/attn_kvcache.hip",
+    "bwd_prep": "exact_attention_66_amd/csrc/attn_bwd.hip",
 }
 
 
@@ -44,7 +48,7 @@ def source_hash(kernel: str) -> str | None:
     path = KERNEL_SOURCES.get(kernel)
     if path is None:
         return None
-    files = [path, "exact_attention_66_amd/csrc/attn_device.h"]
+    files = [path, "exact_attention_66_amd/csrc/attn_device.h", "exact_attention_66_amd/csrc/attn_launch.h"]
     h = hashlib.sha256()
     for f in files:
         with open(os.path.join(ROOT, f), "rb") as fh:
@@ -108,18 +112,200 @@ def cpu_baseline(w: workloads.Workload, x, budget_s: float):
     }
 
 
+KERNEL_NAME_KINDS = [("fwd_kernel<", "fwd"), ("bwd_prep<", "bwd_prep"), ("bwd_dkdv<", "bwd_dkdv"),
+                     ("bwd_dq<", "bwd_dq"), ("kv_split_kernel<", "kv_split"), ("kv_merge_kernel<", "kv_merge")]
+
+
+def record_traffic(fetch_csv: str, write_csv: str, workload: str) -> int:
+    """Turn two rocprofv3 counter files (FETCH_SIZE, WRITE_SIZE; KiB per
+    dispatch) of a run with --copy-calibration-bytes into HBM bytes per
+    launch of each kernel: fetched and written KiB are scaled by what the same
+    counters read for the plain 1 GiB device copy in that run.  Updates the
+    workload's entry of profiles/hbm_traffic.json (with the current kernel
+    source hash) and prints a markdown table."""
+    import csv
+    from collections import defaultdict
+
+    def per_kernel(path, counter):
+        vals = defaultdict(list)
+        with open(path, newline="") as f:
+            for row in csv.DictReader(f):
+                if row.get("Counter_Name") != counter:
+                    continue
+                vals[row["Kernel_Name"]].append(float(row["Counter_Value"]))
+        return vals
+
+    fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
+    gib_kib = 1024.0 * 1024.0
+    copy_f = max((max(v) for k, v in fetch.items() if "copyBuffer" in k), default=None)
+    copy_w = max((max(v) for k, v in write.items() if "copyBuffer" in k), default=None)
+    if not copy_f or not copy_w:
+        print("no 1 GiB copy kernel in the counter files (run with --copy-calibration-bytes 1073741824)",
+              file=sys.stderr)
+        return 1
+    fs, wsc = gib_kib / copy_f, gib_kib / copy_w
+    try:
+        with open(TRAFFIC_FILE) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        data = {}
+    entry = {}
+    print(f"Calibration: a plain 1 GiB device copy reads FETCH_SIZE = {copy_f:.0f} KiB and WRITE_SIZE = "
+          f"{copy_w:.0f} KiB, so fetched KiB are scaled by {fs:.4f} and written KiB by {wsc:.4f}.\n")
+    print("| kernel | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | scaled bytes read | scaled bytes written | total (GB) |")
+    print("|---|---|---|---|---|---|")
+    for name in sorted(set(fetch) & set(write)):
+        kind = next((kd for pre, kd in KERNEL_NAME_KINDS if pre in name), None)
+        if kind is None:
+            continue
+        fk = sum(fetch[name]) / len(fetch[name])
+        wk = sum(write[name]) / len(write[name])
+        rd, wr = fk * 1024 * fs, wk * 1024 * wsc
+        entry[kind] = {"bytes_per_launch": int(rd + wr), "bytes_read": int(rd), "bytes_written": int(wr),
+                       "fetch_kib": round(fk, 1), "write_kib": round(wk, 1), "fetch_scale": round(fs, 4),
+                       "write_scale": round(wsc, 4), "source_hash": source_hash(kind)}
+        short = name.replace("attn::(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+        print(f"| `{short}` | {fk:.0f} | {wk:.0f} | {rd / 1e9:.3f} GB | {wr / 1e9:.3f} GB | {(rd + wr) / 1e9:.3f} |")
+    data.setdefault(workload, {}).update(entry)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(data, f, indent=1)
+        f.write("\n")
+    return 0
+
+
+def copy_calibration(nbytes: int, dev) -> None:
+    """A plain device-to-device copy of nbytes (three times): the reference
+    kernel whose byte counters scale those of the attention kernels."""
+    if not nbytes:
+        return
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+
+
+def cpu_baseline_kv(w: workloads.KvWorkload, x, budget_s: float):
+    """Time the fp64 oracle (as it stands) on whole heads of a KV-cache workload."""
+    import oracle
+
+    heads, t0 = 0, time.perf_counter()
+    for b in range(w.B):
+        for h in range(w.H):
+            oracle.forward_head(*(workloads.to_f64_numpy(x[n][b, h]) for n in ("q", "k", "v")), w.scale, w.causal)
+            heads += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    per_head = w.io_bytes() / (w.B * w.H)
+    return {
+        "value": round(heads * per_head / dt / 1e9, 4),
+        "unit": "GB/s",
+        "cores": os.cpu_count(),
+        "kind": "oracle",
+        "sample": f"{heads} of {w.B * w.H} heads (b, h in order) of {w.name}, numpy fp64, {dt:.2f} s",
+        "host_cpus": os.cpu_count(),
+        "seconds": round(dt, 3),
+    }
+
+
+def bench_kvcache(args, w: workloads.KvWorkload) -> int:
+    """Decoding against a KV cache: one step is one attn_fwd_kvcache call
+    (split kernel + merge kernel) over a batch of caches resident in HBM.
+    Consecutive steps use different copies of the inputs (enough copies to
+    exceed the 256 MB last-level cache three times over), so every step
+    streams its K and V from HBM, as decoding a new batch would."""
+    import torch
+    import exact_attention_66_amd as ea
+
+    dev = torch.device("cuda:0")
+    x = workloads.make_kv_inputs(w)
+    copies = max(1, min(8, -(-3 * 256 * 2**20 // w.kv_bytes())))
+    sets = [{n: x[n].to(dev) for n in ("q", "k", "v")} for _ in range(copies)]
+    o = torch.empty((w.B, w.H, w.Nq, w.d), dtype=w.torch_dtype, device=dev)
+    lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
+    ws = torch.empty(ea.attn_fwd_kvcache_workspace_bytes(w.B, w.H, w.Nq, w.Nk, w.d, 0), dtype=torch.uint8,
+                     device=dev)
+    splits = ea.attn_fwd_kvcache_splits(w.B, w.H, w.Nq, w.Nk, w.d, 0)
+
+    def step(i):
+        t = sets[i % copies]
+        ea.attn_fwd_kvcache(t["q"], t["k"], t["v"], o, lse, w.scale, w.causal, ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ea.attn_profile_start()
+    e0.record()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    e1.record()
+    torch.cuda.synchronize()
+    prof = ea.attn_profile_stop()
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    copy_calibration(args.copy_calibration_bytes, dev)
+    kernels = {kname: {"launches": n, "avg_ms": round(t / n, 5)} for kname, (n, t) in prof.items() if n}
+    # the split kernel reads K, V and Q once: its algorithmic bytes (its
+    # workspace writes, 4 (d + 4) bytes per query row and split, are not counted)
+    split_bytes = w.kv_bytes() + w.B * w.H * w.Nq * w.d * 2
+    avg_ms = prof["kv_split"][1] / prof["kv_split"][0]
+    achieved = split_bytes / (avg_ms * 1e-3) / 1e9
+    line = {
+        "metric": "KV-cache attention forward GB/s (K, V, Q read + O, lse written, per call)",
+        "value": round(w.io_bytes() / (ms_per_step * 1e-3) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d, "causal": w.causal,
+                   "splits": splits, "input_copies": copies, "seed": w.seed},
+        "kernels": kernels,
+        "roofline": {
+            "kernel": "kv_split",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic("kv_split", w.name),
+        },
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_kv(w, x, min(args.cpu_baseline_seconds, 5.0))
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default=workloads.HEADLINE, choices=sorted(workloads.WORKLOADS))
+    ap.add_argument("--workload", default=workloads.HEADLINE,
+                    choices=sorted(workloads.WORKLOADS) + sorted(workloads.KV_WORKLOADS))
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-bytes", type=int, default=0,
                     help="after the timed steps, also run a plain device copy of this many bytes "
                          "(reference kernel for scaling the HBM byte counters)")
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU run: turn rocprofv3 FETCH_SIZE / WRITE_SIZE counter files into the "
+                         "workload's HBM bytes per launch in profiles/hbm_traffic.json")
     args = ap.parse_args()
+
+    if args.record_traffic:
+        return record_traffic(*args.record_traffic, args.workload)
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this library has no "
@@ -133,6 +319,9 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
     ea.load()
+
+    if args.workload in workloads.KV_WORKLOADS:
+        return bench_kvcache(args, workloads.KV_WORKLOADS[args.workload])
 
     w = workloads.WORKLOADS[args.workload]
     x = workloads.make_inputs(w)
@@ -164,14 +353,7 @@ def main() -> int:
     prof = ea.attn_profile_stop()
     ms_per_step = e0.elapsed_time(e1) / args.steps
 
-    if args.copy_calibration_bytes:
-        src = torch.empty(args.copy_calibration_bytes, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+    copy_calibration(args.copy_calibration_bytes, dev)
 
     flops = w.fwd_flops() + w.bwd_flops()
     value = flops / (ms_per_step * 1e-3) / 1e12

@@ -94,10 +94,16 @@ __device__ __forceinline__ int swz(int row, int col) {
   return row * ROWLEN + (((col >> 3) ^ f) << 3) + (col & 7);
 }
 
+// Maximum of two / three floats with NaN propagation (IEEE maximum, gfx950
+// v_maximum3_f32).  Unlike fmaxf it needs no quieting of its inputs, which
+// would cost one extra instruction per MFMA result read.
+__device__ __forceinline__ float fmax2(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float fmax3(float a, float b, float c) { return fmax2(fmax2(a, b), c); }
+
 // max / sum of a value across the two 32-lane halves (lane l and l ^ 32).
 __device__ __forceinline__ float xhalf_max(float x) {
   auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  return fmax2(__uint_as_float(p[0]), __uint_as_float(p[1]));
 }
 __device__ __forceinline__ float xhalf_sum(float x) {
   auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);

@@ -281,10 +281,10 @@ __global__ __launch_bounds__(NW * 64, ATTN_FWD_MINW) void fwd_kernel(const typen
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const f32x16& x = s[qb];
-      const float m0 = fmaxf(fmaxf(x[0], x[1]), x[2]), m1 = fmaxf(fmaxf(x[3], x[4]), x[5]);
-      const float m2 = fmaxf(fmaxf(x[6], x[7]), x[8]), m3 = fmaxf(fmaxf(x[9], x[10]), x[11]);
-      const float m4 = fmaxf(fmaxf(x[12], x[13]), x[14]);
-      float mx = fmaxf(fmaxf(fmaxf(m0, m1), m2), fmaxf(fmaxf(m3, m4), x[15]));
+      const float m0 = fmax3(x[0], x[1], x[2]), m1 = fmax3(x[3], x[4], x[5]);
+      const float m2 = fmax3(x[6], x[7], x[8]), m3 = fmax3(x[9], x[10], x[11]);
+      const float m4 = fmax3(x[12], x[13], x[14]);
+      float mx = fmax3(fmax3(m0, m1, m2), fmax3(m3, m4, x[15]), -__builtin_inff());
       mx = xhalf_max(mx);
       const float mt = mx * scale_log2;
       const bool need = mt > m_run[qb] + kRescaleSlack;

@@ -19,9 +19,9 @@
 //    runs the square forward's per-block step: S^T = K Q^T and O^T += V^T P^T
 //    on v_mfma_f32_32x32x16, softmax in registers.  It writes its unnormalised
 //    O^T rows and (m, l, l_rounded) per query to a workspace.
-//  * kv_merge_kernel: one wave per query row combines the splits and writes
-//    O (normalised by the merged sum of the rounded weights, as in the square
-//    forward) and the natural-log lse.
+//  * kv_merge_kernel: one workgroup per query row combines the splits and
+//    writes O (normalised by the merged sum of the rounded weights, as in the
+//    square forward) and the natural-log lse.
 //
 // Causal alignment for Nq != Nk: query i is position Nk - Nq + i of the
 // sequence, so it sees keys j <= i + Nk - Nq.
@@ -53,10 +53,6 @@ struct KvTile {
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-__device__ __forceinline__ float max3(float a, float b, float c) {
-  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
 }
 
 template <typename E, int D, bool CAUSAL>
@@ -194,8 +190,8 @@ __global__ __launch_bounds__(64) void kv_split_kernel(const typename E::T* __res
       }
     }
     // ---- online softmax in the log2 domain
-    float mx = max3(max3(max3(s[0], s[1], s[2]), max3(s[3], s[4], s[5]), max3(s[6], s[7], s[8])),
-                    max3(max3(s[9], s[10], s[11]), max3(s[12], s[13], s[14]), s[15]), -__builtin_inff());
+    float mx = fmax3(fmax3(fmax3(s[0], s[1], s[2]), fmax3(s[3], s[4], s[5]), fmax3(s[6], s[7], s[8])),
+                     fmax3(fmax3(s[9], s[10], s[11]), fmax3(s[12], s[13], s[14]), s[15]), -__builtin_inff());
     mx = xhalf_max(mx);
     const float mt = mx * scale_log2;   // -inf when every key of the block is masked for this row
     if (__builtin_amdgcn_ballot_w64(mt > m_run + kRescaleSlack) != 0) {
@@ -249,37 +245,78 @@ __global__ __launch_bounds__(64) void kv_split_kernel(const typename E::T* __res
   if (h == 0) *(f32x4*)(part_stat + row * 4) = f32x4{m_run, l, lr, 0.f};
 }
 
-// One wave per query row: merge the P partial states of that row.
+// One workgroup (four waves) per query row merges the P partial states of
+// that row: the row max M over the splits first (each thread a strided share
+// of the splits, then a tree over the workgroup), then wave w sums splits
+// w, w + 4, ... with weights 2^(m_p - M), every lane over its own elements of
+// the row, eight splits' loads in flight at a time; the four waves' sums are
+// added through LDS.
 template <typename E, int D>
 __global__ __launch_bounds__(256) void kv_merge_kernel(const float* __restrict__ part_acc,
                                                        const float* __restrict__ part_stat,
                                                        typename E::T* __restrict__ O, float* __restrict__ LSE,
-                                                       int rows, int P) {
+                                                       int P) {
   using T = typename E::T;
   constexpr int EL = D / 64;   // elements of the row per lane
-  const int lane = threadIdx.x & 63;
-  const int row = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6);
-  if (row >= rows) return;
-  const float* st = part_stat + (size_t)row * P * 4;
-  const float* acc = part_acc + (size_t)row * P * D + lane * EL;
+  constexpr int U = 8;         // splits per batch of loads
+  __shared__ float red_m[4];
+  __shared__ float red_acc[4][D];
+  __shared__ float red_s[4][2];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const size_t row = blockIdx.x;
+  const float* st = part_stat + row * P * 4;
+  const float* acc = part_acc + row * P * D + lane * EL;
+
   float M = -__builtin_inff();
-  for (int p = 0; p < P; ++p) M = fmaxf(M, st[4 * p]);
+  for (int p = tid; p < P; p += 256) M = fmaxf(M, st[4 * p]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  if (lane == 0) red_m[w] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
+
   float num[EL], den = 0.f, lsum = 0.f;
 #pragma unroll
   for (int e = 0; e < EL; ++e) num[e] = 0.f;
-  for (int p = 0; p < P; ++p) {
-    const float m = st[4 * p];
-    // a split in which this row saw no key holds m = -inf and zero sums
-    const float a = m == -__builtin_inff() ? 0.0f : fast_exp2(m - M);
-    lsum = fmaf(a, st[4 * p + 1], lsum);
-    den = fmaf(a, st[4 * p + 2], den);
+  for (int p0 = w; p0 < P; p0 += 4 * U) {
+    float m[U], l[U], lr[U], x[U][EL];
 #pragma unroll
-    for (int e = 0; e < EL; ++e) num[e] = fmaf(a, acc[(size_t)p * D + e], num[e]);
+    for (int u = 0; u < U; ++u) {
+      const int p = p0 + 4 * u;
+      const bool ok = p < P;
+      m[u] = ok ? st[4 * p] : -__builtin_inff();
+      l[u] = ok ? st[4 * p + 1] : 0.f;
+      lr[u] = ok ? st[4 * p + 2] : 0.f;
+#pragma unroll
+      for (int e = 0; e < EL; ++e) x[u][e] = ok ? acc[(size_t)p * D + e] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      // a split in which this row saw no key holds m = -inf and zero sums
+      const float a = m[u] == -__builtin_inff() ? 0.0f : fast_exp2(m[u] - M);
+      lsum = fmaf(a, l[u], lsum);
+      den = fmaf(a, lr[u], den);
+#pragma unroll
+      for (int e = 0; e < EL; ++e) num[e] = fmaf(a, x[u][e], num[e]);
+    }
   }
-  const float inv = 1.0f / den;
-  T* orow = O + (size_t)row * D + lane * EL;
 #pragma unroll
-  for (int e = 0; e < EL; ++e) orow[e] = (T)(num[e] * inv);
+  for (int e = 0; e < EL; ++e) red_acc[w][lane * EL + e] = num[e];
+  if (lane == 0) {
+    red_s[w][0] = den;
+    red_s[w][1] = lsum;
+  }
+  __syncthreads();
+  if (w != 0) return;
+  den = (red_s[0][0] + red_s[1][0]) + (red_s[2][0] + red_s[3][0]);
+  lsum = (red_s[0][1] + red_s[1][1]) + (red_s[2][1] + red_s[3][1]);
+  const float inv = 1.0f / den;
+  T* orow = O + row * D + lane * EL;
+#pragma unroll
+  for (int e = 0; e < EL; ++e) {
+    const int d = lane * EL + e;
+    orow[e] = (T)(((red_acc[0][d] + red_acc[1][d]) + (red_acc[2][d] + red_acc[3][d])) * inv);
+  }
   if (lane == 0) LSE[row] = (M + __builtin_amdgcn_logf(lsum)) * kLn2;
 }
 
@@ -304,9 +341,8 @@ hipError_t launch_kv_cfg(const KvArgs& a) {
   float* lse = a.lse;
   const float* cacc = pacc;
   const float* cst = pst;
-  void* margs[] = {(void*)&cacc, (void*)&cst, (void*)&o, (void*)&lse, (void*)&rows, (void*)&P};
-  return launch_kernel((const void*)kv_merge_kernel<E, D>, dim3((unsigned)((rows + 3) / 4)), dim3(256), margs,
-                       a.stream, 5);
+  void* margs[] = {(void*)&cacc, (void*)&cst, (void*)&o, (void*)&lse, (void*)&P};
+  return launch_kernel((const void*)kv_merge_kernel<E, D>, dim3((unsigned)rows), dim3(256), margs, a.stream, 5);
 }
 
 template <typename E, int D>

@@ -71,8 +71,8 @@ struct KvArgs {
   hipStream_t stream;
 };
 
-// Split plan: `requested` splits (0: about 2048 waves in all, at least 128
-// keys per split), then the keys per split rounded up to a multiple of 32
+// Split plan: `requested` splits (0: about 1024 waves in all, i.e. one per
+// SIMD of the chip, and at least 128 keys per split), then the keys per split rounded up to a multiple of 32
 // and the split count recomputed from it, so that no split is empty unless
 // the causal mask empties it.  A pure function of the sizes: the workspace
 // size and the launch agree on it.
@@ -80,7 +80,7 @@ inline void kv_split_plan(int64_t BH, int64_t Nq, int64_t Nk, int requested, int
   const int64_t units = BH * ((Nq + 31) / 32);
   int64_t P = requested;
   if (P <= 0) {
-    P = (2048 + units - 1) / units;
+    P = (1024 + units - 1) / units;
     const int64_t cap = (Nk + 127) / 128;
     if (P > cap) P = cap;
   }

@@ -124,9 +124,10 @@ def test_python_binding_rejects_noncontiguous():
 # ---------------------------------------------------------------- KV-cache forward
 
 def test_kvcache_split_plan_and_workspace():
-    # decode, 128 heads, 4096 keys: about 2048 waves -> 16 splits of 256 keys
-    assert ea.attn_fwd_kvcache_splits(4, 32, 1, 4096, 128) == 16
-    assert ea.attn_fwd_kvcache_workspace_bytes(4, 32, 1, 4096, 128) == 128 * 16 * 128 * 4 + 128 * 16 * 16
+    # decode, 128 heads, 4096 keys: about 1024 waves -> 8 splits of 512 keys
+    assert ea.attn_fwd_kvcache_splits(4, 32, 1, 4096, 128) == 8
+    assert ea.attn_fwd_kvcache_workspace_bytes(4, 32, 1, 4096, 128) == 128 * 8 * 128 * 4 + 128 * 8 * 16
+    assert ea.attn_fwd_kvcache_splits(1, 16, 1, 32768, 128) == 64
     # at least 128 keys per automatic split; a requested count is cut to whole 32-key blocks
     assert ea.attn_fwd_kvcache_splits(1, 1, 1, 300, 64) == 3
     assert ea.attn_fwd_kvcache_splits(1, 1, 1, 100, 64, 1000) == 4
