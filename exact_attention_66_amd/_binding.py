@@ -23,9 +23,11 @@ STATUS_NAMES = {
     0: "ATTN_OK", 1: "ATTN_ERR_NULL_PTR", 2: "ATTN_ERR_BAD_SHAPE", 3: "ATTN_ERR_UNSUPPORTED_HEAD_DIM",
     4: "ATTN_ERR_BAD_DTYPE", 5: "ATTN_ERR_MISALIGNED", 6: "ATTN_ERR_UNSUPPORTED_SEQLEN",
     7: "ATTN_ERR_BAD_SCALE", 8: "ATTN_ERR_WORKSPACE_TOO_SMALL", 9: "ATTN_ERR_ALIASING", 10: "ATTN_ERR_HIP",
+    11: "ATTN_ERR_BAD_LAYOUT",
 }
-EXPORTED = ["attn_fwd", "attn_bwd_workspace_bytes", "attn_bwd", "attn_fwd_kvcache",
-            "attn_fwd_kvcache_workspace_bytes", "attn_fwd_kvcache_splits", "attn_profile_start",
+EXPORTED = ["attn_fwd", "attn_fwd_strided", "attn_bwd_workspace_bytes", "attn_bwd", "attn_fwd_kvcache",
+            "attn_fwd_kvcache_strided", "attn_fwd_kvcache_workspace_bytes", "attn_fwd_kvcache_splits",
+            "attn_profile_start",
             "attn_profile_stop", "attn_status_string", "attn_last_hip_error"]
 # attn_kernel_kind values
 KERNEL_KINDS = ["fwd", "bwd_prep", "bwd_dkdv", "bwd_dq", "kv_split", "kv_merge"]
@@ -61,6 +63,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_bwd.restype = i32
     lib.attn_fwd_kvcache.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, f32, i32, i32, i32, vp, sz, vp]
     lib.attn_fwd_kvcache.restype = i32
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    lib.attn_fwd_strided.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64p, f32, i32, i32, vp]
+    lib.attn_fwd_strided.restype = i32
+    lib.attn_fwd_kvcache_strided.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64p, f32, i32, i32, i32,
+                                             vp, sz, vp]
+    lib.attn_fwd_kvcache_strided.restype = i32
     lib.attn_fwd_kvcache_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i32]
     lib.attn_fwd_kvcache_workspace_bytes.restype = sz
     lib.attn_fwd_kvcache_splits.argtypes = [i64, i64, i64, i64, i64, i32]
@@ -130,6 +138,25 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return t.data_ptr() or None
 
 
+def _strided_ptr(t: torch.Tensor) -> Optional[int]:
+    """Device pointer of a tensor whose last dimension is contiguous (any other strides)."""
+    if t.dim() and t.shape[-1] > 1 and t.stride(-1) != 1:
+        raise ValueError("the last (head-dimension) axis must be contiguous")
+    return t.data_ptr() or None
+
+
+def _strides12(*ts) -> "ctypes.Array":
+    """(batch, head, token) element strides of four [B, H, N, d] tensors, as int64[12]."""
+    vals = []
+    for t in ts:
+        vals += [int(t.stride(0)), int(t.stride(1)), int(t.stride(2))]
+    return (ctypes.c_int64 * 12)(*vals)
+
+
+def _all_contiguous(*ts) -> bool:
+    return all(t.is_contiguous() for t in ts)
+
+
 def _stream(stream) -> Optional[int]:
     if stream is None:
         return torch.cuda.current_stream().cuda_stream or None
@@ -152,8 +179,13 @@ def attn_fwd(q, k, v, o, lse, scale: float, causal: bool, stream=None) -> None:
             raise ValueError("q, k, v and o must share shape and dtype")
     if tuple(lse.shape) != (B, H, N) or lse.dtype != torch.float32:
         raise ValueError("lse must be a float32 [B, H, N] tensor")
-    st = load().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, float(scale),
-                         int(bool(causal)), _dtype_code(q), _stream(stream))
+    if _all_contiguous(q, k, v, o):
+        st = load().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, float(scale),
+                             int(bool(causal)), _dtype_code(q), _stream(stream))
+    else:   # [B, H, N, d] views of other layouts (e.g. [B, N, H, d] transposed): strides passed through
+        st = load().attn_fwd_strided(_strided_ptr(q), _strided_ptr(k), _strided_ptr(v), _strided_ptr(o),
+                                     _ptr(lse), B, H, N, d, _strides12(q, k, v, o), float(scale),
+                                     int(bool(causal)), _dtype_code(q), _stream(stream))
     if st != ATTN_OK:
         raise AttnError(st, "attn_fwd")
 
@@ -186,9 +218,15 @@ def attn_fwd_kvcache(q, k, v, o, lse, scale: float, causal: bool, workspace, num
     if tuple(lse.shape) != (B, H, Nq) or lse.dtype != torch.float32:
         raise ValueError("lse must be a float32 [B, H, Nq] tensor")
     ws_bytes = workspace.numel() * workspace.element_size()
-    st = load().attn_fwd_kvcache(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk, d, float(scale),
-                                 int(bool(causal)), _dtype_code(q), int(num_splits), _ptr(workspace), ws_bytes,
-                                 _stream(stream))
+    if _all_contiguous(q, k, v, o):
+        st = load().attn_fwd_kvcache(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk, d, float(scale),
+                                     int(bool(causal)), _dtype_code(q), int(num_splits), _ptr(workspace), ws_bytes,
+                                     _stream(stream))
+    else:
+        st = load().attn_fwd_kvcache_strided(_strided_ptr(q), _strided_ptr(k), _strided_ptr(v), _strided_ptr(o),
+                                             _ptr(lse), B, H, Nq, Nk, d, _strides12(q, k, v, o), float(scale),
+                                             int(bool(causal)), _dtype_code(q), int(num_splits), _ptr(workspace),
+                                             ws_bytes, _stream(stream))
     if st != ATTN_OK:
         raise AttnError(st, "attn_fwd_kvcache")
 

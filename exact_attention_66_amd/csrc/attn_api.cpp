@@ -2,6 +2,7 @@
 // no HIP call before every check has passed), then dispatch to the kernels.
 #include "../../include/attn.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <limits>
@@ -45,11 +46,121 @@ int check_common(int64_t B, int64_t H, int64_t N, int64_t d, float scale, int dt
   return ATTN_OK;
 }
 
+// A caller-supplied [B, H, N, d] layout (element strides, d contiguous):
+// strides non-negative and multiples of 8 (every row 16-byte aligned when the
+// base is), token stride below 2^24 (copy offsets of a 128-row tile stay
+// within 32 bits), batch and head strides below 2^40.
+bool lay_ok(const attn::Lay& l) {
+  const int64_t big = (int64_t)1 << 40;
+  return l.sb >= 0 && l.sh >= 0 && l.sn >= 0 && l.sb < big && l.sh < big && l.sn < (1 << 24) && l.sb % 8 == 0 &&
+         l.sh % 8 == 0 && l.sn % 8 == 0;
+}
+
+// Bytes from the base to the end of the last element of a layout.
+size_t lay_extent(const attn::Lay& l, int64_t B, int64_t H, int64_t N, int64_t d) {
+  return (size_t)((B - 1) * l.sb + (H - 1) * l.sh + (N - 1) * l.sn + d) * 2;
+}
+
+// No two elements of an output layout share an address: with the
+// dimensions of size > 1 sorted by stride, each stride must reach past
+// everything the smaller ones span (the d elements of a row included).
+bool lay_injective(const attn::Lay& l, int64_t B, int64_t H, int64_t N, int64_t d) {
+  struct Dm { int64_t n, s; } dims[3] = {{B, l.sb}, {H, l.sh}, {N, l.sn}};
+  for (int i = 0; i < 3; ++i)
+    for (int j = i + 1; j < 3; ++j)
+      if (dims[j].s < dims[i].s) std::swap(dims[i], dims[j]);
+  int64_t span = d;
+  for (const Dm& x : dims) {
+    if (x.n <= 1) continue;
+    if (x.s < span) return false;
+    span = x.s * (x.n - 1) + span;
+  }
+  return true;
+}
+
 int launch_status(hipError_t e) {
   if (e == hipSuccess) return ATTN_OK;
   g_last_hip_error = (int)e;
   return ATTN_ERR_HIP;
 }
+
+// Forward with per-tensor layouts (lays: q, k, v, o); lse is contiguous.
+int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H, int64_t N,
+             int64_t d, const attn::Lay* lays, float scale, int causal, int dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL_PTR;
+  int st = check_common(B, H, N, d, scale, dtype);
+  if (st != ATTN_OK) return st;
+  for (int i = 0; i < 4; ++i)
+    if (!lay_ok(lays[i])) return ATTN_ERR_BAD_LAYOUT;
+  if (!lay_injective(lays[3], B, H, N, d)) return ATTN_ERR_BAD_LAYOUT;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return ATTN_ERR_MISALIGNED;
+  const size_t lb = (size_t)(B * H * N) * 4, ob = lay_extent(lays[3], B, H, N, d);
+  const void* ins[] = {q, k, v};
+  for (int i = 0; i < 3; ++i) {
+    const size_t ib = lay_extent(lays[i], B, H, N, d);
+    if (overlaps(o, ob, ins[i], ib) || overlaps(lse, lb, ins[i], ib)) return ATTN_ERR_ALIASING;
+  }
+  if (overlaps(o, ob, lse, lb)) return ATTN_ERR_ALIASING;
+
+  attn::FwdArgs a{q, k, v, o, lse, B, H, N, d, scale, causal != 0, dtype, (hipStream_t)stream,
+                  lays[0], lays[1], lays[2], lays[3]};
+  return launch_status(attn::launch_fwd(a));
+}
+
+// Sizes of a KV-cache call: both lengths as in check_common (B*H*ceil(len/64)
+// units fit a launch), plus the split grid and the merge rows.
+int check_kvcache(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale, int causal, int dtype,
+                  int num_splits) {
+  int st = check_common(B, H, Nq, d, scale, dtype);
+  if (st != ATTN_OK) return st;
+  st = check_common(B, H, Nk, d, scale, dtype);
+  if (st != ATTN_OK) return st;
+  if (causal && Nk < Nq) return ATTN_ERR_BAD_SHAPE;   // rows with no visible key
+  if (num_splits < 0 || num_splits > 4096) return ATTN_ERR_BAD_SHAPE;
+  int P = 1, chunk = 32;
+  attn::kv_split_plan(B * H, Nq, Nk, num_splits, &P, &chunk);
+  if (B * H * ((Nq + 31) / 32) * P > (int64_t)INT32_MAX || B * H * Nq > (int64_t)INT32_MAX - 3) return ATTN_ERR_BAD_SHAPE;
+  if (checked_elems(B * H, Nq, P, d) < 0) return ATTN_ERR_BAD_SHAPE;
+  return ATTN_OK;
+}
+
+// KV-cache forward with per-tensor layouts (lays: q, k, v, o); lse contiguous.
+int kv_impl(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H, int64_t Nq,
+            int64_t Nk, int64_t d, const attn::Lay* lays, float scale, int causal, int dtype, int num_splits,
+            void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL_PTR;
+  int st = check_kvcache(B, H, Nq, Nk, d, scale, causal, dtype, num_splits);
+  if (st != ATTN_OK) return st;
+  for (int i = 0; i < 4; ++i)
+    if (!lay_ok(lays[i])) return ATTN_ERR_BAD_LAYOUT;
+  if (!lay_injective(lays[3], B, H, Nq, d)) return ATTN_ERR_BAD_LAYOUT;
+  int P = 1, chunk = 32;
+  attn::kv_split_plan(B * H, Nq, Nk, num_splits, &P, &chunk);
+  const size_t need = attn::kv_acc_bytes(B * H, Nq, P, d) + attn::kv_stat_bytes(B * H, Nq, P);
+  if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE_TOO_SMALL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return ATTN_ERR_MISALIGNED;
+  const size_t lb = (size_t)(B * H * Nq) * 4;
+  struct R { const void* p; size_t n; };
+  const R ins[] = {{q, lay_extent(lays[0], B, H, Nq, d)}, {k, lay_extent(lays[1], B, H, Nk, d)},
+                   {v, lay_extent(lays[2], B, H, Nk, d)}};
+  const R outs[] = {{o, lay_extent(lays[3], B, H, Nq, d)}, {lse, lb}, {workspace, need}};
+  for (const R& x : outs) {
+    for (const R& y : ins)
+      if (overlaps(x.p, x.n, y.p, y.n)) return ATTN_ERR_ALIASING;
+    for (const R& y : outs)
+      if (&x != &y && overlaps(x.p, x.n, y.p, y.n)) return ATTN_ERR_ALIASING;
+  }
+  char* ws = (char*)workspace;
+  attn::KvArgs a{q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal != 0, dtype, P, chunk,
+                 (float*)ws, (float*)(ws + attn::kv_acc_bytes(B * H, Nq, P, d)), (hipStream_t)stream,
+                 lays[0], lays[1], lays[2], lays[3]};
+  return launch_status(attn::launch_kvcache(a));
+}
+
+attn::Lay lay_from(const int64_t* s) { return attn::Lay{s[0], s[1], (int32_t)std::min<int64_t>(s[2], INT32_MAX), 0}; }
 
 }  // namespace
 
@@ -57,18 +168,19 @@ extern "C" {
 
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
              int64_t N, int64_t d, float scale, int causal, int dtype, void* stream) {
-  if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL_PTR;
-  int st = check_common(B, H, N, d, scale, dtype);
-  if (st != ATTN_OK) return st;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
-    return ATTN_ERR_MISALIGNED;
-  const size_t tb = (size_t)(B * H * N * d) * 2, lb = (size_t)(B * H * N) * 4;
-  for (const void* in : {q, k, v})
-    if (overlaps(o, tb, in, tb) || overlaps(lse, lb, in, tb)) return ATTN_ERR_ALIASING;
-  if (overlaps(o, tb, lse, lb)) return ATTN_ERR_ALIASING;
+  if (checked_elems(B, H, N, d) < 0) return ATTN_ERR_BAD_SHAPE;
+  const attn::Lay c = attn::contiguous_lay(H, N, d);
+  const attn::Lay lays[4] = {c, c, c, c};
+  return fwd_impl(q, k, v, o, lse, B, H, N, d, lays, scale, causal, dtype, stream);
+}
 
-  attn::FwdArgs a{q, k, v, o, lse, B, H, N, d, scale, causal != 0, dtype, (hipStream_t)stream};
-  return launch_status(attn::launch_fwd(a));
+int attn_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                     int64_t N, int64_t d, const int64_t* strides, float scale, int causal, int dtype, void* stream) {
+  if (!strides) return ATTN_ERR_NULL_PTR;
+  for (int i = 0; i < 12; ++i)
+    if (strides[i] < 0 || strides[i] > ((int64_t)1 << 40)) return ATTN_ERR_BAD_LAYOUT;
+  const attn::Lay lays[4] = {lay_from(strides), lay_from(strides + 3), lay_from(strides + 6), lay_from(strides + 9)};
+  return fwd_impl(q, k, v, o, lse, B, H, N, d, lays, scale, causal, dtype, stream);
 }
 
 size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d) {
@@ -113,23 +225,6 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
   return launch_status(attn::launch_bwd(a));
 }
 
-// Sizes of a KV-cache call: both lengths as in check_common (B*H*ceil(len/64)
-// units fit a launch), plus the split grid and the merge rows.
-int check_kvcache(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale, int causal, int dtype,
-                  int num_splits) {
-  int st = check_common(B, H, Nq, d, scale, dtype);
-  if (st != ATTN_OK) return st;
-  st = check_common(B, H, Nk, d, scale, dtype);
-  if (st != ATTN_OK) return st;
-  if (causal && Nk < Nq) return ATTN_ERR_BAD_SHAPE;   // rows with no visible key
-  if (num_splits < 0 || num_splits > 4096) return ATTN_ERR_BAD_SHAPE;
-  int P = 1, chunk = 32;
-  attn::kv_split_plan(B * H, Nq, Nk, num_splits, &P, &chunk);
-  if (B * H * ((Nq + 31) / 32) * P > (int64_t)INT32_MAX || B * H * Nq > (int64_t)INT32_MAX - 3) return ATTN_ERR_BAD_SHAPE;
-  if (checked_elems(B * H, Nq, P, d) < 0) return ATTN_ERR_BAD_SHAPE;
-  return ATTN_OK;
-}
-
 size_t attn_fwd_kvcache_workspace_bytes(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int num_splits) {
   if (check_kvcache(B, H, Nq, Nk, d, 1.0f, 0, ATTN_DTYPE_BF16, num_splits) != ATTN_OK) return 0;
   int P = 1, chunk = 32;
@@ -147,31 +242,22 @@ int attn_fwd_kvcache_splits(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_
 int attn_fwd_kvcache(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
                      int64_t Nq, int64_t Nk, int64_t d, float scale, int causal, int dtype, int num_splits,
                      void* workspace, size_t workspace_bytes, void* stream) {
-  if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL_PTR;
-  int st = check_kvcache(B, H, Nq, Nk, d, scale, causal, dtype, num_splits);
-  if (st != ATTN_OK) return st;
-  const size_t need = attn_fwd_kvcache_workspace_bytes(B, H, Nq, Nk, d, num_splits);
-  if (need == 0) return ATTN_ERR_BAD_SHAPE;
-  if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE_TOO_SMALL;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
-      (reinterpret_cast<uintptr_t>(workspace) & 255u))
-    return ATTN_ERR_MISALIGNED;
-  const size_t qb = (size_t)(B * H * Nq * d) * 2, kb = (size_t)(B * H * Nk * d) * 2, lb = (size_t)(B * H * Nq) * 4;
-  struct R { const void* p; size_t n; };
-  const R ins[] = {{q, qb}, {k, kb}, {v, kb}};
-  const R outs[] = {{o, qb}, {lse, lb}, {workspace, need}};
-  for (const R& x : outs) {
-    for (const R& y : ins)
-      if (overlaps(x.p, x.n, y.p, y.n)) return ATTN_ERR_ALIASING;
-    for (const R& y : outs)
-      if (&x != &y && overlaps(x.p, x.n, y.p, y.n)) return ATTN_ERR_ALIASING;
-  }
-  int P = 1, chunk = 32;
-  attn::kv_split_plan(B * H, Nq, Nk, num_splits, &P, &chunk);
-  char* ws = (char*)workspace;
-  attn::KvArgs a{q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal != 0, dtype, P, chunk,
-                 (float*)ws, (float*)(ws + attn::kv_acc_bytes(B * H, Nq, P, d)), (hipStream_t)stream};
-  return launch_status(attn::launch_kvcache(a));
+  if (checked_elems(B, H, Nq, d) < 0 || checked_elems(B, H, Nk, d) < 0) return ATTN_ERR_BAD_SHAPE;
+  const attn::Lay cq = attn::contiguous_lay(H, Nq, d), ck = attn::contiguous_lay(H, Nk, d);
+  const attn::Lay lays[4] = {cq, ck, ck, cq};
+  return kv_impl(q, k, v, o, lse, B, H, Nq, Nk, d, lays, scale, causal, dtype, num_splits, workspace,
+                 workspace_bytes, stream);
+}
+
+int attn_fwd_kvcache_strided(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                             int64_t Nq, int64_t Nk, int64_t d, const int64_t* strides, float scale, int causal,
+                             int dtype, int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!strides) return ATTN_ERR_NULL_PTR;
+  for (int i = 0; i < 12; ++i)
+    if (strides[i] < 0 || strides[i] > ((int64_t)1 << 40)) return ATTN_ERR_BAD_LAYOUT;
+  const attn::Lay lays[4] = {lay_from(strides), lay_from(strides + 3), lay_from(strides + 6), lay_from(strides + 9)};
+  return kv_impl(q, k, v, o, lse, B, H, Nq, Nk, d, lays, scale, causal, dtype, num_splits, workspace,
+                 workspace_bytes, stream);
 }
 
 const char* attn_status_string(int status) {
@@ -187,6 +273,9 @@ const char* attn_status_string(int status) {
     case ATTN_ERR_WORKSPACE_TOO_SMALL: return "workspace is NULL or smaller than attn_bwd_workspace_bytes()";
     case ATTN_ERR_ALIASING: return "an output overlaps an input or another output";
     case ATTN_ERR_HIP: return "a HIP kernel launch failed (see attn_last_hip_error())";
+    case ATTN_ERR_BAD_LAYOUT:
+      return "strides must be >= 0 and multiples of 8 elements (token stride < 2^24), and an output's elements "
+             "must not overlap";
     default: return "unknown status";
   }
 }

@@ -69,7 +69,8 @@ __global__ __launch_bounds__(NW * 64, ATTN_FWD_MINW) void fwd_kernel(const typen
                                                                      const typename E::T* __restrict__ K,
                                                                      const typename E::T* __restrict__ V,
                                                                      typename E::T* __restrict__ O,
-                                                                     float* __restrict__ LSE, int BH, int N,
+                                                                     float* __restrict__ LSE, Lay lq, Lay lk,
+                                                                     Lay lv, Lay lo, int H, int BH, int N,
                                                                      int nqb, float scale_log2) {
   using T = typename E::T;
   using v8 = typename E::v8;
@@ -118,10 +119,10 @@ __global__ __launch_bounds__(NW * 64, ATTN_FWD_MINW) void fwd_kernel(const typen
   const int q0 = qblk * BM;
   const int qw0 = q0 + w * 32 * QB;
   const bool wave_valid = qw0 < N;
-  const size_t head = (size_t)bh * (size_t)N * D;
-  const T* Qh = Q + head;
-  const T* Kh = K + head;
-  const T* Vh = V + head;
+  const int bi = bh / H, hi = bh - bi * H;   // batch and head of this unit
+  const T* Qh = Q + (bi * lq.sb + hi * lq.sh);
+  const T* Kh = K + (bi * lk.sb + hi * lk.sh);
+  const T* Vh = V + (bi * lv.sb + hi * lv.sh);
 
   // Q fragments, B operand of S^T = K Q^T: lane holds Q[q = qw0+32qb+r][16ks + 8h .. +7]
   // (loaded below, while the first tile copies are in flight)
@@ -156,19 +157,22 @@ __global__ __launch_bounds__(NW * 64, ATTN_FWD_MINW) void fwd_kernel(const typen
   // of 64-slot blocks.  Per-lane byte offsets are the same for every tile.
   const int wu = wave_id() & (NW - 1);
   unsigned koff[KC], voff[VC];
+  int krow[TAIL ? KC : 1], vrow[TAIL ? VC : 1];   // rows of the copies, for the tail clamp
 #pragma unroll
   for (int c = 0; c < KC; ++c) {
     const int sl = 64 * (wu + NW * c) + lane;
     const int row = min(sl / KSL, BN - 1);
     const int col = min(sl % KSL, D / 8 - 1);
-    koff[c] = (unsigned)(row * D + col * 8) * 2u;
+    koff[c] = (unsigned)(row * lk.sn + col * 8) * 2u;
+    if constexpr (TAIL) krow[c] = row;
   }
 #pragma unroll
   for (int c = 0; c < VC; ++c) {
     const int sl = 64 * (wu + NW * c) + lane;
     const int row = min(sl / VSL, BN - 1);
     const int col = min(sl % VSL, D / 8 - 1);
-    voff[c] = (unsigned)(row * D + col * 8) * 2u;
+    voff[c] = (unsigned)(row * lv.sn + col * 8) * 2u;
+    if constexpr (TAIL) vrow[c] = row;
   }
   // Without TAIL (N a multiple of 64) only a 128-key tile can run past the
   // end of the sequence, by exactly 64 keys: it is copied as its first half,
@@ -176,16 +180,15 @@ __global__ __launch_bounds__(NW * 64, ATTN_FWD_MINW) void fwd_kernel(const typen
   // half is never read.  With TAIL (any other N) the last tile's copies clamp
   // every row to the last key, N - 1, so the rows past the end hold finite
   // duplicates that are read only under the key mask, and no copy reads
-  // beyond the input.  A copy offset is row * 2D + column bytes with 2D a
-  // power of two, so the clamp is one shift, min and or per lane.
+  // beyond the input.  The clamp takes (row - lim) row strides off a copy's
+  // offset when its row lies past the last key.
   static_assert((64 * KSL) % 64 == 0 && (64 * VSL) % 64 == 0, "half tiles are whole blocks");
-  constexpr int RSH = D == 128 ? 8 : 7;   // log2 of a row's bytes
-  auto clamp_row = [](unsigned off, int lim) {
-    return ((unsigned)min((int)(off >> RSH), lim) << RSH) | (off & ((1u << RSH) - 1u));
+  auto clamp_row = [](unsigned off, int row, int lim, int sn) {
+    return off - (unsigned)(max(row - lim, 0) * sn) * 2u;
   };
   auto copy_tile = [&](const int t, const int b) {
-    const char* gk = (const char*)(Kh + (size_t)t * BN * D);
-    const char* gv = (const char*)(Vh + (size_t)t * BN * D);
+    const char* gk = (const char*)(Kh + (size_t)t * BN * lk.sn);
+    const char* gv = (const char*)(Vh + (size_t)t * BN * lv.sn);
     if constexpr (!TAIL) {
       const bool half = t * BN + BN > N;
       const int ki = half ? 64 * KSL / 64 : KI;
@@ -200,10 +203,10 @@ __global__ __launch_bounds__(NW * 64, ATTN_FWD_MINW) void fwd_kernel(const typen
       const int lim = min(N - 1 - t * BN, BN - 1);   // last row of tile t inside the sequence
 #pragma unroll
       for (int c = 0; c < KC; ++c)
-        if (wu + NW * c < KI) lds_copy16(gk, clamp_row(koff[c], lim), &lds_k[b][(wu + NW * c) * 512]);
+        if (wu + NW * c < KI) lds_copy16(gk, clamp_row(koff[c], krow[c], lim, lk.sn), &lds_k[b][(wu + NW * c) * 512]);
 #pragma unroll
       for (int c = 0; c < VC; ++c)
-        if (wu + NW * c < VI) lds_copy16(gv, clamp_row(voff[c], lim), &lds_v[b][(wu + NW * c) * 512]);
+        if (wu + NW * c < VI) lds_copy16(gv, clamp_row(voff[c], vrow[c], lim, lv.sn), &lds_v[b][(wu + NW * c) * 512]);
     }
   };
   // Wait until at most one tile's copies (the most recent) are outstanding:
@@ -328,7 +331,7 @@ __global__ __launch_bounds__(NW * 64, ATTN_FWD_MINW) void fwd_kernel(const typen
   for (int qb = 0; qb < QB; ++qb) {
     const int q = min(qw0 + qb * 32 + r, N - 1);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[qb][ks] = *(const v8*)(Qh + (size_t)q * D + ks * 16 + 8 * h);
+    for (int ks = 0; ks < KS; ++ks) qf[qb][ks] = *(const v8*)(Qh + (size_t)q * lq.sn + ks * 16 + 8 * h);
   }
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb)
@@ -386,7 +389,7 @@ __global__ __launch_bounds__(NW * 64, ATTN_FWD_MINW) void fwd_kernel(const typen
     const float inv = 1.0f / xhalf_sum(lr_run[qb]);
     const int q = qw0 + qb * 32 + r;
     if (TAIL && q >= N) continue;   // rows past the end of the sequence
-    T* orow = O + head + (size_t)q * D;
+    T* orow = O + (bi * lo.sb + hi * lo.sh) + (size_t)q * lo.sn;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -415,8 +418,10 @@ hipError_t launch_fwd_cfg(const FwdArgs& a) {
   const typename E::T* v = (const typename E::T*)a.v;
   typename E::T* o = (typename E::T*)a.o;
   float* lse = a.lse;
-  void* args[] = {(void*)&q, (void*)&k, (void*)&v, (void*)&o, (void*)&lse,
-                  (void*)&BH, (void*)&N, (void*)&nqb, (void*)&scale_log2};
+  Lay lq = a.lq, lk = a.lk, lv = a.lv, lo = a.lo;
+  const int H = (int)a.H;
+  void* args[] = {(void*)&q, (void*)&k, (void*)&v, (void*)&o, (void*)&lse, (void*)&lq, (void*)&lk, (void*)&lv,
+                  (void*)&lo, (void*)&H, (void*)&BH, (void*)&N, (void*)&nqb, (void*)&scale_log2};
   return launch_kernel((const void*)fwd_kernel<E, D, CAUSAL, QB, NW, BN, TAIL>, grid, block, args, a.stream, 0);
 }
 

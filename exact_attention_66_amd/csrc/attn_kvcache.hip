@@ -60,7 +60,8 @@ __global__ __launch_bounds__(64) void kv_split_kernel(const typename E::T* __res
                                                       const typename E::T* __restrict__ K,
                                                       const typename E::T* __restrict__ V,
                                                       float* __restrict__ part_acc, float* __restrict__ part_stat,
-                                                      int Nq, int Nk, int nqb, int P, int chunk, float scale_log2) {
+                                                      Lay lq, Lay lk, Lay lv, int H, int Nq, int Nk, int nqb, int P,
+                                                      int chunk, float scale_log2) {
   using T = typename E::T;
   using v8 = typename E::v8;
   using Tl = KvTile<D>;
@@ -88,40 +89,50 @@ __global__ __launch_bounds__(64) void kv_split_kernel(const typename E::T* __res
   const int k_end = min(kvis, k_beg + chunk);
   const int nblk = k_end > k_beg ? (k_end - k_beg + 31) / 32 : 0;
 
-  const T* Kh = K + (size_t)bh * Nk * D;
-  const T* Vh = V + (size_t)bh * Nk * D;
+  const int bi = bh / H, hi = bh - bi * H;   // batch and head of this unit
+  const T* Kh = K + (bi * lk.sb + hi * lk.sh);
+  const T* Vh = V + (bi * lv.sb + hi * lv.sh);
 
   // per-lane copy offsets (bytes) inside a 32-row block; padding slots at a
   // row's end duplicate its last chunk, slots past row 31 duplicate row 31
   unsigned koff[KI], voff[VI];
+  int krow[KI], vrow[VI];
 #pragma unroll
   for (int c = 0; c < KI; ++c) {
     const int sl = 64 * c + lane;
     const int row = min(sl / KSL, 31), col = min(sl % KSL, D / 8 - 1);
-    koff[c] = (unsigned)(row * D + col * 8) * 2u;
+    koff[c] = (unsigned)(row * lk.sn + col * 8) * 2u;
+    krow[c] = row;
   }
 #pragma unroll
   for (int c = 0; c < VI; ++c) {
     const int sl = 64 * c + lane;
     const int row = min(sl / VSL, 31), col = min(sl % VSL, D / 8 - 1);
-    voff[c] = (unsigned)(row * D + col * 8) * 2u;
+    voff[c] = (unsigned)(row * lv.sn + col * 8) * 2u;
+    vrow[c] = row;
   }
-  constexpr int RSH = D == 128 ? 8 : 7;   // log2 of a row's bytes
-  // Copy key block i of this split into buffer b.  Rows past the split's
-  // end are clamped to its last key (finite duplicates, masked below), so no
-  // copy reads past the end of K or V.
+  // Copy key block i of this split into buffer b.  In the split's last
+  // block, rows past its end are clamped to its last key (finite duplicates,
+  // masked below: the clamp takes (row - lim) row strides off the offset),
+  // so no copy reads past the end of K or V.
   auto copy_block = [&](const int i, const int b) {
     const int k0 = k_beg + 32 * i;
-    const int lim = min(k_end - 1 - k0, 31);
-    const char* gk = (const char*)(Kh + (size_t)k0 * D);
-    const char* gv = (const char*)(Vh + (size_t)k0 * D);
-    auto clamp_row = [&](unsigned off) {
-      return ((unsigned)min((int)(off >> RSH), lim) << RSH) | (off & ((1u << RSH) - 1u));
-    };
+    const char* gk = (const char*)(Kh + (size_t)k0 * lk.sn);
+    const char* gv = (const char*)(Vh + (size_t)k0 * lv.sn);
+    if (k0 + 32 <= k_end) {
 #pragma unroll
-    for (int c = 0; c < KI; ++c) lds_copy16(gk, clamp_row(koff[c]), &lds_k[b][c * 512]);
+      for (int c = 0; c < KI; ++c) lds_copy16(gk, koff[c], &lds_k[b][c * 512]);
 #pragma unroll
-    for (int c = 0; c < VI; ++c) lds_copy16(gv, clamp_row(voff[c]), &lds_v[b][c * 512]);
+      for (int c = 0; c < VI; ++c) lds_copy16(gv, voff[c], &lds_v[b][c * 512]);
+    } else {
+      const int lim = k_end - 1 - k0;
+#pragma unroll
+      for (int c = 0; c < KI; ++c)
+        lds_copy16(gk, koff[c] - (unsigned)(max(krow[c] - lim, 0) * lk.sn) * 2u, &lds_k[b][c * 512]);
+#pragma unroll
+      for (int c = 0; c < VI; ++c)
+        lds_copy16(gv, voff[c] - (unsigned)(max(vrow[c] - lim, 0) * lv.sn) * 2u, &lds_v[b][c * 512]);
+    }
   };
 
   if (nblk > 0) copy_block(0, 0);
@@ -131,7 +142,7 @@ __global__ __launch_bounds__(64) void kv_split_kernel(const typename E::T* __res
   v8 qf[KS];
   {
     const bool qv = q0 + r < Nq;
-    const T* qrow = Q + ((size_t)bh * Nq + (qv ? q0 + r : 0)) * D;
+    const T* qrow = Q + (bi * lq.sb + hi * lq.sh) + (size_t)(qv ? q0 + r : 0) * lq.sn;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       v8 x = *(const v8*)(qrow + ks * 16 + 8 * h);
@@ -255,7 +266,7 @@ template <typename E, int D>
 __global__ __launch_bounds__(256) void kv_merge_kernel(const float* __restrict__ part_acc,
                                                        const float* __restrict__ part_stat,
                                                        typename E::T* __restrict__ O, float* __restrict__ LSE,
-                                                       int P) {
+                                                       Lay lo, int H, int Nq, int P) {
   using T = typename E::T;
   constexpr int EL = D / 64;   // elements of the row per lane
   constexpr int U = 8;         // splits per batch of loads
@@ -311,7 +322,9 @@ __global__ __launch_bounds__(256) void kv_merge_kernel(const float* __restrict__
   den = (red_s[0][0] + red_s[1][0]) + (red_s[2][0] + red_s[3][0]);
   lsum = (red_s[0][1] + red_s[1][1]) + (red_s[2][1] + red_s[3][1]);
   const float inv = 1.0f / den;
-  T* orow = O + row * D + lane * EL;
+  const int qi = (int)(row % (unsigned)Nq), bh = (int)(row / (unsigned)Nq);
+  const int bi = bh / H, hi = bh - bi * H;
+  T* orow = O + (bi * lo.sb + hi * lo.sh) + (size_t)qi * lo.sn + lane * EL;
 #pragma unroll
   for (int e = 0; e < EL; ++e) {
     const int d = lane * EL + e;
@@ -331,8 +344,10 @@ hipError_t launch_kv_cfg(const KvArgs& a) {
   const typename E::T* v = (const typename E::T*)a.v;
   float* pacc = a.part_acc;
   float* pst = a.part_stat;
-  void* args[] = {(void*)&q, (void*)&k, (void*)&v, (void*)&pacc, (void*)&pst, (void*)&Nq,
-                  (void*)&Nk, (void*)&nqb, (void*)&P, (void*)&chunk, (void*)&scale_log2};
+  Lay lq = a.lq, lk = a.lk, lv = a.lv, lo = a.lo;
+  const int H = (int)a.H;
+  void* args[] = {(void*)&q, (void*)&k, (void*)&v, (void*)&pacc, (void*)&pst, (void*)&lq, (void*)&lk, (void*)&lv,
+                  (void*)&H, (void*)&Nq, (void*)&Nk, (void*)&nqb, (void*)&P, (void*)&chunk, (void*)&scale_log2};
   hipError_t e = launch_kernel((const void*)kv_split_kernel<E, D, CAUSAL>, dim3((unsigned)(BH * nqb * P)),
                                dim3(64), args, a.stream, 4);
   if (e != hipSuccess) return e;
@@ -341,7 +356,7 @@ hipError_t launch_kv_cfg(const KvArgs& a) {
   float* lse = a.lse;
   const float* cacc = pacc;
   const float* cst = pst;
-  void* margs[] = {(void*)&cacc, (void*)&cst, (void*)&o, (void*)&lse, (void*)&P};
+  void* margs[] = {(void*)&cacc, (void*)&cst, (void*)&o, (void*)&lse, (void*)&lo, (void*)&H, (void*)&Nq, (void*)&P};
   return launch_kernel((const void*)kv_merge_kernel<E, D>, dim3((unsigned)rows), dim3(256), margs, a.stream, 5);
 }
 

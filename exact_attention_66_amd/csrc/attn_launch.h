@@ -8,6 +8,16 @@
 
 namespace attn {
 
+// Element strides of one [B, H, N, d] tensor of 16-bit values whose last
+// dimension is contiguous: element (b, h, n, c) sits at b*sb + h*sh + n*sn + c.
+struct Lay {
+  int64_t sb, sh;
+  int32_t sn;
+  int32_t unused;
+};
+
+inline Lay contiguous_lay(int64_t H, int64_t N, int64_t d) { return Lay{H * N * d, N * d, (int32_t)d, 0}; }
+
 struct FwdArgs {
   const void* q;
   const void* k;
@@ -19,6 +29,7 @@ struct FwdArgs {
   bool causal;
   int dtype;  // 0 bf16, 1 fp16
   hipStream_t stream;
+  Lay lq, lk, lv, lo;
 };
 
 struct BwdArgs {
@@ -69,6 +80,7 @@ struct KvArgs {
   float* part_acc;   // workspace [B,H,Nq,splits,d] fp32: unnormalised O of each split
   float* part_stat;  // workspace [B,H,Nq,splits,4] fp32: m (log2 units), l, rounded l, unused
   hipStream_t stream;
+  Lay lq, lk, lv, lo;  // q, o: [B,H,Nq,d]; k, v: [B,H,Nk,d]
 };
 
 // Split plan: `requested` splits (0: about 1024 waves in all, i.e. one per

@@ -70,6 +70,8 @@ enum attn_status {
   ATTN_ERR_WORKSPACE_TOO_SMALL = 8,   /* workspace NULL or below attn_bwd_workspace_bytes() */
   ATTN_ERR_ALIASING = 9,              /* an output overlaps an input or another output */
   ATTN_ERR_HIP = 10,                  /* a kernel launch failed; see attn_last_hip_error() */
+  ATTN_ERR_BAD_LAYOUT = 11,           /* strides negative, not multiples of 8 elements, token stride
+                                         >= 2^24, or an output layout whose elements overlap */
 };
 
 /*
@@ -85,6 +87,28 @@ enum attn_status {
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal,
              int dtype, void* stream);
+
+/*
+ * attn_fwd_strided - attn_fwd for tensors in any [B, H, N, d] layout whose
+ * last dimension is contiguous, e.g. [B, N, H, d] (token-major, "NHD"), a
+ * packed [B, N, 3, H, d] QKV buffer, or a head stride of 0 to share one K
+ * and V over all heads.  Page "Flash Attention V2 大模型时代的算力救星" §4.2
+ * names the layout and 128-bit alignment demands of attention kernels as an
+ * integration cost; here the kernels address the caller's layout directly.
+ *   strides  12 int64 element strides, (batch, head, token) for q, k, v, o in
+ *            that order; element (b, h, n, c) of a tensor is at
+ *            base + b*s_batch + h*s_head + n*s_token + c.
+ * Every stride must be >= 0 and a multiple of 8 (so every row is 16-byte
+ * aligned), token strides < 2^24, batch and head strides <= 2^40; o's
+ * layout must not map two elements to one address (ATTN_ERR_BAD_LAYOUT
+ * otherwise).  lse stays a contiguous [B,H,N] fp32 array.  Aliasing is
+ * checked on each tensor's address range [base, last element].
+ * attn_fwd(...) is attn_fwd_strided with the contiguous strides
+ * (H*N*d, N*d, d) for all four tensors.
+ */
+int attn_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int64_t B, int64_t H, int64_t N, int64_t d, const int64_t* strides,
+                     float scale, int causal, int dtype, void* stream);
 
 /*
  * attn_bwd_workspace_bytes - size of the scratch buffer attn_bwd needs.  With
@@ -150,6 +174,18 @@ int attn_fwd_kvcache(const void* q, const void* k, const void* v, void* o, float
                      int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale,
                      int causal, int dtype, int num_splits, void* workspace,
                      size_t workspace_bytes, void* stream);
+
+/*
+ * attn_fwd_kvcache_strided - attn_fwd_kvcache for tensors in any layout with
+ * a contiguous last dimension, strides as for attn_fwd_strided (q and o
+ * [B,H,Nq,d], k and v [B,H,Nk,d]).  A token-major cache [B, Nmax, H, d]
+ * allocated for Nmax >= Nk positions is passed as it is: batch stride
+ * Nmax*H*d, head stride d, token stride H*d.
+ */
+int attn_fwd_kvcache_strided(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                             const int64_t* strides, float scale, int causal, int dtype,
+                             int num_splits, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * attn_fwd_kvcache_workspace_bytes - workspace of attn_fwd_kvcache: per

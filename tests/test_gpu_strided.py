@@ -1,0 +1,110 @@
+"""Forward and KV-cache forward on tensors in other layouts (GPU).
+
+attn_fwd_strided and attn_fwd_kvcache_strided take per-tensor (batch, head,
+token) strides with a contiguous head dimension.  Each case runs a layout
+the callers of attention use ([B, N, H, d] token-major tensors, a packed
+[B, N, 3, H, d] QKV buffer, one K and V shared by every head, a KV cache
+allocated for more positions than it holds), checks every element against
+the fp64 oracle on contiguous copies, checks that the result is bitwise the
+one the contiguous call gives (the same kernels, only the addresses
+differ), and checks that no element outside the output view was written.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from parity import check_lse, check_o, f64, log, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(B, H, N, d, dt, seed, Nk=None):
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    Nk = N if Nk is None else Nk
+    tdt = {"bf16": torch.bfloat16, "fp16": torch.float16}[dt]
+    q = torch.randn((B, H, N, d), generator=g).to(tdt)
+    k = torch.randn((B, H, Nk, d), generator=g).to(tdt)
+    v = torch.randn((B, H, Nk, d), generator=g).to(tdt)
+    return q, k, v
+
+
+def _oracle(q, k, v, scale, causal):
+    return oracle.forward(*(workloads.to_f64_numpy(t.contiguous().cpu()) for t in (q, k, v)), scale, causal)
+
+
+CASES = [(2, 3, 200, 64, "bf16", True), (1, 4, 256, 128, "fp16", False), (2, 2, 129, 128, "bf16", False),
+         (1, 2, 1000, 128, "bf16", True)]
+
+
+@pytest.mark.parametrize("B,H,N,d,dt,causal", CASES)
+def test_forward_token_major_layout(B, H, N, d, dt, causal):
+    """q, k, v, o stored [B, N, H, d] (viewed as [B, H, N, d])."""
+    ea = require_gpu()
+    q, k, v = _inputs(B, H, N, d, dt, 41000 + N + d)
+    scale = ea.default_scale(d)
+    qs, ks, vs = (t.transpose(1, 2).contiguous().cuda().transpose(1, 2) for t in (q, k, v))
+    # output view inside a NaN buffer with one extra head per token
+    obuf = torch.full((B, N, H + 1, d), float("nan"), dtype=q.dtype, device="cuda")
+    o = obuf[:, :, :H].transpose(1, 2)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    log(f"strided fwd NHD B={B} H={H} N={N} d={d} {dt} causal={causal} strides q={qs.stride()} o={o.stride()}")
+    ea.attn_fwd(qs, ks, vs, o, lse, scale, causal)
+    oc, lc = ea.forward(q.cuda(), k.cuda(), v.cuda(), scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = _oracle(q, k, v, scale, causal)
+    check_o(f64(o), o_ref, dt)
+    check_lse(f64(lse), lse_ref)
+    assert torch.equal(o, oc) and torch.equal(lse, lc), "strided result differs from the contiguous call"
+    assert torch.isnan(obuf[:, :, H]).all(), "wrote outside the output view"
+
+
+def test_forward_packed_qkv_and_shared_kv_heads():
+    ea = require_gpu()
+    B, H, N, d = 2, 4, 300, 128
+    q, k, v = _inputs(B, H, N, d, "bf16", 42001)
+    scale = ea.default_scale(d)
+    # packed [B, N, 3, H, d]
+    qkv = torch.stack([t.transpose(1, 2) for t in (q, k, v)], dim=2).contiguous().cuda()
+    qp, kp, vp = (qkv[:, :, i].transpose(1, 2) for i in range(3))
+    log(f"strided fwd packed QKV strides {qp.stride()}")
+    o, lse = ea.forward(qp, kp, vp, scale=scale, causal=True)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = _oracle(q, k, v, scale, True)
+    check_o(f64(o), o_ref, "bf16")
+    check_lse(f64(lse), lse_ref)
+    # one K and V for all heads: head stride 0
+    k1, v1 = k[:, :1], v[:, :1]
+    ke, ve = k1.cuda().expand(B, H, N, d), v1.cuda().expand(B, H, N, d)
+    log(f"strided fwd shared K/V heads strides {ke.stride()}")
+    o2, lse2 = ea.forward(q.cuda(), ke, ve, scale=scale, causal=False)
+    torch.cuda.synchronize()
+    o_ref2, lse_ref2 = _oracle(q, k1.expand(B, H, N, d), v1.expand(B, H, N, d), scale, False)
+    check_o(f64(o2), o_ref2, "bf16")
+    check_lse(f64(lse2), lse_ref2)
+
+
+@pytest.mark.parametrize("Nq,Nk,Nmax,splits", [(1, 4000, 4096, 0), (8, 1111, 2048, 0), (40, 300, 320, 3)])
+def test_kvcache_token_major_cache(Nq, Nk, Nmax, splits):
+    """A [B, Nmax, H, d] cache holding Nk positions, queries [B, Nq, H, d]."""
+    ea = require_gpu()
+    B, H, d = 2, 4, 128
+    q, k, v = _inputs(B, H, Nq, d, "bf16", 43000 + Nk, Nk=Nk)
+    scale = ea.default_scale(d)
+    kc = torch.full((B, Nmax, H, d), float("nan"), dtype=k.dtype)
+    vc = torch.full((B, Nmax, H, d), float("nan"), dtype=v.dtype)
+    kc[:, :Nk] = k.transpose(1, 2)
+    vc[:, :Nk] = v.transpose(1, 2)
+    kc, vc = kc.cuda(), vc.cuda()
+    ks, vs = kc[:, :Nk].transpose(1, 2), vc[:, :Nk].transpose(1, 2)
+    qs = q.transpose(1, 2).contiguous().cuda().transpose(1, 2)
+    log(f"strided kvcache Nq={Nq} Nk={Nk} Nmax={Nmax} splits={splits} k strides {ks.stride()}")
+    o, lse = ea.forward_kvcache(qs, ks, vs, scale=scale, causal=True, num_splits=splits)
+    oc, lc = ea.forward_kvcache(q.cuda(), k.cuda(), v.cuda(), scale=scale, causal=True, num_splits=splits)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = _oracle(q, k, v, scale, True)
+    check_o(f64(o), o_ref, "bf16")
+    check_lse(f64(lse), lse_ref)
+    assert torch.equal(o.contiguous(), oc) and torch.equal(lse, lc), "strided result differs from the contiguous call"
