@@ -14,6 +14,7 @@ from ._binding import (  # noqa: F401
     STATUS_NAMES,
     AttnError,
     attn_bwd,
+    attn_bwd_strided_workspace_bytes,
     attn_bwd_workspace_bytes,
     attn_fwd,
     attn_fwd_kvcache,

@@ -27,6 +27,7 @@ STATUS_NAMES = {
 }
 EXPORTED = ["attn_fwd", "attn_fwd_strided", "attn_bwd_workspace_bytes", "attn_bwd", "attn_fwd_kvcache",
             "attn_fwd_kvcache_strided", "attn_fwd_kvcache_workspace_bytes", "attn_fwd_kvcache_splits",
+            "attn_bwd_strided", "attn_bwd_strided_workspace_bytes",
             "attn_profile_start",
             "attn_profile_stop", "attn_status_string", "attn_last_hip_error"]
 # attn_kernel_kind values
@@ -69,6 +70,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_fwd_kvcache_strided.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64p, f32, i32, i32, i32,
                                              vp, sz, vp]
     lib.attn_fwd_kvcache_strided.restype = i32
+    lib.attn_bwd_strided.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64p, f32, i32, i32, vp,
+                                     sz, vp]
+    lib.attn_bwd_strided.restype = i32
+    lib.attn_bwd_strided_workspace_bytes.argtypes = [i64, i64, i64, i64]
+    lib.attn_bwd_strided_workspace_bytes.restype = sz
     lib.attn_fwd_kvcache_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i32]
     lib.attn_fwd_kvcache_workspace_bytes.restype = sz
     lib.attn_fwd_kvcache_splits.argtypes = [i64, i64, i64, i64, i64, i32]
@@ -114,6 +120,10 @@ def attn_bwd_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
     return int(load().attn_bwd_workspace_bytes(B, H, N, d))
 
 
+def attn_bwd_strided_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
+    return int(load().attn_bwd_strided_workspace_bytes(B, H, N, d))
+
+
 def attn_fwd_kvcache_workspace_bytes(B: int, H: int, Nq: int, Nk: int, d: int, num_splits: int = 0) -> int:
     return int(load().attn_fwd_kvcache_workspace_bytes(B, H, Nq, Nk, d, int(num_splits)))
 
@@ -146,11 +156,11 @@ def _strided_ptr(t: torch.Tensor) -> Optional[int]:
 
 
 def _strides12(*ts) -> "ctypes.Array":
-    """(batch, head, token) element strides of four [B, H, N, d] tensors, as int64[12]."""
+    """(batch, head, token) element strides of [B, H, N, d] tensors, as int64[3 * len(ts)]."""
     vals = []
     for t in ts:
         vals += [int(t.stride(0)), int(t.stride(1)), int(t.stride(2))]
-    return (ctypes.c_int64 * 12)(*vals)
+    return (ctypes.c_int64 * len(vals))(*vals)
 
 
 def _all_contiguous(*ts) -> bool:
@@ -199,9 +209,16 @@ def attn_bwd(q, k, v, o, dO, lse, dq, dk, dv, scale: float, causal: bool, worksp
     if tuple(lse.shape) != (B, H, N) or lse.dtype != torch.float32:
         raise ValueError("lse must be a float32 [B, H, N] tensor")
     ws_bytes = workspace.numel() * workspace.element_size()
-    st = load().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
-                         B, H, N, d, float(scale), int(bool(causal)), _dtype_code(q), _ptr(workspace),
-                         ws_bytes, _stream(stream))
+    if _all_contiguous(q, k, v, o, dO, dq, dk, dv):
+        st = load().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                             B, H, N, d, float(scale), int(bool(causal)), _dtype_code(q), _ptr(workspace),
+                             ws_bytes, _stream(stream))
+    else:   # other layouts: strides passed through (workspace: attn_bwd_strided_workspace_bytes)
+        ts = (q, k, v, o, dO, dq, dk, dv)
+        st = load().attn_bwd_strided(*(_strided_ptr(t) for t in ts[:5]), _ptr(lse),
+                                     *(_strided_ptr(t) for t in ts[5:]), B, H, N, d, _strides12(*ts),
+                                     float(scale), int(bool(causal)), _dtype_code(q), _ptr(workspace), ws_bytes,
+                                     _stream(stream))
     if st != ATTN_OK:
         raise AttnError(st, "attn_bwd")
 
@@ -252,9 +269,11 @@ def backward(q, k, v, o, lse, dO, scale: Optional[float] = None, causal: bool = 
     """Allocate (dq, dk, dv) and, if not given, the workspace; run attn_bwd."""
     B, H, N, d = _shape4(q)
     scale = default_scale(d) if scale is None else scale
-    if workspace is None:
-        workspace = torch.empty(attn_bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=q.device)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    if workspace is None:
+        nbytes = (attn_bwd_workspace_bytes(B, H, N, d) if _all_contiguous(q, k, v, o, dO, dq, dk, dv)
+                  else attn_bwd_strided_workspace_bytes(B, H, N, d))
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
     attn_bwd(q, k, v, o, dO, lse, dq, dk, dv, scale, causal, workspace, stream)
     return dq, dk, dv
 

@@ -64,10 +64,12 @@ size_t lay_extent(const attn::Lay& l, int64_t B, int64_t H, int64_t N, int64_t d
 // No two elements of an output layout share an address: with the
 // dimensions of size > 1 sorted by stride, each stride must reach past
 // everything the smaller ones span (the d elements of a row included).
-bool lay_injective(const attn::Lay& l, int64_t B, int64_t H, int64_t N, int64_t d) {
-  struct Dm { int64_t n, s; } dims[3] = {{B, l.sb}, {H, l.sh}, {N, l.sn}};
-  for (int i = 0; i < 3; ++i)
-    for (int j = i + 1; j < 3; ++j)
+// An optional fourth dimension (count n4, stride s4) stands for a second
+// tensor of the same layout s4 elements further on.
+bool lay_injective(const attn::Lay& l, int64_t B, int64_t H, int64_t N, int64_t d, int64_t n4 = 1, int64_t s4 = 0) {
+  struct Dm { int64_t n, s; } dims[4] = {{B, l.sb}, {H, l.sh}, {N, l.sn}, {n4, s4}};
+  for (int i = 0; i < 4; ++i)
+    for (int j = i + 1; j < 4; ++j)
       if (dims[j].s < dims[i].s) std::swap(dims[i], dims[j]);
   int64_t span = d;
   for (const Dm& x : dims) {
@@ -76,6 +78,20 @@ bool lay_injective(const attn::Lay& l, int64_t B, int64_t H, int64_t N, int64_t 
     span = x.s * (x.n - 1) + span;
   }
   return true;
+}
+
+// Two output tensors share no element: their address ranges are apart, or
+// they have one layout and sit a whole number of elements apart such that
+// the pair is itself an injective layout (e.g. dQ, dK, dV interleaved in one
+// packed [B, N, 3, H, d] gradient buffer).
+bool outputs_disjoint(const void* a, const attn::Lay& la, const void* b, const attn::Lay& lb, int64_t B, int64_t H,
+                      int64_t N, int64_t d) {
+  if (!overlaps(a, lay_extent(la, B, H, N, d), b, lay_extent(lb, B, H, N, d))) return true;
+  if (la.sb != lb.sb || la.sh != lb.sh || la.sn != lb.sn) return false;
+  const intptr_t delta = reinterpret_cast<intptr_t>(b) - reinterpret_cast<intptr_t>(a);
+  if (delta % 2 != 0) return false;
+  const int64_t de = (int64_t)(delta < 0 ? -delta : delta) / 2;
+  return lay_injective(la, B, H, N, d, 2, de);
 }
 
 int launch_status(hipError_t e) {
@@ -160,6 +176,71 @@ int kv_impl(const void* q, const void* k, const void* v, void* o, float* lse, in
   return launch_status(attn::launch_kvcache(a));
 }
 
+size_t bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d) {
+  // the padded length (N rounded up to 64) must not overflow either
+  if (checked_elems(B, H, N, d) < 0 || checked_elems(B, H, attn::bwd_padded_n(N), d) < 0 || (d != 64 && d != 128))
+    return 0;
+  return 2 * attn::bwd_delta_bytes(B, H, N) + 3 * attn::bwd_tcopy_bytes(B, H, N, d) +
+         4 * attn::bwd_tail_bytes(B, H, N, d);
+}
+
+// Backward with per-tensor layouts (lays: q, k, v, o, dO, dq, dk, dv); lse
+// contiguous.  strided: the workspace also holds contiguous copies of q, k,
+// v and dO, written by the preprocess.
+int bwd_impl(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
+             void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N, int64_t d, const attn::Lay* lays,
+             bool strided, float scale, int causal, int dtype, void* workspace, size_t workspace_bytes,
+             void* stream) {
+  if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv) return ATTN_ERR_NULL_PTR;
+  int st = check_common(B, H, N, d, scale, dtype);
+  if (st != ATTN_OK) return st;
+  for (int i = 0; i < 8; ++i)
+    if (!lay_ok(lays[i])) return ATTN_ERR_BAD_LAYOUT;
+  for (int i = 5; i < 8; ++i)
+    if (!lay_injective(lays[i], B, H, N, d)) return ATTN_ERR_BAD_LAYOUT;
+  const size_t base_need = bwd_workspace_bytes(B, H, N, d);
+  if (base_need == 0) return ATTN_ERR_BAD_SHAPE;
+  const size_t cb = attn::align256((size_t)(B * H * N * d) * 2);   // one contiguous copy
+  const size_t need = base_need + (strided ? 4 * cb : 0);
+  if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE_TOO_SMALL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dO) || !aligned16(lse) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return ATTN_ERR_MISALIGNED;
+  const size_t lb = (size_t)(B * H * N) * 4;
+  struct R { const void* p; size_t n; };
+  const R ins[] = {{q, lay_extent(lays[0], B, H, N, d)},  {k, lay_extent(lays[1], B, H, N, d)},
+                   {v, lay_extent(lays[2], B, H, N, d)},  {o, lay_extent(lays[3], B, H, N, d)},
+                   {dO, lay_extent(lays[4], B, H, N, d)}, {lse, lb}};
+  const R outs[] = {{dq, lay_extent(lays[5], B, H, N, d)}, {dk, lay_extent(lays[6], B, H, N, d)},
+                    {dv, lay_extent(lays[7], B, H, N, d)}, {workspace, need}};
+  for (int i = 0; i < 4; ++i) {
+    for (const R& y : ins)
+      if (overlaps(outs[i].p, outs[i].n, y.p, y.n)) return ATTN_ERR_ALIASING;
+    if (i < 3 && overlaps(outs[i].p, outs[i].n, workspace, need)) return ATTN_ERR_ALIASING;
+  }
+  for (int i = 0; i < 3; ++i)
+    for (int j = i + 1; j < 3; ++j)
+      if (!outputs_disjoint(outs[i].p, lays[5 + i], outs[j].p, lays[5 + j], B, H, N, d)) return ATTN_ERR_ALIASING;
+
+  char* ws = (char*)workspace;
+  const size_t sb = attn::bwd_delta_bytes(B, H, N), t0 = 2 * sb, tcb = attn::bwd_tcopy_bytes(B, H, N, d);
+  const size_t tl0 = t0 + 3 * tcb, tlb = attn::bwd_tail_bytes(B, H, N, d);
+  char* tail = tlb ? ws + tl0 : nullptr;
+  attn::BwdArgs a{q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal != 0, dtype,
+                  (float*)ws, (float*)(ws + sb), ws + t0, ws + t0 + tcb, ws + t0 + 2 * tcb,
+                  tail, tail ? tail + tlb : nullptr, tail ? tail + 2 * tlb : nullptr, tail ? tail + 3 * tlb : nullptr,
+                  (hipStream_t)stream, strided, lays[0], lays[1], lays[2], lays[3], lays[4], lays[5], lays[6],
+                  lays[7], nullptr, nullptr, nullptr, nullptr};
+  if (strided) {
+    char* cp = ws + base_need;
+    a.qc = cp;
+    a.kc = cp + cb;
+    a.vc = cp + 2 * cb;
+    a.doc = cp + 3 * cb;
+  }
+  return launch_status(attn::launch_bwd(a));
+}
+
 attn::Lay lay_from(const int64_t* s) { return attn::Lay{s[0], s[1], (int32_t)std::min<int64_t>(s[2], INT32_MAX), 0}; }
 
 }  // namespace
@@ -184,45 +265,34 @@ int attn_fwd_strided(const void* q, const void* k, const void* v, void* o, float
 }
 
 size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d) {
-  // the padded length (N rounded up to 64) must not overflow either
-  if (checked_elems(B, H, N, d) < 0 || checked_elems(B, H, attn::bwd_padded_n(N), d) < 0 || (d != 64 && d != 128))
-    return 0;
-  return 2 * attn::bwd_delta_bytes(B, H, N) + 3 * attn::bwd_tcopy_bytes(B, H, N, d) +
-         4 * attn::bwd_tail_bytes(B, H, N, d);
+  return bwd_workspace_bytes(B, H, N, d);
 }
 
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
              void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal,
              int dtype, void* workspace, size_t workspace_bytes, void* stream) {
-  if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv) return ATTN_ERR_NULL_PTR;
-  int st = check_common(B, H, N, d, scale, dtype);
-  if (st != ATTN_OK) return st;
-  const size_t need = attn_bwd_workspace_bytes(B, H, N, d);
-  if (need == 0) return ATTN_ERR_BAD_SHAPE;
-  if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE_TOO_SMALL;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dO) || !aligned16(lse) ||
-      !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || (reinterpret_cast<uintptr_t>(workspace) & 255u))
-    return ATTN_ERR_MISALIGNED;
-  const size_t tb = (size_t)(B * H * N * d) * 2, lb = (size_t)(B * H * N) * 4;
-  struct R { const void* p; size_t n; };
-  const R ins[] = {{q, tb}, {k, tb}, {v, tb}, {o, tb}, {dO, tb}, {lse, lb}};
-  const R outs[] = {{dq, tb}, {dk, tb}, {dv, tb}, {workspace, need}};
-  for (const R& x : outs) {
-    for (const R& y : ins)
-      if (overlaps(x.p, x.n, y.p, y.n)) return ATTN_ERR_ALIASING;
-    for (const R& y : outs)
-      if (&x != &y && overlaps(x.p, x.n, y.p, y.n)) return ATTN_ERR_ALIASING;
-  }
+  if (checked_elems(B, H, N, d) < 0) return ATTN_ERR_BAD_SHAPE;
+  const attn::Lay c = attn::contiguous_lay(H, N, d);
+  const attn::Lay lays[8] = {c, c, c, c, c, c, c, c};
+  return bwd_impl(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, lays, false, scale, causal, dtype, workspace,
+                  workspace_bytes, stream);
+}
 
-  char* ws = (char*)workspace;
-  const size_t sb = attn::bwd_delta_bytes(B, H, N), t0 = 2 * sb, tcb = attn::bwd_tcopy_bytes(B, H, N, d);
-  const size_t tl0 = t0 + 3 * tcb, tlb = attn::bwd_tail_bytes(B, H, N, d);
-  char* tail = tlb ? ws + tl0 : nullptr;
-  attn::BwdArgs a{q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal != 0, dtype,
-                  (float*)ws, (float*)(ws + sb), ws + t0, ws + t0 + tcb, ws + t0 + 2 * tcb,
-                  tail, tail ? tail + tlb : nullptr, tail ? tail + 2 * tlb : nullptr, tail ? tail + 3 * tlb : nullptr,
-                  (hipStream_t)stream};
-  return launch_status(attn::launch_bwd(a));
+size_t attn_bwd_strided_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d) {
+  const size_t base = attn_bwd_workspace_bytes(B, H, N, d);
+  return base ? base + 4 * attn::align256((size_t)(B * H * N * d) * 2) : 0;
+}
+
+int attn_bwd_strided(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
+                     void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N, int64_t d, const int64_t* strides,
+                     float scale, int causal, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!strides) return ATTN_ERR_NULL_PTR;
+  for (int i = 0; i < 24; ++i)
+    if (strides[i] < 0 || strides[i] > ((int64_t)1 << 40)) return ATTN_ERR_BAD_LAYOUT;
+  attn::Lay lays[8];
+  for (int i = 0; i < 8; ++i) lays[i] = lay_from(strides + 3 * i);
+  return bwd_impl(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, lays, true, scale, causal, dtype, workspace,
+                  workspace_bytes, stream);
 }
 
 size_t attn_fwd_kvcache_workspace_bytes(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int num_splits) {

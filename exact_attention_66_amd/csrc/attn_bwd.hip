@@ -85,7 +85,7 @@ constexpr float kLog2e = 1.44269504088896340736f;
 // from there and never read past the end of an input.  TAIL (N not a
 // multiple of 64) is a template flag, so that the checks cost nothing when
 // there is no padding.
-template <typename E, int D, bool TAIL>
+template <typename E, int D, bool TAIL, bool STRIDED>
 __global__ __launch_bounds__(256) void bwd_prep(const typename E::T* __restrict__ Q,
                                                 const typename E::T* __restrict__ K,
                                                 const typename E::T* __restrict__ V,
@@ -96,7 +96,10 @@ __global__ __launch_bounds__(256) void bwd_prep(const typename E::T* __restrict_
                                                 typename E::T* __restrict__ KT, typename E::T* __restrict__ dOT,
                                                 typename E::T* __restrict__ QTail, typename E::T* __restrict__ dOTail,
                                                 typename E::T* __restrict__ KTail, typename E::T* __restrict__ VTail,
-                                                int N, int Np, float inv_scale) {
+                                                int N, int Np, float inv_scale, Lay lq, Lay lk, Lay lv, Lay lo,
+                                                Lay ldo, int H, typename E::T* __restrict__ Qc,
+                                                typename E::T* __restrict__ Kc, typename E::T* __restrict__ Vc,
+                                                typename E::T* __restrict__ dOc) {
   using T = typename E::T;
   using v8 = typename E::v8;
   constexpr int R = 64;                // tokens per workgroup
@@ -112,8 +115,9 @@ __global__ __launch_bounds__(256) void bwd_prep(const typename E::T* __restrict_
   const int nrb = Np / R;
   const int bh = (int)(blockIdx.x / nrb);
   const int rb = (int)(blockIdx.x % nrb);
-  const size_t head = (size_t)bh * N * D;     // inputs [B*H][N][d]
+  const size_t head = (size_t)bh * N * D;     // inputs [B*H][N][d] (contiguous copies when STRIDED)
   const size_t headp = (size_t)bh * Np * D;   // transposed copies [B*H][d][Np]
+  const int bi = bh / H, hi = bh - bi * H;    // batch and head (STRIDED: the inputs' own layouts)
   const int row0 = rb * R;
   const bool tail = TAIL && row0 + R > N;     // the block holding the last tokens of a ragged N
 
@@ -125,8 +129,23 @@ __global__ __launch_bounds__(256) void bwd_prep(const typename E::T* __restrict_
     const int tok = row0 + row;
     const bool in = !TAIL || tok < N;
     const size_t g = head + (size_t)tok * D + col;
-    v8 qv = {}, kv = {}, dov = {}, ov = {};
-    if (in) {
+    v8 qv = {}, kv = {}, dov = {}, ov = {}, vv = {};
+    if constexpr (STRIDED) {
+      // read each input in its own layout and keep contiguous copies of Q,
+      // K, V and dO for the dK/dV and dQ kernels
+      if (in) {
+        auto at = [&](const Lay& l) { return bi * l.sb + hi * l.sh + (int64_t)tok * l.sn + col; };
+        qv = *(const v8*)(Q + at(lq));
+        kv = *(const v8*)(K + at(lk));
+        dov = *(const v8*)(dO + at(ldo));
+        ov = *(const v8*)(O + at(lo));
+        vv = *(const v8*)(V + at(lv));
+        *(v8*)(Qc + g) = qv;
+        *(v8*)(Kc + g) = kv;
+        *(v8*)(Vc + g) = vv;
+        *(v8*)(dOc + g) = dov;
+      }
+    } else if (in) {
       qv = *(const v8*)(Q + g);
       kv = *(const v8*)(K + g);
       dov = *(const v8*)(dO + g);
@@ -148,8 +167,7 @@ __global__ __launch_bounds__(256) void bwd_prep(const typename E::T* __restrict_
     }
     if (tail) {
       const size_t gt = (size_t)bh * R * D + (size_t)row * D + col;
-      v8 vv = {};
-      if (in) vv = *(const v8*)(V + g);
+      if (!STRIDED && in) vv = *(const v8*)(V + g);
       *(v8*)(QTail + gt) = qv;
       *(v8*)(dOTail + gt) = dov;
       *(v8*)(KTail + gt) = kv;
@@ -209,14 +227,15 @@ __global__ __launch_bounds__(256) void bwd_prep(const typename E::T* __restrict_
 // tile after it starts into the buffer just released.  Tiles that reach the
 // causal diagonal come first and run the same pipeline with the mask applied
 // (sub-tiles entirely above the diagonal come out as P = 0).
-template <typename E, int D, bool CAUSAL, int NW, int BMQ, bool TAIL>
+template <typename E, int D, bool CAUSAL, int NW, int BMQ, bool TAIL, bool STRIDED>
 __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv(
     const typename E::T* __restrict__ Q, const typename E::T* __restrict__ K,
     const typename E::T* __restrict__ V, const typename E::T* __restrict__ dO,
     const typename E::T* __restrict__ QT, const typename E::T* __restrict__ dOT,
     const typename E::T* __restrict__ QTail, const typename E::T* __restrict__ dOTail,
     const float* __restrict__ NLSE, const float* __restrict__ Dvec, typename E::T* __restrict__ dK,
-    typename E::T* __restrict__ dV, int BH, int N, int Np_arg, int nkb, float scale, float scale_log2) {
+    typename E::T* __restrict__ dV, int BH, int N, int Np_arg, int nkb, float scale, float scale_log2, Lay ldk,
+    Lay ldv, int H) {
   using T = typename E::T;
   using v8 = typename E::v8;
   const int Np = TAIL ? Np_arg : N;     // padded length: N itself unless TAIL
@@ -258,6 +277,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv(
   const int nfull = N / BMQ;            // tiles wholly inside the sequence
   int kb0, kw0, it0, ntile, nmask;
   size_t head;
+  int64_t out_k = 0, out_v = 0;         // STRIDED: dK, dV offsets of (batch, head, key kw0)
   const T *Qh, *dOh, *QTh, *dOTh, *Qtl, *dOtl;
   const float *lse_h, *dd_h;
   auto set_unit = [&](const int u) {
@@ -265,6 +285,11 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv(
     kb0 = (u % nkb) * BN;
     kw0 = kb0 + wu * 32;                 // first key of this wave
     head = (size_t)bh * (size_t)N * D;
+    if constexpr (STRIDED) {
+      const int bi = bh / H, hi = bh - bi * H;
+      out_k = bi * ldk.sb + hi * ldk.sh + (int64_t)kw0 * ldk.sn;
+      out_v = bi * ldv.sb + hi * ldv.sh + (int64_t)kw0 * ldv.sn;
+    }
     const size_t headp = (size_t)bh * (size_t)Np * D;
     Qh = Q + head;
     dOh = dO + head;
@@ -529,6 +554,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv(
     // start the next unit, then store this one's dK = scale * acc, dV = acc
     // (lane holds key kw0 + acc_row(j, h), d = 32db + r)
     const size_t out = head + (size_t)kw0 * D;
+    const int64_t ok0 = out_k, ov0 = out_v;
     const int nvalid = N - kw0;          // keys of this wave inside the sequence
     unit = xcd_snake_unit((int)blockIdx.x, (int)gridDim.x, BH * nkb, ++round);
     __syncthreads();  // every wave is done with this unit's tiles
@@ -544,9 +570,14 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv(
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          const size_t off = out + (size_t)acc_row(j, h) * D + db * 32 + r;
-          dK[off] = (T)(dk_acc[db][j] * scale);
-          dV[off] = (T)dv_acc[db][j];
+          if constexpr (STRIDED) {
+            dK[ok0 + (int64_t)acc_row(j, h) * ldk.sn + db * 32 + r] = (T)(dk_acc[db][j] * scale);
+            dV[ov0 + (int64_t)acc_row(j, h) * ldv.sn + db * 32 + r] = (T)dv_acc[db][j];
+          } else {
+            const size_t off = out + (size_t)acc_row(j, h) * D + db * 32 + r;
+            dK[off] = (T)(dk_acc[db][j] * scale);
+            dV[off] = (T)dv_acc[db][j];
+          }
         }
     } else if (TAIL && nvalid > 0) {  // the sequence ends inside this wave's keys
 #pragma unroll
@@ -554,9 +585,14 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv(
 #pragma unroll
         for (int j = 0; j < 16; ++j)
           if (acc_row(j, h) < nvalid) {
-            const size_t off = out + (size_t)acc_row(j, h) * D + db * 32 + r;
-            dK[off] = (T)(dk_acc[db][j] * scale);
-            dV[off] = (T)dv_acc[db][j];
+            if constexpr (STRIDED) {
+              dK[ok0 + (int64_t)acc_row(j, h) * ldk.sn + db * 32 + r] = (T)(dk_acc[db][j] * scale);
+              dV[ov0 + (int64_t)acc_row(j, h) * ldv.sn + db * 32 + r] = (T)dv_acc[db][j];
+            } else {
+              const size_t off = out + (size_t)acc_row(j, h) * D + db * 32 + r;
+              dK[off] = (T)(dk_acc[db][j] * scale);
+              dV[off] = (T)dv_acc[db][j];
+            }
           }
     }
     if (unit < 0) break;
@@ -582,13 +618,14 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv(
 // buffers, two tiles ahead of their use; a copy instruction fills 64
 // consecutive 16-byte slots, so the padding slot of each row gets a
 // duplicate of the row's last chunk and a tile is a whole number of blocks.
-template <typename E, int D, bool CAUSAL, int NW, int BN, bool TAIL>
+template <typename E, int D, bool CAUSAL, int NW, int BN, bool TAIL, bool STRIDED>
 __global__ __launch_bounds__(NW * 64, ATTN_DQ_MINW) void bwd_dq(
     const typename E::T* __restrict__ Q, const typename E::T* __restrict__ K,
     const typename E::T* __restrict__ V, const typename E::T* __restrict__ dO,
     const typename E::T* __restrict__ KT, const typename E::T* __restrict__ KTail,
     const typename E::T* __restrict__ VTail, const float* __restrict__ NLSE, const float* __restrict__ ND,
-    typename E::T* __restrict__ dQ, int BH, int N, int Np_arg, int nqb, float scale, float scale_log2) {
+    typename E::T* __restrict__ dQ, int BH, int N, int Np_arg, int nqb, float scale, float scale_log2, Lay ldq,
+    int H) {
   using T = typename E::T;
   const int Np = TAIL ? Np_arg : N;     // padded length: N itself unless TAIL
   using v8 = typename E::v8;
@@ -858,7 +895,8 @@ __global__ __launch_bounds__(NW * 64, ATTN_DQ_MINW) void bwd_dq(
     // then store this one's dQ = scale * dQ^T (lane holds query qw0 + r,
     // d = 32db + acc_row(j, h))
     const bool valid = wave_valid && (!TAIL || qw0 + r < N);   // rows past the end are not stored
-    T* const qrow_out = dQ + head + (size_t)(qw0 + r) * D;
+    T* const qrow_out = STRIDED ? dQ + ((bh / H) * ldq.sb + (bh % H) * ldq.sh + (int64_t)(qw0 + r) * ldq.sn)
+                                : dQ + head + (size_t)(qw0 + r) * D;
     unit = xcd_snake_unit((int)blockIdx.x, (int)gridDim.x, BH * nqb, ++round);
     if (unit >= 0) {
       set_unit(unit);
@@ -885,7 +923,7 @@ __global__ __launch_bounds__(NW * 64, ATTN_DQ_MINW) void bwd_dq(
   }
 }
 
-template <typename E, int D, bool CAUSAL, bool TAIL>
+template <typename E, int D, bool CAUSAL, bool TAIL, bool STRIDED>
 hipError_t launch_bwd_cfg(const BwdArgs& a) {
   constexpr int NWK = 4;            // dK/dV: waves per workgroup (32 keys each)
   constexpr int NWQ = ATTN_DQ_NW;
@@ -899,6 +937,18 @@ hipError_t launch_bwd_cfg(const BwdArgs& a) {
   const T* v = (const T*)a.v;
   const T* o = (const T*)a.o;
   const T* dO = (const T*)a.dO;
+  // STRIDED: the preprocess reads the inputs in their layouts and writes
+  // contiguous copies of Q, K, V, dO, which the dK/dV and dQ kernels read
+  T* qc = (T*)a.qc;
+  T* kc = (T*)a.kc;
+  T* vc = (T*)a.vc;
+  T* doc = (T*)a.doc;
+  const T* q2 = STRIDED ? qc : q;
+  const T* k2 = STRIDED ? kc : k;
+  const T* v2 = STRIDED ? vc : v;
+  const T* dO2 = STRIDED ? doc : dO;
+  Lay lq = a.lq, lk = a.lk, lv = a.lv, lo = a.lo, ldo = a.ldo, ldq = a.ldq, ldk = a.ldk, ldv = a.ldv;
+  int H = (int)a.H;
   const float* lse = a.lse;
   T* dq = (T*)a.dq;
   T* dk = (T*)a.dk;
@@ -919,40 +969,48 @@ hipError_t launch_bwd_cfg(const BwdArgs& a) {
   {
     void* args[] = {(void*)&q,   (void*)&k,     (void*)&v,    (void*)&o,     (void*)&dO,    (void*)&lse,
                     (void*)&delta, (void*)&nlse, (void*)&qt, (void*)&kt, (void*)&dot, (void*)&qtail,
-                    (void*)&dotail, (void*)&ktail, (void*)&vtail, (void*)&N, (void*)&Np, (void*)&inv_scale};
-    hipError_t e = launch_kernel((const void*)bwd_prep<E, D, TAIL>, dim3((unsigned)(BH * (Np / 64))), dim3(256), args,
+                    (void*)&dotail, (void*)&ktail, (void*)&vtail, (void*)&N, (void*)&Np, (void*)&inv_scale,
+                    (void*)&lq, (void*)&lk, (void*)&lv, (void*)&lo, (void*)&ldo, (void*)&H, (void*)&qc, (void*)&kc,
+                    (void*)&vc, (void*)&doc};
+    hipError_t e = launch_kernel((const void*)bwd_prep<E, D, TAIL, STRIDED>, dim3((unsigned)(BH * (Np / 64))), dim3(256), args,
                                  a.stream, 1);
     if (e != hipSuccess) return e;
   }
   {
     const int nkb = (N + NWK * 32 - 1) / (NWK * 32);
-    void* args[] = {(void*)&q,     (void*)&k,  (void*)&v,  (void*)&dO, (void*)&qt,  (void*)&dot,
+    void* args[] = {(void*)&q2,    (void*)&k2, (void*)&v2, (void*)&dO2, (void*)&qt,  (void*)&dot,
                     (void*)&qtail, (void*)&dotail, (void*)&nlse, (void*)&delta, (void*)&dk, (void*)&dv,
-                    (void*)&BH, (void*)&N, (void*)&Np, (void*)&nkb, (void*)&scale, (void*)&scale_log2};
-    const void* fn = (const void*)bwd_dkdv<E, D, CAUSAL, NWK, 64, TAIL>;
+                    (void*)&BH, (void*)&N, (void*)&Np, (void*)&nkb, (void*)&scale, (void*)&scale_log2,
+                    (void*)&ldk, (void*)&ldv, (void*)&H};
+    const void* fn = (const void*)bwd_dkdv<E, D, CAUSAL, NWK, 64, TAIL, STRIDED>;
     hipError_t e = launch_kernel(fn, dim3((unsigned)persistent_grid(fn, NWK * 64, nkb * BH)), dim3(NWK * 64), args,
                                  a.stream, 2);
     if (e != hipSuccess) return e;
   }
   {
     const int nqb = (N + NWQ * 32 - 1) / (NWQ * 32);
-    void* args[] = {(void*)&q,    (void*)&k,  (void*)&v,  (void*)&dO, (void*)&kt, (void*)&ktail, (void*)&vtail,
+    void* args[] = {(void*)&q2,   (void*)&k2, (void*)&v2, (void*)&dO2, (void*)&kt, (void*)&ktail, (void*)&vtail,
                     (void*)&nlse, (void*)&delta, (void*)&dq, (void*)&BH, (void*)&N, (void*)&Np, (void*)&nqb,
-                    (void*)&scale, (void*)&scale_log2};
-    const void* fn = (const void*)bwd_dq<E, D, CAUSAL, NWQ, BNQ, TAIL>;
+                    (void*)&scale, (void*)&scale_log2, (void*)&ldq, (void*)&H};
+    const void* fn = (const void*)bwd_dq<E, D, CAUSAL, NWQ, BNQ, TAIL, STRIDED>;
     return launch_kernel(fn, dim3((unsigned)persistent_grid(fn, NWQ * 64, nqb * BH)), dim3(NWQ * 64), args,
                          a.stream, 3);
   }
 }
 
+template <typename E, int D, bool STRIDED>
+hipError_t launch_bwd_s(const BwdArgs& a) {
+  if (a.N % 64 == 0) {
+    if (a.causal) return launch_bwd_cfg<E, D, true, false, STRIDED>(a);
+    return launch_bwd_cfg<E, D, false, false, STRIDED>(a);
+  }
+  if (a.causal) return launch_bwd_cfg<E, D, true, true, STRIDED>(a);
+  return launch_bwd_cfg<E, D, false, true, STRIDED>(a);
+}
+
 template <typename E, int D>
 hipError_t launch_bwd_d(const BwdArgs& a) {
-  if (a.N % 64 == 0) {
-    if (a.causal) return launch_bwd_cfg<E, D, true, false>(a);
-    return launch_bwd_cfg<E, D, false, false>(a);
-  }
-  if (a.causal) return launch_bwd_cfg<E, D, true, true>(a);
-  return launch_bwd_cfg<E, D, false, true>(a);
+  return a.strided ? launch_bwd_s<E, D, true>(a) : launch_bwd_s<E, D, false>(a);
 }
 
 }  // namespace

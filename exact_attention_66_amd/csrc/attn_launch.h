@@ -60,6 +60,17 @@ struct BwdArgs {
   void* ktail;
   void* vtail;
   hipStream_t stream;
+  // Layouts of the eight 16-bit tensors.  When `strided`, the preprocess
+  // reads q, k, v, o, dO in their layouts and writes contiguous [B,H,N,d]
+  // copies of q, k, v, dO to qc, kc, vc, doc (workspace), and dq, dk, dv are
+  // stored in their layouts; otherwise every tensor is contiguous and the
+  // copies are NULL.
+  bool strided;
+  Lay lq, lk, lv, lo, ldo, ldq, ldk, ldv;
+  void* qc;
+  void* kc;
+  void* vc;
+  void* doc;
 };
 
 // Forward for KV-cache shapes: Nq queries against Nk keys, the key axis cut

@@ -200,6 +200,30 @@ size_t attn_fwd_kvcache_workspace_bytes(int64_t B, int64_t H, int64_t Nq, int64_
  * uses (0 for invalid sizes). */
 int attn_fwd_kvcache_splits(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int num_splits);
 
+/*
+ * attn_bwd_strided - attn_bwd for tensors in any [B, H, N, d] layout with a
+ * contiguous last dimension (see attn_fwd_strided).
+ *   strides  24 int64 element strides, (batch, head, token) for q, k, v, o,
+ *            dO, dq, dk, dv in that order.
+ *   workspace  at least attn_bwd_strided_workspace_bytes(B,H,N,d) bytes: the
+ *            preprocess reads q, k, v, o, dO in their layouts and also writes
+ *            contiguous copies of q, k, v and dO there, which the dK/dV and
+ *            dQ kernels read; dq, dk, dv are stored in their own layouts.
+ * dq, dk and dv may interleave in one buffer when they share a layout and
+ * no element is shared (a packed [B, N, 3, H, d] gradient); otherwise outputs
+ * must not overlap inputs, each other or the workspace by address range.
+ * Layout rules and errors as for attn_fwd_strided.
+ */
+int attn_bwd_strided(const void* q, const void* k, const void* v, const void* o,
+                     const void* dO, const float* lse, void* dq, void* dk, void* dv,
+                     int64_t B, int64_t H, int64_t N, int64_t d, const int64_t* strides,
+                     float scale, int causal, int dtype, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/* attn_bwd_strided_workspace_bytes - attn_bwd_workspace_bytes plus four
+ * contiguous 16-bit [B,H,N,d] copies (each rounded up to 256 bytes). */
+size_t attn_bwd_strided_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d);
+
 /* Kernels the library launches, as counted by the profiling window below. */
 enum attn_kernel_kind {
   ATTN_KERNEL_FWD = 0,         /* forward: O and lse */

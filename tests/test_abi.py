@@ -232,3 +232,30 @@ def test_kvcache_strided_checks(lib):
     assert call(qo + cache + cache + [0, 128, 512]) == LAYOUT
     assert lib.attn_fwd_kvcache_strided(P[0], P[1], P[2], P[3], P[4], 2, 4, 3, 500, 128, None, 0.1, 1, 0, 0, P[5],
                                         1 << 24, None) == NULL
+
+
+def bwds(lib, strides=None, dq=P[6], dk=P[7], dv=P[8], ws=P[9], ws_bytes=None, B=1, H=2, N=128, d=64):
+    if strides is None:
+        strides = _contig(H, N, d) * 8
+    arr = None if strides == "null" else (ctypes.c_int64 * 24)(*strides)
+    if ws_bytes is None:
+        ws_bytes = ea.attn_bwd_strided_workspace_bytes(B, H, N, d)
+    return lib.attn_bwd_strided(P[0], P[1], P[2], P[3], P[4], P[5], dq, dk, dv, B, H, N, d, arr, 0.125, 1, 0, ws,
+                                ws_bytes, None)
+
+
+def test_bwd_strided_checks(lib):
+    B, H, N, d = 1, 2, 128, 64
+    assert ea.attn_bwd_strided_workspace_bytes(B, H, N, d) == ea.attn_bwd_workspace_bytes(B, H, N, d) + 4 * B * H * N * d * 2
+    assert ea.attn_bwd_strided_workspace_bytes(0, H, N, d) == 0
+    assert bwds(lib, "null") == NULL
+    assert bwds(lib, _contig(H, N, d) * 7 + [H * N * d, N * d, 4]) == LAYOUT           # dv token stride < 8
+    assert bwds(lib, _contig(H, N, d) * 7 + [H * N * d, 0, d]) == LAYOUT               # dv heads overlap
+    assert bwds(lib, ws_bytes=ea.attn_bwd_workspace_bytes(B, H, N, d)) == WS          # no room for the copies
+    # gradients interleaved in one packed [B, N, 3, H, d] buffer, but shifted by
+    # half a row: dq and dk share elements
+    packed = [N * 3 * H * d, d, 3 * H * d]
+    s = _contig(H, N, d) * 5 + packed * 3
+    assert bwds(lib, s, dq=P[6], dk=P[6] + d, dv=P[6] + 2 * H * d * 2) == ALIAS
+    # dq on top of dk with the same layout
+    assert bwds(lib, dq=P[7]) == ALIAS

@@ -108,3 +108,60 @@ def test_kvcache_token_major_cache(Nq, Nk, Nmax, splits):
     check_o(f64(o), o_ref, "bf16")
     check_lse(f64(lse), lse_ref)
     assert torch.equal(o.contiguous(), oc) and torch.equal(lse, lc), "strided result differs from the contiguous call"
+
+
+def _grads_ref(q, k, v, do, scale, causal):
+    return oracle.backward(*(workloads.to_f64_numpy(t.contiguous().cpu()) for t in (q, k, v, do)), scale, causal)
+
+
+@pytest.mark.parametrize("B,H,N,d,dt,causal", [(2, 3, 256, 64, "bf16", True), (1, 2, 100, 128, "fp16", False),
+                                               (1, 4, 640, 128, "bf16", True)])
+def test_backward_token_major_layout(B, H, N, d, dt, causal):
+    """Forward and backward with all eight tensors stored [B, N, H, d]."""
+    ea = require_gpu()
+    from parity import check_grad
+    q, k, v = _inputs(B, H, N, d, dt, 44000 + N + d)
+    g = torch.Generator(device="cpu")
+    g.manual_seed(44999 + N)
+    do = torch.randn((B, H, N, d), generator=g).to(q.dtype)
+    scale = ea.default_scale(d)
+    nhd = lambda t: t.transpose(1, 2).contiguous().cuda().transpose(1, 2)
+    qs, ks, vs, dos = (nhd(t) for t in (q, k, v, do))
+    log(f"strided bwd NHD B={B} H={H} N={N} d={d} {dt} causal={causal}")
+    o, lse = ea.forward(qs, ks, vs, scale=scale, causal=causal)
+    dq, dk, dv = ea.backward(qs, ks, vs, o, lse, dos, scale=scale, causal=causal)
+    assert dq.stride() == qs.stride() and not dq.is_contiguous()
+    qc, kc, vc, doc = (t.cuda() for t in (q, k, v, do))
+    oc, lc = ea.forward(qc, kc, vc, scale=scale, causal=causal)
+    gc = ea.backward(qc, kc, vc, oc, lc, doc, scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    ref = _grads_ref(q, k, v, do, scale, causal)
+    for name, gg, gr, gcc in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref, gc):
+        check_grad(f64(gg), gr, name)
+        assert torch.equal(gg.contiguous(), gcc), f"{name}: strided result differs from the contiguous call"
+
+
+def test_backward_packed_qkv_and_packed_gradient():
+    """q, k, v views of one [B, N, 3, H, d] buffer; dq, dk, dv written into one packed gradient buffer."""
+    ea = require_gpu()
+    from parity import check_grad
+    B, H, N, d = 2, 4, 200, 128
+    q, k, v = _inputs(B, H, N, d, "bf16", 45001)
+    g = torch.Generator(device="cpu")
+    g.manual_seed(45002)
+    do = torch.randn((B, H, N, d), generator=g).to(q.dtype)
+    scale = ea.default_scale(d)
+    qkv = torch.stack([t.transpose(1, 2) for t in (q, k, v)], dim=2).contiguous().cuda()
+    qp, kp, vp = (qkv[:, :, i].transpose(1, 2) for i in range(3))
+    dqkv = torch.full_like(qkv, float("nan"))
+    dqp, dkp, dvp = (dqkv[:, :, i].transpose(1, 2) for i in range(3))
+    o, lse = ea.forward(qp, kp, vp, scale=scale, causal=True)
+    dos = do.transpose(1, 2).contiguous().cuda().transpose(1, 2)
+    ws = torch.empty(ea.attn_bwd_strided_workspace_bytes(B, H, N, d), dtype=torch.uint8, device="cuda")
+    log(f"strided bwd packed QKV and packed dQKV, strides {qp.stride()}")
+    ea.attn_bwd(qp, kp, vp, o, dos, lse, dqp, dkp, dvp, scale, True, ws)
+    torch.cuda.synchronize()
+    assert not torch.isnan(dqkv).any(), "a gradient element was not written"
+    ref = _grads_ref(q, k, v, do, scale, True)
+    for name, gg, gr in zip(("dQ", "dK", "dV"), (dqp, dkp, dvp), ref):
+        check_grad(f64(gg), gr, name)
