@@ -35,6 +35,14 @@ Readings where the pages are silent: the causal mask is top-left aligned
 with the diagonal kept; lse is in natural log; dropout is 0; the backward pass
 differentiates O only (lse receives no gradient).
 
+Optional linear position bias (ALiBi) [page "FlashAttention技术解析 如何让GPT
+训练速度提升5-9倍", §4.1 names ALiBi with long contexts; the pages give no
+formula]: reading, the published form, a per-head slope ``m_h`` and
+``S_ij += -m_h * |(i + Nk - Nq) - j|`` added to the scaled scores before the
+softmax; for causal rows this is ``-m_h * (i' - j)`` with ``i'`` the query's
+position, non-causal rows take the distance both ways.  The bias is a
+constant of the inputs, so the backward formulas are unchanged given P.
+
 Query and key counts may differ (``Nq`` rows of Q against ``Nk`` rows of K and
 V), the shape of decoding against a KV cache [page "FlashAttention技术解析
 如何让GPT训练速度提升5-9倍", §4.1: the keys and values of earlier positions
@@ -68,7 +76,8 @@ def _f64(x) -> np.ndarray:
     return np.asarray(x, dtype=np.float64)
 
 
-def masked_scores(q, k, scale: float, causal: bool, rows: Optional[np.ndarray] = None) -> np.ndarray:
+def masked_scores(q, k, scale: float, causal: bool, rows: Optional[np.ndarray] = None,
+                  alibi_slope: Optional[float] = None) -> np.ndarray:
     """S = scale * Q K^T for the given query rows (all rows by default).
 
     Causal reading: query i sees keys j <= i + (Nk - Nq), i.e. j <= i
@@ -82,9 +91,12 @@ def masked_scores(q, k, scale: float, causal: bool, rows: Optional[np.ndarray] =
         rows = np.arange(n)
     rows = np.asarray(rows, dtype=np.int64)
     s = float(scale) * (q[rows] @ k.T)
+    cols = np.arange(k.shape[0])
+    pos = rows[:, None] + (k.shape[0] - n)       # the queries' positions in the key sequence
+    if alibi_slope is not None:
+        s = s - float(alibi_slope) * np.abs(pos - cols[None, :])
     if causal:
-        cols = np.arange(k.shape[0])
-        s[cols[None, :] > rows[:, None] + (k.shape[0] - n)] = -np.inf
+        s[cols[None, :] > pos] = -np.inf
     return s
 
 
@@ -96,16 +108,16 @@ def row_softmax(s: np.ndarray) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
     return e / l[:, None], m, l
 
 
-def forward_head_rows(q, k, v, scale: float, causal: bool, rows) -> Tuple[np.ndarray, np.ndarray]:
+def forward_head_rows(q, k, v, scale: float, causal: bool, rows, alibi_slope=None) -> Tuple[np.ndarray, np.ndarray]:
     """O and lse of the listed query rows of one head (each row is independent)."""
-    s = masked_scores(q, k, scale, causal, rows)
+    s = masked_scores(q, k, scale, causal, rows, alibi_slope)
     p, m, l = row_softmax(s)
     o = p @ _f64(v)
     lse = m + np.log(l)
     return o, lse
 
 
-def forward_head(q, k, v, scale: float, causal: bool, row_block: Optional[int] = None):
+def forward_head(q, k, v, scale: float, causal: bool, row_block: Optional[int] = None, alibi_slope=None):
     """O [N,d] and lse [N] of one head.
 
     ``row_block`` only bounds memory for long sequences: the definition is
@@ -113,16 +125,16 @@ def forward_head(q, k, v, scale: float, causal: bool, row_block: Optional[int] =
     """
     n = np.shape(q)[0]
     if row_block is None or row_block >= n:
-        return forward_head_rows(q, k, v, scale, causal, np.arange(n))
+        return forward_head_rows(q, k, v, scale, causal, np.arange(n), alibi_slope)
     o = np.empty((n, np.shape(v)[1]))
     lse = np.empty(n)
     for r0 in range(0, n, row_block):
         rows = np.arange(r0, min(n, r0 + row_block))
-        o[rows], lse[rows] = forward_head_rows(q, k, v, scale, causal, rows)
+        o[rows], lse[rows] = forward_head_rows(q, k, v, scale, causal, rows, alibi_slope)
     return o, lse
 
 
-def backward_head(q, k, v, do, scale: float, causal: bool, row_block: Optional[int] = None):
+def backward_head(q, k, v, do, scale: float, causal: bool, row_block: Optional[int] = None, alibi_slope=None):
     """dQ, dK, dV [N,d] of one head for upstream gradient dO (exact chain rule).
 
     ``row_block`` evaluates the same sums ``dV = sum_i P_i^T dO_i`` and
@@ -140,7 +152,7 @@ def backward_head(q, k, v, do, scale: float, causal: bool, row_block: Optional[i
     dv = np.zeros_like(v)
     for r0 in range(0, n, rb):
         rows = np.arange(r0, min(n, r0 + rb))
-        s = masked_scores(q, k, scale, causal, rows)
+        s = masked_scores(q, k, scale, causal, rows, alibi_slope)
         p, _, _ = row_softmax(s)
         dv += p.T @ do[rows]
         dp = do[rows] @ v.T
@@ -158,26 +170,28 @@ def _heads(x) -> Iterable[Tuple[int, int]]:
             yield bi, hi
 
 
-def forward(q, k, v, scale: float, causal: bool, row_block: Optional[int] = None):
-    """O [B,H,Nq,d] and lse [B,H,Nq] over all heads (K, V: [B,H,Nk,d])."""
+def forward(q, k, v, scale: float, causal: bool, row_block: Optional[int] = None, alibi_slopes=None):
+    """O [B,H,Nq,d] and lse [B,H,Nq] over all heads (K, V: [B,H,Nk,d]); alibi_slopes: [H] or None."""
     q = _f64(q)
     b, h, n, d = q.shape
     o = np.empty((b, h, n, np.shape(v)[3]))
     lse = np.empty((b, h, n))
     for bi, hi in _heads(q):
-        o[bi, hi], lse[bi, hi] = forward_head(q[bi, hi], k[bi, hi], v[bi, hi], scale, causal, row_block)
+        sl = None if alibi_slopes is None else float(alibi_slopes[hi])
+        o[bi, hi], lse[bi, hi] = forward_head(q[bi, hi], k[bi, hi], v[bi, hi], scale, causal, row_block, sl)
     return o, lse
 
 
-def backward(q, k, v, do, scale: float, causal: bool, row_block: Optional[int] = None):
-    """dQ, dK, dV [B,H,N,d] over all heads."""
+def backward(q, k, v, do, scale: float, causal: bool, row_block: Optional[int] = None, alibi_slopes=None):
+    """dQ, dK, dV [B,H,N,d] over all heads; alibi_slopes: [H] or None."""
     q = _f64(q)
     dq = np.empty_like(q)
     dk = np.empty_like(q)
     dv = np.empty((q.shape[0], q.shape[1], q.shape[2], np.shape(v)[3]))
     for bi, hi in _heads(q):
+        sl = None if alibi_slopes is None else float(alibi_slopes[hi])
         dq[bi, hi], dk[bi, hi], dv[bi, hi] = backward_head(
-            q[bi, hi], k[bi, hi], v[bi, hi], do[bi, hi], scale, causal, row_block)
+            q[bi, hi], k[bi, hi], v[bi, hi], do[bi, hi], scale, causal, row_block, sl)
     return dq, dk, dv
 
 

@@ -417,3 +417,123 @@ def test_planted_kv_mask_mistake_is_caught(kind):
         except (AssertionError, FloatingPointError, ValueError, IndexError):
             caught.append(pin.__name__)
     assert caught, f"planted KV-cache mask mistake {kind!r} passed every pin"
+
+
+# ---------------------------------------------------------------- ALiBi (linear position bias)
+# Reading (the pages name ALiBi without a formula): a per-head slope m and
+# S_ij += -m |pos_i - j| before the softmax, pos_i = i + Nk - Nq the query's
+# position.  Pins: closed forms of the geometric weights it gives to equal
+# scores, the KV-cache suffix property with the bias, finite differences.
+
+def pin_alibi_causal_geometric(fwd, bwd=None):
+    """Q = 0, causal: row i weights key j by r^(i-j), r = e^-m: lse_i = ln((1 - r^(i+1)) / (1 - r))."""
+    rng = np.random.default_rng(31)
+    n, d, m = 9, 3, 0.37
+    _, k, v = _rand(rng, n, d)
+    o, lse = fwd(np.zeros((n, d)), k, v, 0.8, True, m)
+    r = math.exp(-m)
+    for i in range(n):
+        w = np.array([r ** (i - j) for j in range(i + 1)])
+        np.testing.assert_allclose(o[i], (w[:, None] * v[: i + 1]).sum(0) / w.sum(), rtol=0, atol=1e-13)
+        np.testing.assert_allclose(lse[i], math.log((1 - r ** (i + 1)) / (1 - r)), rtol=0, atol=1e-13)
+
+
+def pin_alibi_noncausal_symmetric(fwd, bwd=None):
+    """Q = 0, non-causal: weights r^|i-j| both ways: lse_i = ln(sum_{t<=i} r^t + sum_{1<=t<n-i} r^t)."""
+    rng = np.random.default_rng(32)
+    n, d, m = 7, 2, 0.9
+    _, k, v = _rand(rng, n, d)
+    o, lse = fwd(np.zeros((n, d)), k, v, 0.5, False, m)
+    r = math.exp(-m)
+    for i in range(n):
+        w = np.array([r ** abs(i - j) for j in range(n)])
+        np.testing.assert_allclose(o[i], (w[:, None] * v).sum(0) / w.sum(), rtol=0, atol=1e-13)
+        geo = (1 - r ** (i + 1)) / (1 - r) + r * (1 - r ** (n - 1 - i)) / (1 - r)
+        np.testing.assert_allclose(lse[i], math.log(geo), rtol=0, atol=1e-13)
+
+
+def pin_alibi_kv_suffix(fwd, bwd=None):
+    """The bias follows positions: the last Nq rows of the square causal result equal an Nq-query call."""
+    rng = np.random.default_rng(33)
+    nk, d, m = 11, 4, 0.25
+    q, k, v = _rand(rng, nk, d)
+    o_full, lse_full = fwd(q, k, v, 0.7, True, m)
+    for nq in (1, 4):
+        o, lse = fwd(q[nk - nq:], k, v, 0.7, True, m)
+        np.testing.assert_allclose(o, o_full[nk - nq:], rtol=0, atol=1e-13)
+        np.testing.assert_allclose(lse, lse_full[nk - nq:], rtol=0, atol=1e-13)
+
+
+def pin_alibi_zero_slope(fwd, bwd=None):
+    rng = np.random.default_rng(34)
+    q, k, v = _rand(rng, 6, 3)
+    for causal in (False, True):
+        a, la = fwd(q, k, v, 0.6, causal, 0.0)
+        b, lb = oracle.forward_head(q, k, v, 0.6, causal)
+        np.testing.assert_allclose(a, b, rtol=0, atol=1e-14)
+        np.testing.assert_allclose(la, lb, rtol=0, atol=1e-14)
+
+
+ALIBI_PINS = [pin_alibi_causal_geometric, pin_alibi_noncausal_symmetric, pin_alibi_kv_suffix, pin_alibi_zero_slope]
+
+
+def _alibi_fwd(q, k, v, scale, causal, m):
+    return oracle.forward_head(q, k, v, scale, causal, alibi_slope=m)
+
+
+@pytest.mark.parametrize("pin", ALIBI_PINS, ids=[p.__name__ for p in ALIBI_PINS])
+def test_oracle_alibi_pin(pin):
+    pin(_alibi_fwd)
+
+
+def test_alibi_finite_differences():
+    """The bias is a constant of the inputs: the backward formulas hold unchanged (central differences)."""
+    rng = np.random.default_rng(35)
+    h = 1e-6
+    for causal in (False, True):
+        for nq, nk in ((3, 3), (2, 5)):
+            if causal and nk < nq:
+                continue
+            q = rng.standard_normal((nq, 3))
+            k = rng.standard_normal((nk, 3))
+            v = rng.standard_normal((nk, 2))
+            do = rng.standard_normal((nq, 2))
+            grads = oracle.backward_head(q, k, v, do, 0.8, causal, alibi_slope=0.45)
+            for which, g in enumerate(grads):
+                base = [q, k, v]
+                fd = np.zeros_like(g)
+                for idx in np.ndindex(*g.shape):
+                    plus = [x.copy() for x in base]
+                    minus = [x.copy() for x in base]
+                    plus[which][idx] += h
+                    minus[which][idx] -= h
+                    lp = float((oracle.forward_head(*plus, 0.8, causal, alibi_slope=0.45)[0] * do).sum())
+                    lm = float((oracle.forward_head(*minus, 0.8, causal, alibi_slope=0.45)[0] * do).sum())
+                    fd[idx] = (lp - lm) / (2 * h)
+                assert np.linalg.norm(fd - g) <= 1e-6 * max(np.linalg.norm(fd), 1e-12), (causal, nq, nk, which)
+
+
+def _mut_alibi_fwd(kind):
+    def fwd(q, k, v, scale, causal, m):
+        nq, nk = q.shape[0], k.shape[0]
+        s = float(scale) * (q @ k.T)
+        j, i = np.meshgrid(np.arange(nk), np.arange(nq))
+        pos = i + (0 if kind == "no_shift" else nk - nq)
+        dist = {"sign": -np.abs(pos - j), "no_abs": pos - j}.get(kind, np.abs(pos - j))
+        s = s - m * dist
+        if causal:
+            s[j > i + nk - nq] = -np.inf
+        p, mx, l = A.row_softmax(s)
+        return p @ v, mx + np.log(l)
+    return fwd
+
+
+@pytest.mark.parametrize("kind", ["sign", "no_abs", "no_shift"])
+def test_planted_alibi_mistake_is_caught(kind):
+    caught = []
+    for pin in ALIBI_PINS:
+        try:
+            pin(_mut_alibi_fwd(kind))
+        except (AssertionError, FloatingPointError, ValueError, IndexError):
+            caught.append(pin.__name__)
+    assert caught, f"planted ALiBi mistake {kind!r} passed every pin"
