@@ -28,5 +28,8 @@ from ._binding import (  # noqa: F401
     default_scale,
     forward,
     forward_kvcache,
+    forward_alibi,
+    backward_alibi,
+    forward_kvcache_alibi,
     load,
 )

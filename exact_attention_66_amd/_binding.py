@@ -27,7 +27,8 @@ STATUS_NAMES = {
 }
 EXPORTED = ["attn_fwd", "attn_fwd_strided", "attn_bwd_workspace_bytes", "attn_bwd", "attn_fwd_kvcache",
             "attn_fwd_kvcache_strided", "attn_fwd_kvcache_workspace_bytes", "attn_fwd_kvcache_splits",
-            "attn_bwd_strided", "attn_bwd_strided_workspace_bytes",
+            "attn_bwd_strided", "attn_bwd_strided_workspace_bytes", "attn_fwd_alibi", "attn_bwd_alibi",
+            "attn_fwd_kvcache_alibi",
             "attn_profile_start",
             "attn_profile_stop", "attn_status_string", "attn_last_hip_error"]
 # attn_kernel_kind values
@@ -73,6 +74,14 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_bwd_strided.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64p, f32, i32, i32, vp,
                                      sz, vp]
     lib.attn_bwd_strided.restype = i32
+    lib.attn_fwd_alibi.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, f32, i32, i32, vp]
+    lib.attn_fwd_alibi.restype = i32
+    lib.attn_bwd_alibi.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, f32, i32, i32, vp,
+                                   sz, vp]
+    lib.attn_bwd_alibi.restype = i32
+    lib.attn_fwd_kvcache_alibi.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, vp, f32, i32, i32, i32, vp,
+                                           sz, vp]
+    lib.attn_fwd_kvcache_alibi.restype = i32
     lib.attn_bwd_strided_workspace_bytes.argtypes = [i64, i64, i64, i64]
     lib.attn_bwd_strided_workspace_bytes.restype = sz
     lib.attn_fwd_kvcache_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i32]
@@ -290,4 +299,61 @@ def forward_kvcache(q, k, v, scale: Optional[float] = None, causal: bool = False
     o = torch.empty_like(q)
     lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
     attn_fwd_kvcache(q, k, v, o, lse, scale, causal, workspace, num_splits, stream)
+    return o, lse
+
+
+def _slopes(alibi_slopes, H: int, device):
+    """The [H] fp32 slopes as a contiguous device tensor."""
+    t = torch.as_tensor(alibi_slopes, dtype=torch.float32, device=device).contiguous()
+    if tuple(t.shape) != (H,):
+        raise ValueError(f"alibi_slopes must have shape [H] = [{H}]")
+    return t
+
+
+def forward_alibi(q, k, v, alibi_slopes, scale: Optional[float] = None, causal: bool = False, stream=None):
+    """attn_fwd_alibi on contiguous [B, H, N, d] tensors: (o, lse)."""
+    B, H, N, d = _shape4(q)
+    scale = default_scale(d) if scale is None else scale
+    sl = _slopes(alibi_slopes, H, q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    st = load().attn_fwd_alibi(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, _ptr(sl), float(scale),
+                               int(bool(causal)), _dtype_code(q), _stream(stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fwd_alibi")
+    return o, lse
+
+
+def backward_alibi(q, k, v, o, lse, dO, alibi_slopes, scale: Optional[float] = None, causal: bool = False,
+                   stream=None):
+    """attn_bwd_alibi on contiguous tensors: (dq, dk, dv)."""
+    B, H, N, d = _shape4(q)
+    scale = default_scale(d) if scale is None else scale
+    sl = _slopes(alibi_slopes, H, q.device)
+    ws = torch.empty(attn_bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    st = load().attn_bwd_alibi(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                               B, H, N, d, _ptr(sl), float(scale), int(bool(causal)), _dtype_code(q), _ptr(ws),
+                               ws.numel(), _stream(stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_bwd_alibi")
+    return dq, dk, dv
+
+
+def forward_kvcache_alibi(q, k, v, alibi_slopes, scale: Optional[float] = None, causal: bool = False,
+                          num_splits: int = 0, stream=None):
+    """attn_fwd_kvcache_alibi on contiguous tensors: (o, lse)."""
+    B, H, Nq, d = _shape4(q)
+    Nk = int(k.shape[2])
+    scale = default_scale(d) if scale is None else scale
+    sl = _slopes(alibi_slopes, H, q.device)
+    ws = torch.empty(attn_fwd_kvcache_workspace_bytes(B, H, Nq, Nk, d, num_splits), dtype=torch.uint8,
+                     device=q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    st = load().attn_fwd_kvcache_alibi(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk, d, _ptr(sl),
+                                       float(scale), int(bool(causal)), _dtype_code(q), int(num_splits), _ptr(ws),
+                                       ws.numel(), _stream(stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fwd_kvcache_alibi")
     return o, lse

@@ -102,7 +102,8 @@ int launch_status(hipError_t e) {
 
 // Forward with per-tensor layouts (lays: q, k, v, o); lse is contiguous.
 int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H, int64_t N,
-             int64_t d, const attn::Lay* lays, float scale, int causal, int dtype, void* stream) {
+             int64_t d, const attn::Lay* lays, float scale, int causal, int dtype, void* stream,
+             const float* slopes = nullptr) {
   if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL_PTR;
   int st = check_common(B, H, N, d, scale, dtype);
   if (st != ATTN_OK) return st;
@@ -118,9 +119,11 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
     if (overlaps(o, ob, ins[i], ib) || overlaps(lse, lb, ins[i], ib)) return ATTN_ERR_ALIASING;
   }
   if (overlaps(o, ob, lse, lb)) return ATTN_ERR_ALIASING;
+  if (slopes && (overlaps(o, ob, slopes, (size_t)H * 4) || overlaps(lse, lb, slopes, (size_t)H * 4)))
+    return ATTN_ERR_ALIASING;
 
   attn::FwdArgs a{q, k, v, o, lse, B, H, N, d, scale, causal != 0, dtype, (hipStream_t)stream,
-                  lays[0], lays[1], lays[2], lays[3]};
+                  lays[0], lays[1], lays[2], lays[3], slopes};
   return launch_status(attn::launch_fwd(a));
 }
 
@@ -144,7 +147,7 @@ int check_kvcache(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, float
 // KV-cache forward with per-tensor layouts (lays: q, k, v, o); lse contiguous.
 int kv_impl(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H, int64_t Nq,
             int64_t Nk, int64_t d, const attn::Lay* lays, float scale, int causal, int dtype, int num_splits,
-            void* workspace, size_t workspace_bytes, void* stream) {
+            void* workspace, size_t workspace_bytes, void* stream, const float* slopes = nullptr) {
   if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL_PTR;
   int st = check_kvcache(B, H, Nq, Nk, d, scale, causal, dtype, num_splits);
   if (st != ATTN_OK) return st;
@@ -161,7 +164,7 @@ int kv_impl(const void* q, const void* k, const void* v, void* o, float* lse, in
   const size_t lb = (size_t)(B * H * Nq) * 4;
   struct R { const void* p; size_t n; };
   const R ins[] = {{q, lay_extent(lays[0], B, H, Nq, d)}, {k, lay_extent(lays[1], B, H, Nk, d)},
-                   {v, lay_extent(lays[2], B, H, Nk, d)}};
+                   {v, lay_extent(lays[2], B, H, Nk, d)}, {slopes, slopes ? (size_t)H * 4 : 0}};
   const R outs[] = {{o, lay_extent(lays[3], B, H, Nq, d)}, {lse, lb}, {workspace, need}};
   for (const R& x : outs) {
     for (const R& y : ins)
@@ -172,7 +175,7 @@ int kv_impl(const void* q, const void* k, const void* v, void* o, float* lse, in
   char* ws = (char*)workspace;
   attn::KvArgs a{q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal != 0, dtype, P, chunk,
                  (float*)ws, (float*)(ws + attn::kv_acc_bytes(B * H, Nq, P, d)), (hipStream_t)stream,
-                 lays[0], lays[1], lays[2], lays[3]};
+                 lays[0], lays[1], lays[2], lays[3], slopes};
   return launch_status(attn::launch_kvcache(a));
 }
 
@@ -190,7 +193,7 @@ size_t bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d) {
 int bwd_impl(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
              void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N, int64_t d, const attn::Lay* lays,
              bool strided, float scale, int causal, int dtype, void* workspace, size_t workspace_bytes,
-             void* stream) {
+             void* stream, const float* slopes = nullptr) {
   if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv) return ATTN_ERR_NULL_PTR;
   int st = check_common(B, H, N, d, scale, dtype);
   if (st != ATTN_OK) return st;
@@ -210,7 +213,7 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const v
   struct R { const void* p; size_t n; };
   const R ins[] = {{q, lay_extent(lays[0], B, H, N, d)},  {k, lay_extent(lays[1], B, H, N, d)},
                    {v, lay_extent(lays[2], B, H, N, d)},  {o, lay_extent(lays[3], B, H, N, d)},
-                   {dO, lay_extent(lays[4], B, H, N, d)}, {lse, lb}};
+                   {dO, lay_extent(lays[4], B, H, N, d)}, {lse, lb}, {slopes, slopes ? (size_t)H * 4 : 0}};
   const R outs[] = {{dq, lay_extent(lays[5], B, H, N, d)}, {dk, lay_extent(lays[6], B, H, N, d)},
                     {dv, lay_extent(lays[7], B, H, N, d)}, {workspace, need}};
   for (int i = 0; i < 4; ++i) {
@@ -230,7 +233,7 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const v
                   (float*)ws, (float*)(ws + sb), ws + t0, ws + t0 + tcb, ws + t0 + 2 * tcb,
                   tail, tail ? tail + tlb : nullptr, tail ? tail + 2 * tlb : nullptr, tail ? tail + 3 * tlb : nullptr,
                   (hipStream_t)stream, strided, lays[0], lays[1], lays[2], lays[3], lays[4], lays[5], lays[6],
-                  lays[7], nullptr, nullptr, nullptr, nullptr};
+                  lays[7], nullptr, nullptr, nullptr, nullptr, slopes};
   if (strided) {
     char* cp = ws + base_need;
     a.qc = cp;
@@ -239,6 +242,13 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const v
     a.doc = cp + 3 * cb;
   }
   return launch_status(attn::launch_bwd(a));
+}
+
+// ALiBi slopes: a device array of H fp32, 4-byte aligned.
+int check_slopes(const float* slopes) {
+  if (!slopes) return ATTN_ERR_NULL_PTR;
+  if (reinterpret_cast<uintptr_t>(slopes) & 3u) return ATTN_ERR_MISALIGNED;
+  return ATTN_OK;
 }
 
 attn::Lay lay_from(const int64_t* s) { return attn::Lay{s[0], s[1], (int32_t)std::min<int64_t>(s[2], INT32_MAX), 0}; }
@@ -293,6 +303,40 @@ int attn_bwd_strided(const void* q, const void* k, const void* v, const void* o,
   for (int i = 0; i < 8; ++i) lays[i] = lay_from(strides + 3 * i);
   return bwd_impl(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, lays, true, scale, causal, dtype, workspace,
                   workspace_bytes, stream);
+}
+
+int attn_fwd_alibi(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                   int64_t N, int64_t d, const float* alibi_slopes, float scale, int causal, int dtype, void* stream) {
+  if (checked_elems(B, H, N, d) < 0) return ATTN_ERR_BAD_SHAPE;
+  const int st = check_slopes(alibi_slopes);
+  if (st != ATTN_OK) return st;
+  const attn::Lay c = attn::contiguous_lay(H, N, d);
+  const attn::Lay lays[4] = {c, c, c, c};
+  return fwd_impl(q, k, v, o, lse, B, H, N, d, lays, scale, causal, dtype, stream, alibi_slopes);
+}
+
+int attn_bwd_alibi(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
+                   void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N, int64_t d, const float* alibi_slopes,
+                   float scale, int causal, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (checked_elems(B, H, N, d) < 0) return ATTN_ERR_BAD_SHAPE;
+  const int st = check_slopes(alibi_slopes);
+  if (st != ATTN_OK) return st;
+  const attn::Lay c = attn::contiguous_lay(H, N, d);
+  const attn::Lay lays[8] = {c, c, c, c, c, c, c, c};
+  return bwd_impl(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, lays, false, scale, causal, dtype, workspace,
+                  workspace_bytes, stream, alibi_slopes);
+}
+
+int attn_fwd_kvcache_alibi(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                           int64_t Nq, int64_t Nk, int64_t d, const float* alibi_slopes, float scale, int causal,
+                           int dtype, int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  if (checked_elems(B, H, Nq, d) < 0 || checked_elems(B, H, Nk, d) < 0) return ATTN_ERR_BAD_SHAPE;
+  const int st = check_slopes(alibi_slopes);
+  if (st != ATTN_OK) return st;
+  const attn::Lay cq = attn::contiguous_lay(H, Nq, d), ck = attn::contiguous_lay(H, Nk, d);
+  const attn::Lay lays[4] = {cq, ck, ck, cq};
+  return kv_impl(q, k, v, o, lse, B, H, Nq, Nk, d, lays, scale, causal, dtype, num_splits, workspace,
+                 workspace_bytes, stream, alibi_slopes);
 }
 
 size_t attn_fwd_kvcache_workspace_bytes(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int num_splits) {

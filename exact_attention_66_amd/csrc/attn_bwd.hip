@@ -227,7 +227,7 @@ __global__ __launch_bounds__(256) void bwd_prep(const typename E::T* __restrict_
 // tile after it starts into the buffer just released.  Tiles that reach the
 // causal diagonal come first and run the same pipeline with the mask applied
 // (sub-tiles entirely above the diagonal come out as P = 0).
-template <typename E, int D, bool CAUSAL, int NW, int BMQ, bool TAIL, bool STRIDED>
+template <typename E, int D, bool CAUSAL, int NW, int BMQ, bool TAIL, bool STRIDED, bool ALIBI>
 __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv(
     const typename E::T* __restrict__ Q, const typename E::T* __restrict__ K,
     const typename E::T* __restrict__ V, const typename E::T* __restrict__ dO,
@@ -235,7 +235,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv(
     const typename E::T* __restrict__ QTail, const typename E::T* __restrict__ dOTail,
     const float* __restrict__ NLSE, const float* __restrict__ Dvec, typename E::T* __restrict__ dK,
     typename E::T* __restrict__ dV, int BH, int N, int Np_arg, int nkb, float scale, float scale_log2, Lay ldk,
-    Lay ldv, int H) {
+    Lay ldv, int H, const float* __restrict__ slopes) {
   using T = typename E::T;
   using v8 = typename E::v8;
   const int Np = TAIL ? Np_arg : N;     // padded length: N itself unless TAIL
@@ -278,6 +278,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv(
   int kb0, kw0, it0, ntile, nmask;
   size_t head;
   int64_t out_k = 0, out_v = 0;         // STRIDED: dK, dV offsets of (batch, head, key kw0)
+  float nslope2 = 0.f;                  // ALIBI: -slope * log2(e) of this unit's head
   const T *Qh, *dOh, *QTh, *dOTh, *Qtl, *dOtl;
   const float *lse_h, *dd_h;
   auto set_unit = [&](const int u) {
@@ -285,6 +286,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv(
     kb0 = (u % nkb) * BN;
     kw0 = kb0 + wu * 32;                 // first key of this wave
     head = (size_t)bh * (size_t)N * D;
+    if constexpr (ALIBI) nslope2 = -slopes[bh % H] * kLog2e;
     if constexpr (STRIDED) {
       const int bi = bh / H, hi = bh - bi * H;
       out_k = bi * ldk.sb + hi * ldk.sh + (int64_t)kw0 * ldk.sn;
@@ -455,8 +457,15 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv(
       dpacc = E::mfma32(da[ks], vB[ks], dpacc);
     }
     float p[16];
+    if constexpr (ALIBI) {   // query qs0 + 4h + c (c = 8(j/4) + j%4) at distance dqk + c from key kw0 + r
+      const float dqk = (float)(qs0 + 4 * h - kw0 - r);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) p[j] = fast_exp2(sacc[j] * scale_log2);
+      for (int j = 0; j < 16; ++j)
+        p[j] = fast_exp2(fmaf(sacc[j], scale_log2, nslope2 * fabsf(dqk + (float)(8 * (j / 4) + j % 4))));
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) p[j] = fast_exp2(sacc[j] * scale_log2);
+    }
     if constexpr (decltype(maskc)::value) {  // key > query -> P = 0
 #pragma unroll
       for (int j = 0; j < 16; ++j)
@@ -618,14 +627,14 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv(
 // buffers, two tiles ahead of their use; a copy instruction fills 64
 // consecutive 16-byte slots, so the padding slot of each row gets a
 // duplicate of the row's last chunk and a tile is a whole number of blocks.
-template <typename E, int D, bool CAUSAL, int NW, int BN, bool TAIL, bool STRIDED>
+template <typename E, int D, bool CAUSAL, int NW, int BN, bool TAIL, bool STRIDED, bool ALIBI>
 __global__ __launch_bounds__(NW * 64, ATTN_DQ_MINW) void bwd_dq(
     const typename E::T* __restrict__ Q, const typename E::T* __restrict__ K,
     const typename E::T* __restrict__ V, const typename E::T* __restrict__ dO,
     const typename E::T* __restrict__ KT, const typename E::T* __restrict__ KTail,
     const typename E::T* __restrict__ VTail, const float* __restrict__ NLSE, const float* __restrict__ ND,
     typename E::T* __restrict__ dQ, int BH, int N, int Np_arg, int nqb, float scale, float scale_log2, Lay ldq,
-    int H) {
+    int H, const float* __restrict__ slopes) {
   using T = typename E::T;
   const int Np = TAIL ? Np_arg : N;     // padded length: N itself unless TAIL
   using v8 = typename E::v8;
@@ -666,6 +675,7 @@ __global__ __launch_bounds__(NW * 64, ATTN_DQ_MINW) void bwd_dq(
   if (unit < 0) return;
   const int nfull = N / BN;   // key tiles wholly inside the sequence
   int bh, q0, qw0, kv_end, ntiles, q_last;
+  float nslope2 = 0.f;   // ALIBI: -slope * log2(e) of this unit's head
   bool wave_valid;
   size_t head;
   const T *Kh, *Vh, *KTh, *Ktl, *Vtl;
@@ -675,6 +685,7 @@ __global__ __launch_bounds__(NW * 64, ATTN_DQ_MINW) void bwd_dq(
     q0 = qblk * BM;
     qw0 = q0 + wu * 32;
     wave_valid = qw0 < N;
+    if constexpr (ALIBI) nslope2 = -slopes[bh % H] * kLog2e;
     head = (size_t)bh * (size_t)N * D;
     Kh = K + head;
     Vh = V + head;
@@ -793,8 +804,15 @@ __global__ __launch_bounds__(NW * 64, ATTN_DQ_MINW) void bwd_dq(
       for (int db = 0; db < DB; ++db) kta[kk][db] = *(const v8*)(ktl + db * 32 * LT + 16 * kk);
 #endif
     float ds[16];
+    if constexpr (ALIBI) {   // key kbk0 + 4h + c (c = 8(j/4) + j%4) at distance dq - c from query qw0 + r
+      const float dq = (float)(qw0 + r - kbk0 - 4 * h);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) ds[j] = fast_exp2(sacc[j] * scale_log2);
+      for (int j = 0; j < 16; ++j)
+        ds[j] = fast_exp2(fmaf(sacc[j], scale_log2, nslope2 * fabsf(dq - (float)(8 * (j / 4) + j % 4))));
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) ds[j] = fast_exp2(sacc[j] * scale_log2);
+    }
     if (TAIL && !CAUSAL && kbk0 + 32 > N) {   // keys past the end of the sequence -> P = 0
 #pragma unroll
       for (int j = 0; j < 16; ++j)
@@ -923,7 +941,7 @@ __global__ __launch_bounds__(NW * 64, ATTN_DQ_MINW) void bwd_dq(
   }
 }
 
-template <typename E, int D, bool CAUSAL, bool TAIL, bool STRIDED>
+template <typename E, int D, bool CAUSAL, bool TAIL, bool STRIDED, bool ALIBI>
 hipError_t launch_bwd_cfg(const BwdArgs& a) {
   constexpr int NWK = 4;            // dK/dV: waves per workgroup (32 keys each)
   constexpr int NWQ = ATTN_DQ_NW;
@@ -949,6 +967,7 @@ hipError_t launch_bwd_cfg(const BwdArgs& a) {
   const T* dO2 = STRIDED ? doc : dO;
   Lay lq = a.lq, lk = a.lk, lv = a.lv, lo = a.lo, ldo = a.ldo, ldq = a.ldq, ldk = a.ldk, ldv = a.ldv;
   int H = (int)a.H;
+  const float* slopes = a.alibi_slopes;
   const float* lse = a.lse;
   T* dq = (T*)a.dq;
   T* dk = (T*)a.dk;
@@ -981,8 +1000,8 @@ hipError_t launch_bwd_cfg(const BwdArgs& a) {
     void* args[] = {(void*)&q2,    (void*)&k2, (void*)&v2, (void*)&dO2, (void*)&qt,  (void*)&dot,
                     (void*)&qtail, (void*)&dotail, (void*)&nlse, (void*)&delta, (void*)&dk, (void*)&dv,
                     (void*)&BH, (void*)&N, (void*)&Np, (void*)&nkb, (void*)&scale, (void*)&scale_log2,
-                    (void*)&ldk, (void*)&ldv, (void*)&H};
-    const void* fn = (const void*)bwd_dkdv<E, D, CAUSAL, NWK, 64, TAIL, STRIDED>;
+                    (void*)&ldk, (void*)&ldv, (void*)&H, (void*)&slopes};
+    const void* fn = (const void*)bwd_dkdv<E, D, CAUSAL, NWK, 64, TAIL, STRIDED, ALIBI>;
     hipError_t e = launch_kernel(fn, dim3((unsigned)persistent_grid(fn, NWK * 64, nkb * BH)), dim3(NWK * 64), args,
                                  a.stream, 2);
     if (e != hipSuccess) return e;
@@ -991,26 +1010,28 @@ hipError_t launch_bwd_cfg(const BwdArgs& a) {
     const int nqb = (N + NWQ * 32 - 1) / (NWQ * 32);
     void* args[] = {(void*)&q2,   (void*)&k2, (void*)&v2, (void*)&dO2, (void*)&kt, (void*)&ktail, (void*)&vtail,
                     (void*)&nlse, (void*)&delta, (void*)&dq, (void*)&BH, (void*)&N, (void*)&Np, (void*)&nqb,
-                    (void*)&scale, (void*)&scale_log2, (void*)&ldq, (void*)&H};
-    const void* fn = (const void*)bwd_dq<E, D, CAUSAL, NWQ, BNQ, TAIL, STRIDED>;
+                    (void*)&scale, (void*)&scale_log2, (void*)&ldq, (void*)&H, (void*)&slopes};
+    const void* fn = (const void*)bwd_dq<E, D, CAUSAL, NWQ, BNQ, TAIL, STRIDED, ALIBI>;
     return launch_kernel(fn, dim3((unsigned)persistent_grid(fn, NWQ * 64, nqb * BH)), dim3(NWQ * 64), args,
                          a.stream, 3);
   }
 }
 
-template <typename E, int D, bool STRIDED>
+template <typename E, int D, bool STRIDED, bool ALIBI>
 hipError_t launch_bwd_s(const BwdArgs& a) {
   if (a.N % 64 == 0) {
-    if (a.causal) return launch_bwd_cfg<E, D, true, false, STRIDED>(a);
-    return launch_bwd_cfg<E, D, false, false, STRIDED>(a);
+    if (a.causal) return launch_bwd_cfg<E, D, true, false, STRIDED, ALIBI>(a);
+    return launch_bwd_cfg<E, D, false, false, STRIDED, ALIBI>(a);
   }
-  if (a.causal) return launch_bwd_cfg<E, D, true, true, STRIDED>(a);
-  return launch_bwd_cfg<E, D, false, true, STRIDED>(a);
+  if (a.causal) return launch_bwd_cfg<E, D, true, true, STRIDED, ALIBI>(a);
+  return launch_bwd_cfg<E, D, false, true, STRIDED, ALIBI>(a);
 }
 
+// ALiBi calls are contiguous (the C ABI has no strided ALiBi entry point)
 template <typename E, int D>
 hipError_t launch_bwd_d(const BwdArgs& a) {
-  return a.strided ? launch_bwd_s<E, D, true>(a) : launch_bwd_s<E, D, false>(a);
+  if (a.alibi_slopes) return launch_bwd_s<E, D, false, true>(a);
+  return a.strided ? launch_bwd_s<E, D, true, false>(a) : launch_bwd_s<E, D, false, false>(a);
 }
 
 }  // namespace

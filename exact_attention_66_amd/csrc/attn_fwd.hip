@@ -64,14 +64,15 @@ constexpr float kRescaleSlack = 8.0f;
 // with ds_read_b64_tr_b16 by 32 lanes covering 4 rows x 64 bytes (rows 16
 // banks apart: the 4 rows land on 4 disjoint 16-bank groups).  Both are
 // affine, so every read is one per-lane base plus an immediate offset.
-template <typename E, int D, bool CAUSAL, int QB, int NW, int BN, bool TAIL>
+template <typename E, int D, bool CAUSAL, int QB, int NW, int BN, bool TAIL, bool ALIBI>
 __global__ __launch_bounds__(NW * 64, ATTN_FWD_MINW) void fwd_kernel(const typename E::T* __restrict__ Q,
                                                                      const typename E::T* __restrict__ K,
                                                                      const typename E::T* __restrict__ V,
                                                                      typename E::T* __restrict__ O,
                                                                      float* __restrict__ LSE, Lay lq, Lay lk,
                                                                      Lay lv, Lay lo, int H, int BH, int N,
-                                                                     int nqb, float scale_log2) {
+                                                                     int nqb, float scale_log2,
+                                                                     const float* __restrict__ slopes) {
   using T = typename E::T;
   using v8 = typename E::v8;
   using v4 = typename E::v4;
@@ -123,6 +124,8 @@ __global__ __launch_bounds__(NW * 64, ATTN_FWD_MINW) void fwd_kernel(const typen
   const T* Qh = Q + (bi * lq.sb + hi * lq.sh);
   const T* Kh = K + (bi * lk.sb + hi * lk.sh);
   const T* Vh = V + (bi * lv.sb + hi * lv.sh);
+  // ALiBi: score bias -slope * |query position - key position|, in log2 units
+  const float nslope2 = ALIBI ? -slopes[hi] * kLog2e : 0.f;
 
   // Q fragments, B operand of S^T = K Q^T: lane holds Q[q = qw0+32qb+r][16ks + 8h .. +7]
   // (loaded below, while the first tile copies are in flight)
@@ -283,13 +286,22 @@ __global__ __launch_bounds__(NW * 64, ATTN_FWD_MINW) void fwd_kernel(const typen
     v8 pf[2][QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      const f32x16& x = s[qb];
+      // With ALiBi the scores are first taken to the log2 domain with their
+      // bias (key kbk0 + 4h + c, c = 8(j/4) + j%4, at distance dq - c from
+      // the query), so that the row max is over biased scores.
+      f32x16 x = s[qb];
+      if constexpr (ALIBI) {
+        const float dq = (float)(qw0 + qb * 32 + r - kbk0 - 4 * h);
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          x[j] = fmaf(x[j], scale_log2, nslope2 * fabsf(dq - (float)(8 * (j / 4) + j % 4)));
+      }
       const float m0 = fmax3(x[0], x[1], x[2]), m1 = fmax3(x[3], x[4], x[5]);
       const float m2 = fmax3(x[6], x[7], x[8]), m3 = fmax3(x[9], x[10], x[11]);
       const float m4 = fmax3(x[12], x[13], x[14]);
       float mx = fmax3(fmax3(m0, m1, m2), fmax3(m3, m4, x[15]), -__builtin_inff());
       mx = xhalf_max(mx);
-      const float mt = mx * scale_log2;
+      const float mt = ALIBI ? mx : mx * scale_log2;
       const bool need = mt > m_run[qb] + kRescaleSlack;
       if (__builtin_amdgcn_ballot_w64(need) != 0) {
         const float mn = fmaxf(m_run[qb], mt);
@@ -303,7 +315,7 @@ __global__ __launch_bounds__(NW * 64, ATTN_FWD_MINW) void fwd_kernel(const typen
       const float neg_m = -m_run[qb];
       float p[16];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) p[j] = fast_exp2(fmaf(x[j], scale_log2, neg_m));
+      for (int j = 0; j < 16; ++j) p[j] = fast_exp2(ALIBI ? x[j] + neg_m : fmaf(x[j], scale_log2, neg_m));
       float q4[4];
 #pragma unroll
       for (int g = 0; g < 4; ++g) q4[g] = (p[4 * g] + p[4 * g + 1]) + (p[4 * g + 2] + p[4 * g + 3]);
@@ -405,7 +417,7 @@ __global__ __launch_bounds__(NW * 64, ATTN_FWD_MINW) void fwd_kernel(const typen
   }
 }
 
-template <typename E, int D, bool CAUSAL, int QB, int NW, int BN, bool TAIL>
+template <typename E, int D, bool CAUSAL, int QB, int NW, int BN, bool TAIL, bool ALIBI>
 hipError_t launch_fwd_cfg(const FwdArgs& a) {
   constexpr int BM = NW * 32 * QB;
   const int BH = (int)(a.B * a.H);
@@ -420,21 +432,29 @@ hipError_t launch_fwd_cfg(const FwdArgs& a) {
   float* lse = a.lse;
   Lay lq = a.lq, lk = a.lk, lv = a.lv, lo = a.lo;
   const int H = (int)a.H;
+  const float* slopes = a.alibi_slopes;
   void* args[] = {(void*)&q, (void*)&k, (void*)&v, (void*)&o, (void*)&lse, (void*)&lq, (void*)&lk, (void*)&lv,
-                  (void*)&lo, (void*)&H, (void*)&BH, (void*)&N, (void*)&nqb, (void*)&scale_log2};
-  return launch_kernel((const void*)fwd_kernel<E, D, CAUSAL, QB, NW, BN, TAIL>, grid, block, args, a.stream, 0);
+                  (void*)&lo, (void*)&H, (void*)&BH, (void*)&N, (void*)&nqb, (void*)&scale_log2,
+                  (void*)&slopes};
+  return launch_kernel((const void*)fwd_kernel<E, D, CAUSAL, QB, NW, BN, TAIL, ALIBI>, grid, block, args, a.stream,
+                       0);
+}
+
+template <typename E, int D, bool ALIBI>
+hipError_t launch_fwd_a(const FwdArgs& a) {
+  constexpr int BN = ATTN_FWD_BN ? ATTN_FWD_BN : (D == 128 ? 128 : 64);
+  constexpr int QB = ATTN_FWD_QB, NW = ATTN_FWD_NW;
+  if (a.N % 64 == 0) {
+    if (a.causal) return launch_fwd_cfg<E, D, true, QB, NW, BN, false, ALIBI>(a);
+    return launch_fwd_cfg<E, D, false, QB, NW, BN, false, ALIBI>(a);
+  }
+  if (a.causal) return launch_fwd_cfg<E, D, true, QB, NW, BN, true, ALIBI>(a);
+  return launch_fwd_cfg<E, D, false, QB, NW, BN, true, ALIBI>(a);
 }
 
 template <typename E, int D>
 hipError_t launch_fwd_d(const FwdArgs& a) {
-  constexpr int BN = ATTN_FWD_BN ? ATTN_FWD_BN : (D == 128 ? 128 : 64);
-  constexpr int QB = ATTN_FWD_QB, NW = ATTN_FWD_NW;
-  if (a.N % 64 == 0) {
-    if (a.causal) return launch_fwd_cfg<E, D, true, QB, NW, BN, false>(a);
-    return launch_fwd_cfg<E, D, false, QB, NW, BN, false>(a);
-  }
-  if (a.causal) return launch_fwd_cfg<E, D, true, QB, NW, BN, true>(a);
-  return launch_fwd_cfg<E, D, false, QB, NW, BN, true>(a);
+  return a.alibi_slopes ? launch_fwd_a<E, D, true>(a) : launch_fwd_a<E, D, false>(a);
 }
 
 }  // namespace

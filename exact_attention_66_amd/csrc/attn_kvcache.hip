@@ -55,13 +55,13 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <typename E, int D, bool CAUSAL>
+template <typename E, int D, bool CAUSAL, bool ALIBI>
 __global__ __launch_bounds__(64) void kv_split_kernel(const typename E::T* __restrict__ Q,
                                                       const typename E::T* __restrict__ K,
                                                       const typename E::T* __restrict__ V,
                                                       float* __restrict__ part_acc, float* __restrict__ part_stat,
                                                       Lay lq, Lay lk, Lay lv, int H, int Nq, int Nk, int nqb, int P,
-                                                      int chunk, float scale_log2) {
+                                                      int chunk, float scale_log2, const float* __restrict__ slopes) {
   using T = typename E::T;
   using v8 = typename E::v8;
   using Tl = KvTile<D>;
@@ -92,6 +92,8 @@ __global__ __launch_bounds__(64) void kv_split_kernel(const typename E::T* __res
   const int bi = bh / H, hi = bh - bi * H;   // batch and head of this unit
   const T* Kh = K + (bi * lk.sb + hi * lk.sh);
   const T* Vh = V + (bi * lv.sb + hi * lv.sh);
+  // ALiBi: score bias -slope * |query position - key position|, in log2 units
+  const float nslope2 = ALIBI ? -slopes[hi] * kLog2e : 0.f;
 
   // per-lane copy offsets (bytes) inside a 32-row block; padding slots at a
   // row's end duplicate its last chunk, slots past row 31 duplicate row 31
@@ -200,11 +202,17 @@ __global__ __launch_bounds__(64) void kv_split_kernel(const typename E::T* __res
         if (key >= k_end || (CAUSAL && key > qrow_lim)) s[j] = -__builtin_inff();
       }
     }
-    // ---- online softmax in the log2 domain
+    // ---- online softmax in the log2 domain (with ALiBi the scores first get
+    // their bias: key k0 + 4h + c, c = 8(j/4) + j%4, at distance dq - c)
+    if constexpr (ALIBI) {
+      const float dq = (float)(q0 + r + shift - k0 - 4 * h);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) s[j] = fmaf(s[j], scale_log2, nslope2 * fabsf(dq - (float)(8 * (j / 4) + j % 4)));
+    }
     float mx = fmax3(fmax3(fmax3(s[0], s[1], s[2]), fmax3(s[3], s[4], s[5]), fmax3(s[6], s[7], s[8])),
                      fmax3(fmax3(s[9], s[10], s[11]), fmax3(s[12], s[13], s[14]), s[15]), -__builtin_inff());
     mx = xhalf_max(mx);
-    const float mt = mx * scale_log2;   // -inf when every key of the block is masked for this row
+    const float mt = ALIBI ? mx : mx * scale_log2;   // -inf when every key of the block is masked for this row
     if (__builtin_amdgcn_ballot_w64(mt > m_run + kRescaleSlack) != 0) {
       const float mn = fmaxf(m_run, mt);
       // equal maxima (also both -inf: a row that has seen no key yet) need no rescale
@@ -219,7 +227,7 @@ __global__ __launch_bounds__(64) void kv_split_kernel(const typename E::T* __res
     const float neg_m = m_run == -__builtin_inff() ? 0.0f : -m_run;
     float pw[16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) pw[j] = fast_exp2(fmaf(s[j], scale_log2, neg_m));
+    for (int j = 0; j < 16; ++j) pw[j] = fast_exp2(ALIBI ? s[j] + neg_m : fmaf(s[j], scale_log2, neg_m));
     float q4[4];
 #pragma unroll
     for (int g = 0; g < 4; ++g) q4[g] = (pw[4 * g] + pw[4 * g + 1]) + (pw[4 * g + 2] + pw[4 * g + 3]);
@@ -333,7 +341,7 @@ __global__ __launch_bounds__(256) void kv_merge_kernel(const float* __restrict__
   if (lane == 0) LSE[row] = (M + __builtin_amdgcn_logf(lsum)) * kLn2;
 }
 
-template <typename E, int D, bool CAUSAL>
+template <typename E, int D, bool CAUSAL, bool ALIBI>
 hipError_t launch_kv_cfg(const KvArgs& a) {
   const int BH = (int)(a.B * a.H);
   const int Nq = (int)a.Nq, Nk = (int)a.Nk, P = a.splits, chunk = a.chunk;
@@ -346,9 +354,11 @@ hipError_t launch_kv_cfg(const KvArgs& a) {
   float* pst = a.part_stat;
   Lay lq = a.lq, lk = a.lk, lv = a.lv, lo = a.lo;
   const int H = (int)a.H;
+  const float* slopes = a.alibi_slopes;
   void* args[] = {(void*)&q, (void*)&k, (void*)&v, (void*)&pacc, (void*)&pst, (void*)&lq, (void*)&lk, (void*)&lv,
-                  (void*)&H, (void*)&Nq, (void*)&Nk, (void*)&nqb, (void*)&P, (void*)&chunk, (void*)&scale_log2};
-  hipError_t e = launch_kernel((const void*)kv_split_kernel<E, D, CAUSAL>, dim3((unsigned)(BH * nqb * P)),
+                  (void*)&H, (void*)&Nq, (void*)&Nk, (void*)&nqb, (void*)&P, (void*)&chunk, (void*)&scale_log2,
+                  (void*)&slopes};
+  hipError_t e = launch_kernel((const void*)kv_split_kernel<E, D, CAUSAL, ALIBI>, dim3((unsigned)(BH * nqb * P)),
                                dim3(64), args, a.stream, 4);
   if (e != hipSuccess) return e;
   const int rows = BH * Nq;
@@ -362,7 +372,8 @@ hipError_t launch_kv_cfg(const KvArgs& a) {
 
 template <typename E, int D>
 hipError_t launch_kv_d(const KvArgs& a) {
-  return a.causal ? launch_kv_cfg<E, D, true>(a) : launch_kv_cfg<E, D, false>(a);
+  if (a.alibi_slopes) return a.causal ? launch_kv_cfg<E, D, true, true>(a) : launch_kv_cfg<E, D, false, true>(a);
+  return a.causal ? launch_kv_cfg<E, D, true, false>(a) : launch_kv_cfg<E, D, false, false>(a);
 }
 
 }  // namespace

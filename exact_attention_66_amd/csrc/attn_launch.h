@@ -30,6 +30,7 @@ struct FwdArgs {
   int dtype;  // 0 bf16, 1 fp16
   hipStream_t stream;
   Lay lq, lk, lv, lo;
+  const float* alibi_slopes;   // [H] fp32 device array, or NULL: no position bias
 };
 
 struct BwdArgs {
@@ -71,6 +72,7 @@ struct BwdArgs {
   void* kc;
   void* vc;
   void* doc;
+  const float* alibi_slopes;   // [H] fp32 device array, or NULL (contiguous calls only)
 };
 
 // Forward for KV-cache shapes: Nq queries against Nk keys, the key axis cut
@@ -92,6 +94,7 @@ struct KvArgs {
   float* part_stat;  // workspace [B,H,Nq,splits,4] fp32: m (log2 units), l, rounded l, unused
   hipStream_t stream;
   Lay lq, lk, lv, lo;  // q, o: [B,H,Nq,d]; k, v: [B,H,Nk,d]
+  const float* alibi_slopes;   // [H] fp32 device array, or NULL
 };
 
 // Split plan: `requested` splits (0: about 1024 waves in all, i.e. one per

@@ -224,6 +224,35 @@ int attn_bwd_strided(const void* q, const void* k, const void* v, const void* o,
  * contiguous 16-bit [B,H,N,d] copies (each rounded up to 256 bytes). */
 size_t attn_bwd_strided_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d);
 
+/*
+ * ALiBi: attn_fwd, attn_bwd and attn_fwd_kvcache with a linear position bias
+ * added to the scaled scores before the softmax (page "FlashAttention技术
+ * 解析 如何让GPT训练速度提升5-9倍" §4.1 names ALiBi for long contexts):
+ *   S_ij = scale * q_i . k_j - m_h * |p_i - j|,  p_i = i + Nk - Nq
+ * (the query's position; Nk = Nq = N outside the KV-cache call), with m_h
+ * the slope of head h.  Causal rows see j <= p_i only, so the bias is
+ * -m_h (p_i - j) there; non-causal rows take the distance both ways.  The
+ * bias enters lse, and the backward recomputes it; no gradient flows to the
+ * slopes.
+ *   alibi_slopes  device array of H fp32 slopes (4-byte aligned; read only;
+ *                 any finite values), the same array for the forward and
+ *                 backward of one computation.
+ * Tensors are contiguous as for attn_fwd / attn_bwd / attn_fwd_kvcache;
+ * every other argument, the workspace sizes and the errors are theirs.
+ */
+int attn_fwd_alibi(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int64_t B, int64_t H, int64_t N, int64_t d, const float* alibi_slopes,
+                   float scale, int causal, int dtype, void* stream);
+int attn_bwd_alibi(const void* q, const void* k, const void* v, const void* o,
+                   const void* dO, const float* lse, void* dq, void* dk, void* dv,
+                   int64_t B, int64_t H, int64_t N, int64_t d, const float* alibi_slopes,
+                   float scale, int causal, int dtype, void* workspace,
+                   size_t workspace_bytes, void* stream);
+int attn_fwd_kvcache_alibi(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                           const float* alibi_slopes, float scale, int causal, int dtype,
+                           int num_splits, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Kernels the library launches, as counted by the profiling window below. */
 enum attn_kernel_kind {
   ATTN_KERNEL_FWD = 0,         /* forward: O and lse */

@@ -259,3 +259,19 @@ def test_bwd_strided_checks(lib):
     assert bwds(lib, s, dq=P[6], dk=P[6] + d, dv=P[6] + 2 * H * d * 2) == ALIAS
     # dq on top of dk with the same layout
     assert bwds(lib, dq=P[7]) == ALIAS
+
+
+def test_alibi_entry_points_check_slopes(lib):
+    assert lib.attn_fwd_alibi(P[0], P[1], P[2], P[3], P[4], 1, 2, 128, 64, None, 0.125, 1, 0, None) == NULL
+    assert lib.attn_fwd_alibi(P[0], P[1], P[2], P[3], P[4], 1, 2, 128, 64, P[10] + 2, 0.125, 1, 0, None) == ALIGN
+    # slopes overlapping an output
+    assert lib.attn_fwd_alibi(P[0], P[1], P[2], P[3], P[4], 1, 2, 128, 64, P[4], 0.125, 1, 0, None) == ALIAS
+    ws = ea.attn_bwd_workspace_bytes(1, 2, 128, 64)
+    assert lib.attn_bwd_alibi(P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7], P[8], 1, 2, 128, 64, None, 0.125, 1, 0,
+                              P[9], ws, None) == NULL
+    assert lib.attn_bwd_alibi(P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7], P[8], 1, 2, 128, 64, P[6], 0.125, 1, 0,
+                              P[9], ws, None) == ALIAS
+    assert lib.attn_fwd_kvcache_alibi(P[0], P[1], P[2], P[3], P[4], 1, 2, 1, 100, 64, None, 0.1, 1, 0, 0, P[5],
+                                      1 << 20, None) == NULL
+    assert lib.attn_fwd_kvcache_alibi(P[0], P[1], P[2], P[3], P[4], 1, 2, 1, 100, 64, P[3], 0.1, 1, 0, 0, P[5],
+                                      1 << 20, None) == ALIAS
