@@ -299,6 +299,8 @@ def main() -> int:
     ap.add_argument("--copy-calibration-bytes", type=int, default=0,
                     help="after the timed steps, also run a plain device copy of this many bytes "
                          "(reference kernel for scaling the HBM byte counters)")
+    ap.add_argument("--alibi", action="store_true",
+                    help="run the ALiBi entry points (slopes 2^(-8(h+1)/H)) on the same workload")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU run: turn rocprofv3 FETCH_SIZE / WRITE_SIZE counter files into the "
                          "workload's HBM bytes per launch in profiles/hbm_traffic.json")
@@ -334,10 +336,28 @@ def main() -> int:
         dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
         ws = torch.empty(ea.attn_bwd_workspace_bytes(*w.shape()), dtype=torch.uint8, device=dev)
 
-    def step():
-        ea.attn_fwd(q, k, v, o, lse, w.scale, w.causal)
-        if w.backward:
-            ea.attn_bwd(q, k, v, o, do, lse, dq, dk, dv, w.scale, w.causal, ws)
+    if args.alibi:
+        import ctypes
+        lib = ea.load()
+        slopes = torch.tensor([2.0 ** (-8.0 * (h + 1) / w.H) for h in range(w.H)], dtype=torch.float32, device=dev)
+        stream = torch.cuda.current_stream().cuda_stream or None
+        dt = ea.ATTN_DTYPE_BF16 if w.dtype == "bf16" else ea.ATTN_DTYPE_FP16
+
+        def step():
+            st = lib.attn_fwd_alibi(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), w.B, w.H,
+                                    w.N, w.d, slopes.data_ptr(), w.scale, int(w.causal), dt, stream)
+            if st == 0 and w.backward:
+                st = lib.attn_bwd_alibi(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                                        lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), w.B, w.H, w.N,
+                                        w.d, slopes.data_ptr(), w.scale, int(w.causal), dt, ws.data_ptr(),
+                                        ws.numel(), stream)
+            if st != 0:
+                raise ea.AttnError(st, "alibi step")
+    else:
+        def step():
+            ea.attn_fwd(q, k, v, o, lse, w.scale, w.causal)
+            if w.backward:
+                ea.attn_bwd(q, k, v, o, do, lse, dq, dk, dv, w.scale, w.causal, ws)
 
     for _ in range(args.warmup):
         step()
@@ -374,7 +394,7 @@ def main() -> int:
         "peak": PEAK_TFLOPS,
         "unit": "TFLOP/s",
         "frac": round(achieved / PEAK_TFLOPS, 4),
-        "traffic": measured_traffic(dominant, w.name),
+        "traffic": None if args.alibi else measured_traffic(dominant, w.name),
     }
 
     line = {
@@ -391,7 +411,7 @@ def main() -> int:
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
-                   "passes": "fwd+bwd" if w.backward else "fwd", "seed": w.seed},
+                   "passes": "fwd+bwd" if w.backward else "fwd", "seed": w.seed, "alibi": bool(args.alibi)},
         "pct_of_peak": round(100 * value / PEAK_TFLOPS, 2),
         "kernels": kernels,
         "roofline": roofline,
