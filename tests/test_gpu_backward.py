@@ -79,8 +79,8 @@ def test_backward_full_size_sampled_heads(name):
         log(f"  oracle head ({b},{h})")
         ref = oracle.backward_head(*(workloads.to_f64_numpy(x[n][b, h]) for n in ("q", "k", "v", "do")),
                                    w.scale, w.causal, row_block=rb)
-        for gname, g, gr in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref):
-            check_grad(f64(g[b, h]), gr, f"{gname}[{b},{h}]")
+        errs = [check_grad(f64(g[b, h]), gr, f"{gname}[{b},{h}]") for gname, g, gr in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref)]
+        log(f"  head ({b},{h}): relative Frobenius error dQ {errs[0]:.2e} dK {errs[1]:.2e} dV {errs[2]:.2e}")
 
 
 def test_backward_deterministic():
