@@ -8,7 +8,9 @@ attention with B=4, H=32, N=4096, d=128 in bf16.  Throughput counts
 4*B*H*N^2*d flops for the forward (halved when causal) and 2.5x that for the
 backward.
 
-Besides the headline number the line carries:
+The K timed steps run twice: once plainly for the step time (the headline
+value), once with per-launch HIP events for the kernel durations.  Besides
+the headline number the line carries:
   roofline      the dominant kernel's counted flops per launch over its
                 average duration, both measured live with HIP events that
                 the launches themselves record, against MI355X's dense
@@ -173,6 +175,32 @@ def record_traffic(fetch_csv: str, write_csv: str, workload: str) -> int:
     return 0
 
 
+def timed_passes(step, steps: int):
+    """Time `steps` steps twice, each pass bracketed by a device synchronize:
+    first plainly (events around the whole pass: the step time), then with
+    the library's profiling window open, in which every launch records its
+    own event pair on its stream (the per-kernel durations).  Per-launch
+    events add host work to each launch, about 10 us, which would otherwise
+    show up as idle time between short kernels in the step time."""
+    import torch
+    import exact_attention_66_amd as ea
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_per_step = e0.elapsed_time(e1) / steps
+    ea.attn_profile_start()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    prof = ea.attn_profile_stop()
+    return ms_per_step, prof
+
+
 def copy_calibration(nbytes: int, dev) -> None:
     """A plain device-to-device copy of nbytes (three times): the reference
     kernel whose byte counters scale those of the attention kernels."""
@@ -239,15 +267,7 @@ def bench_kvcache(args, w: workloads.KvWorkload) -> int:
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ea.attn_profile_start()
-    e0.record()
-    for i in range(args.steps):
-        step(args.warmup + i)
-    e1.record()
-    torch.cuda.synchronize()
-    prof = ea.attn_profile_stop()
-    ms_per_step = e0.elapsed_time(e1) / args.steps
+    ms_per_step, prof = timed_passes(lambda i: step(args.warmup + i), args.steps)
     copy_calibration(args.copy_calibration_bytes, dev)
     kernels = {kname: {"launches": n, "avg_ms": round(t / n, 5)} for kname, (n, t) in prof.items() if n}
     # the split kernel reads K, V and Q once: its algorithmic bytes (its
@@ -362,16 +382,7 @@ def main() -> int:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ea.attn_profile_start()
-    e0.record()
-    for _ in range(args.steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    prof = ea.attn_profile_stop()
-    ms_per_step = e0.elapsed_time(e1) / args.steps
+    ms_per_step, prof = timed_passes(lambda i: step(), args.steps)
 
     copy_calibration(args.copy_calibration_bytes, dev)
 

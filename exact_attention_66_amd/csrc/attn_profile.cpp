@@ -25,22 +25,55 @@ struct Rec {
 std::atomic<bool> g_on{false};
 std::mutex g_mu;
 std::vector<Rec> g_recs;
+// Events created when the window opens, so that timed launches do not pay
+// for hipEventCreate (about 10 us per short launch).  All are destroyed when
+// the window closes.
+std::vector<hipEvent_t> g_pool;
+constexpr int kPoolEvents = 1024;
+
+void destroy_all_locked() {
+  for (auto& r : g_recs) {
+    (void)hipEventDestroy(r.start);
+    (void)hipEventDestroy(r.stop);
+  }
+  g_recs.clear();
+  for (hipEvent_t ev : g_pool) (void)hipEventDestroy(ev);
+  g_pool.clear();
+}
+
+// An event from the pool, or a new one when the pool is empty.
+hipError_t take_event(hipEvent_t* ev) {
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (!g_pool.empty()) {
+      *ev = g_pool.back();
+      g_pool.pop_back();
+      return hipSuccess;
+    }
+  }
+  return hipEventCreate(ev);
+}
+
+void give_back(hipEvent_t ev) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  g_pool.push_back(ev);
+}
 
 }  // namespace
 
 hipError_t launch_kernel(const void* fn, dim3 grid, dim3 block, void** args, hipStream_t stream, int kind) {
   if (!g_on.load(std::memory_order_acquire)) return hipLaunchKernel(fn, grid, block, args, 0, stream);
   hipEvent_t e0 = nullptr, e1 = nullptr;
-  hipError_t e = hipEventCreate(&e0);
-  if (e == hipSuccess) e = hipEventCreate(&e1);
+  hipError_t e = take_event(&e0);
+  if (e == hipSuccess) e = take_event(&e1);
   if (e != hipSuccess) {
-    if (e0) (void)hipEventDestroy(e0);
+    if (e0) give_back(e0);
     return e;
   }
   e = hipExtLaunchKernel(fn, grid, block, args, 0, stream, e0, e1, 0);
   if (e != hipSuccess) {
-    (void)hipEventDestroy(e0);
-    (void)hipEventDestroy(e1);
+    give_back(e0);
+    give_back(e1);
     return e;
   }
   std::lock_guard<std::mutex> lk(g_mu);
@@ -71,11 +104,13 @@ extern "C" {
 
 int attn_profile_start(void) {
   std::lock_guard<std::mutex> lk(attn::g_mu);
-  for (auto& r : attn::g_recs) {
-    (void)hipEventDestroy(r.start);
-    (void)hipEventDestroy(r.stop);
+  attn::destroy_all_locked();
+  attn::g_pool.reserve(attn::kPoolEvents);
+  for (int i = 0; i < attn::kPoolEvents; ++i) {
+    hipEvent_t ev = nullptr;
+    if (hipEventCreate(&ev) != hipSuccess) break;   // launches create what the pool lacks
+    attn::g_pool.push_back(ev);
   }
-  attn::g_recs.clear();
   attn::g_on.store(true, std::memory_order_release);
   return ATTN_OK;
 }
@@ -98,10 +133,8 @@ int attn_profile_stop(int64_t counts[ATTN_KERNEL_KINDS], double total_ms[ATTN_KE
       if (counts) counts[r.kind] += 1;
       if (total_ms) total_ms[r.kind] += ms;
     }
-    (void)hipEventDestroy(r.start);
-    (void)hipEventDestroy(r.stop);
   }
-  attn::g_recs.clear();
+  attn::destroy_all_locked();
   return status;
 }
 

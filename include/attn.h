@@ -270,7 +270,9 @@ enum attn_kernel_kind {
  * launch is bracketed by a HIP event pair recorded by the launch itself on
  * the kernel's own stream; the events are created by the library and are the
  * only resource it holds, until attn_profile_stop.  attn_profile_start
- * discards earlier records and returns ATTN_OK.  attn_profile_stop closes the
+ * discards earlier records, creates a pool of 1024 events (so that launches
+ * inside the window do not pay for creating them; more are created if the
+ * pool runs out) and returns ATTN_OK.  attn_profile_stop closes the
  * window, waits for the recorded events, and writes, per attn_kernel_kind,
  * the number of launches (counts) and their summed duration in milliseconds
  * (total_ms); either array may be NULL.  Returns ATTN_OK, or ATTN_ERR_HIP if
