@@ -126,6 +126,10 @@ __global__ __launch_bounds__(NW * 64, ATTN_FWD_MINW) void fwd_kernel(const typen
   const T* Vh = V + (bi * lv.sb + hi * lv.sh);
   // ALiBi: score bias -slope * |query position - key position|, in log2 units
   const float nslope2 = ALIBI ? -slopes[hi] * kLog2e : 0.f;
+  // causal ALiBi: the per-slot part of the bias, -nslope2 * (4h + c_j)
+  float alibi_k[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) alibi_k[j] = ALIBI && CAUSAL ? -nslope2 * (float)(4 * h + 8 * (j / 4) + j % 4) : 0.f;
 
   // Q fragments, B operand of S^T = K Q^T: lane holds Q[q = qw0+32qb+r][16ks + 8h .. +7]
   // (loaded below, while the first tile copies are in flight)
@@ -288,9 +292,18 @@ __global__ __launch_bounds__(NW * 64, ATTN_FWD_MINW) void fwd_kernel(const typen
     for (int qb = 0; qb < QB; ++qb) {
       // With ALiBi the scores are first taken to the log2 domain with their
       // bias (key kbk0 + 4h + c, c = 8(j/4) + j%4, at distance dq - c from
-      // the query), so that the row max is over biased scores.
+      // the query), so that the row max is over biased scores.  Causal: every
+      // visible key is at distance >= 0, so the bias is nslope2 * (dq0 - 4h - c)
+      // with dq0 = query - kbk0 the same in both halves of the wave; the
+      // per-slot part is a per-lane constant (alibi_k) and the block part
+      // bshift enters only the row max and the exponent offset.
       f32x16 x = s[qb];
-      if constexpr (ALIBI) {
+      float bshift = 0.f;
+      if constexpr (ALIBI && CAUSAL) {
+        bshift = nslope2 * (float)(qw0 + qb * 32 + r - kbk0);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) x[j] = fmaf(x[j], scale_log2, alibi_k[j]);
+      } else if constexpr (ALIBI) {
         const float dq = (float)(qw0 + qb * 32 + r - kbk0 - 4 * h);
 #pragma unroll
         for (int j = 0; j < 16; ++j)
@@ -301,7 +314,7 @@ __global__ __launch_bounds__(NW * 64, ATTN_FWD_MINW) void fwd_kernel(const typen
       const float m4 = fmax3(x[12], x[13], x[14]);
       float mx = fmax3(fmax3(m0, m1, m2), fmax3(m3, m4, x[15]), -__builtin_inff());
       mx = xhalf_max(mx);
-      const float mt = ALIBI ? mx : mx * scale_log2;
+      const float mt = ALIBI ? mx + bshift : mx * scale_log2;
       const bool need = mt > m_run[qb] + kRescaleSlack;
       if (__builtin_amdgcn_ballot_w64(need) != 0) {
         const float mn = fmaxf(m_run[qb], mt);
@@ -312,7 +325,7 @@ __global__ __launch_bounds__(NW * 64, ATTN_FWD_MINW) void fwd_kernel(const typen
         for (int db = 0; db < DB; ++db) oacc[qb][db] *= alpha;
         m_run[qb] = mn;
       }
-      const float neg_m = -m_run[qb];
+      const float neg_m = ALIBI ? bshift - m_run[qb] : -m_run[qb];
       float p[16];
 #pragma unroll
       for (int j = 0; j < 16; ++j) p[j] = fast_exp2(ALIBI ? x[j] + neg_m : fmaf(x[j], scale_log2, neg_m));

@@ -94,6 +94,9 @@ __global__ __launch_bounds__(64) void kv_split_kernel(const typename E::T* __res
   const T* Vh = V + (bi * lv.sb + hi * lv.sh);
   // ALiBi: score bias -slope * |query position - key position|, in log2 units
   const float nslope2 = ALIBI ? -slopes[hi] * kLog2e : 0.f;
+  float alibi_k[16];   // causal ALiBi: the per-slot part of the bias, -nslope2 * (4h + c_j)
+#pragma unroll
+  for (int j = 0; j < 16; ++j) alibi_k[j] = ALIBI && CAUSAL ? -nslope2 * (float)(4 * h + 8 * (j / 4) + j % 4) : 0.f;
 
   // per-lane copy offsets (bytes) inside a 32-row block; padding slots at a
   // row's end duplicate its last chunk, slots past row 31 duplicate row 31
@@ -204,7 +207,15 @@ __global__ __launch_bounds__(64) void kv_split_kernel(const typename E::T* __res
     }
     // ---- online softmax in the log2 domain (with ALiBi the scores first get
     // their bias: key k0 + 4h + c, c = 8(j/4) + j%4, at distance dq - c)
-    if constexpr (ALIBI) {
+    // (causal: every visible key is at distance >= 0, so the bias splits into
+    // the per-lane constants alibi_k and a block part bshift that enters only
+    // the row max and the exponent offset)
+    float bshift = 0.f;
+    if constexpr (ALIBI && CAUSAL) {
+      bshift = nslope2 * (float)(q0 + r + shift - k0);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) s[j] = fmaf(s[j], scale_log2, alibi_k[j]);
+    } else if constexpr (ALIBI) {
       const float dq = (float)(q0 + r + shift - k0 - 4 * h);
 #pragma unroll
       for (int j = 0; j < 16; ++j) s[j] = fmaf(s[j], scale_log2, nslope2 * fabsf(dq - (float)(8 * (j / 4) + j % 4)));
@@ -212,7 +223,7 @@ __global__ __launch_bounds__(64) void kv_split_kernel(const typename E::T* __res
     float mx = fmax3(fmax3(fmax3(s[0], s[1], s[2]), fmax3(s[3], s[4], s[5]), fmax3(s[6], s[7], s[8])),
                      fmax3(fmax3(s[9], s[10], s[11]), fmax3(s[12], s[13], s[14]), s[15]), -__builtin_inff());
     mx = xhalf_max(mx);
-    const float mt = ALIBI ? mx : mx * scale_log2;   // -inf when every key of the block is masked for this row
+    const float mt = ALIBI ? mx + bshift : mx * scale_log2;   // -inf when every key of the block is masked for this row
     if (__builtin_amdgcn_ballot_w64(mt > m_run + kRescaleSlack) != 0) {
       const float mn = fmaxf(m_run, mt);
       // equal maxima (also both -inf: a row that has seen no key yet) need no rescale
@@ -224,7 +235,8 @@ __global__ __launch_bounds__(64) void kv_split_kernel(const typename E::T* __res
       m_run = mn;
     }
     // a row with no visible key so far has only -inf scores: weight exp2(-inf) = 0
-    const float neg_m = m_run == -__builtin_inff() ? 0.0f : -m_run;
+    float neg_m = m_run == -__builtin_inff() ? 0.0f : -m_run;
+    if constexpr (ALIBI) neg_m += bshift;
     float pw[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) pw[j] = fast_exp2(ALIBI ? s[j] + neg_m : fmaf(s[j], scale_log2, neg_m));
