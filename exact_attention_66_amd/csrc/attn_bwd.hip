@@ -46,6 +46,11 @@
 // This file is compiled with MFMA results in VGPRs (the softmax reads them
 // without copies out of AGPRs); the operands read from LDS are steered into
 // AGPRs instead (in_agpr).
+// Two more instantiation flags: STRIDED (the inputs in callers' layouts:
+// (1) reads them through their strides and writes contiguous copies of Q, K,
+// V, dO that (2) and (3) read, whose epilogues store dQ, dK, dV through
+// their strides) and ALIBI (the linear position bias -m_h |i - j| added to
+// the exponent of P in (2) and (3)).  Without them the code is unchanged.
 #include "attn_device.h"
 #include "attn_launch.h"
 

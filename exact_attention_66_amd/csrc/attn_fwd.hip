@@ -30,7 +30,12 @@
 //  * causal launches order work units heaviest query block first;
 //  * any N: rows past the end are neither read nor stored, and the last
 //    tile's keys past the end are masked (the TAIL instantiation, chosen
-//    when N is not a multiple of 64, so that other launches pay nothing).
+//    when N is not a multiple of 64, so that other launches pay nothing);
+//  * every tensor is addressed through its own (batch, head, token) strides
+//    with a contiguous head dimension, so any such layout is read in place;
+//  * the ALIBI instantiation adds the linear position bias
+//    -m_h |i - j| (page "FlashAttention技术解析 如何让GPT训练速度提升5-9倍"
+//    §4.1 names ALiBi) to the scores before the row max.
 #include "attn_device.h"
 #include "attn_launch.h"
 

@@ -24,7 +24,9 @@
 //    square forward) and the natural-log lse.
 //
 // Causal alignment for Nq != Nk: query i is position Nk - Nq + i of the
-// sequence, so it sees keys j <= i + Nk - Nq.
+// sequence, so it sees keys j <= i + Nk - Nq.  The ALIBI instantiation adds
+// the linear position bias -m_h |position - j| to the scores before the row
+// max (the ALiBi entry point of the C ABI).
 #include "attn_device.h"
 #include "attn_launch.h"
 
