@@ -53,9 +53,18 @@ def source_hash(kernel: str) -> str | None:
     files = [path, "exact_attention_66_amd/csrc/attn_device.h", "exact_attention_66_amd/csrc/attn_launch.h"]
     h = hashlib.sha256()
     for f in files:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
+
+
+def _code_only(text: str) -> str:
+    """Source text without comments and blank lines: edits to comments do not
+    invalidate a counter record taken on the same code."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = [re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines()]
+    return "\n".join(ln for ln in lines if ln.strip())
 
 
 def measured_traffic(kernel: str, workload: str):
