@@ -229,9 +229,11 @@ def cpu_baseline_kv(w: workloads.KvWorkload, x, budget_s: float):
     import oracle
 
     heads, t0 = 0, time.perf_counter()
+    G = w.H // w.kv_heads
     for b in range(w.B):
         for h in range(w.H):
-            oracle.forward_head(*(workloads.to_f64_numpy(x[n][b, h]) for n in ("q", "k", "v")), w.scale, w.causal)
+            oracle.forward_head(workloads.to_f64_numpy(x["q"][b, h]), workloads.to_f64_numpy(x["k"][b, h // G]),
+                                workloads.to_f64_numpy(x["v"][b, h // G]), w.scale, w.causal)
             heads += 1
             if time.perf_counter() - t0 >= budget_s:
                 break
@@ -265,13 +267,30 @@ def bench_kvcache(args, w: workloads.KvWorkload) -> int:
     sets = [{n: x[n].to(dev) for n in ("q", "k", "v")} for _ in range(copies)]
     o = torch.empty((w.B, w.H, w.Nq, w.d), dtype=w.torch_dtype, device=dev)
     lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
-    ws = torch.empty(ea.attn_fwd_kvcache_workspace_bytes(w.B, w.H, w.Nq, w.Nk, w.d, 0), dtype=torch.uint8,
-                     device=dev)
-    splits = ea.attn_fwd_kvcache_splits(w.B, w.H, w.Nq, w.Nk, w.d, 0)
+    G = w.H // w.kv_heads
+    if G > 1:   # grouped heads: the G query heads of a KV head share its pass over K and V
+        ws = torch.empty(ea.attn_fwd_kvcache_gqa_workspace_bytes(w.B, w.H, w.kv_heads, w.Nq, w.Nk, w.d, 0),
+                         dtype=torch.uint8, device=dev)
+        splits = ea.attn_fwd_kvcache_splits(w.B, w.kv_heads, G * w.Nq, w.Nk, w.d, 0)
+        lib = ea.load()
+        stream = torch.cuda.current_stream().cuda_stream or None
+        dt = ea.ATTN_DTYPE_BF16 if w.dtype == "bf16" else ea.ATTN_DTYPE_FP16
 
-    def step(i):
-        t = sets[i % copies]
-        ea.attn_fwd_kvcache(t["q"], t["k"], t["v"], o, lse, w.scale, w.causal, ws)
+        def step(i):
+            t = sets[i % copies]
+            st = lib.attn_fwd_kvcache_gqa(t["q"].data_ptr(), t["k"].data_ptr(), t["v"].data_ptr(), o.data_ptr(),
+                                          lse.data_ptr(), w.B, w.H, w.kv_heads, w.Nq, w.Nk, w.d, None, w.scale,
+                                          int(w.causal), dt, 0, ws.data_ptr(), ws.numel(), stream)
+            if st != 0:
+                raise ea.AttnError(st, "attn_fwd_kvcache_gqa")
+    else:
+        ws = torch.empty(ea.attn_fwd_kvcache_workspace_bytes(w.B, w.H, w.Nq, w.Nk, w.d, 0), dtype=torch.uint8,
+                         device=dev)
+        splits = ea.attn_fwd_kvcache_splits(w.B, w.H, w.Nq, w.Nk, w.d, 0)
+
+        def step(i):
+            t = sets[i % copies]
+            ea.attn_fwd_kvcache(t["q"], t["k"], t["v"], o, lse, w.scale, w.causal, ws)
 
     for i in range(args.warmup):
         step(i)
@@ -297,8 +316,8 @@ def bench_kvcache(args, w: workloads.KvWorkload) -> int:
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d, "causal": w.causal,
-                   "splits": splits, "input_copies": copies, "seed": w.seed},
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "Hkv": w.kv_heads, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
+                   "causal": w.causal, "splits": splits, "input_copies": copies, "seed": w.seed},
         "kernels": kernels,
         "roofline": {
             "kernel": "kv_split",

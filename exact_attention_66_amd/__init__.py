@@ -31,5 +31,7 @@ from ._binding import (  # noqa: F401
     forward_alibi,
     backward_alibi,
     forward_kvcache_alibi,
+    forward_kvcache_gqa,
+    attn_fwd_kvcache_gqa_workspace_bytes,
     load,
 )

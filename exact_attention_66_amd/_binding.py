@@ -28,7 +28,7 @@ STATUS_NAMES = {
 EXPORTED = ["attn_fwd", "attn_fwd_strided", "attn_bwd_workspace_bytes", "attn_bwd", "attn_fwd_kvcache",
             "attn_fwd_kvcache_strided", "attn_fwd_kvcache_workspace_bytes", "attn_fwd_kvcache_splits",
             "attn_bwd_strided", "attn_bwd_strided_workspace_bytes", "attn_fwd_alibi", "attn_bwd_alibi",
-            "attn_fwd_kvcache_alibi",
+            "attn_fwd_kvcache_alibi", "attn_fwd_kvcache_gqa", "attn_fwd_kvcache_gqa_workspace_bytes",
             "attn_profile_start",
             "attn_profile_stop", "attn_status_string", "attn_last_hip_error"]
 # attn_kernel_kind values
@@ -82,6 +82,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_fwd_kvcache_alibi.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, vp, f32, i32, i32, i32, vp,
                                            sz, vp]
     lib.attn_fwd_kvcache_alibi.restype = i32
+    lib.attn_fwd_kvcache_gqa.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, vp, f32, i32, i32, i32,
+                                         vp, sz, vp]
+    lib.attn_fwd_kvcache_gqa.restype = i32
+    lib.attn_fwd_kvcache_gqa_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i64, i32]
+    lib.attn_fwd_kvcache_gqa_workspace_bytes.restype = sz
     lib.attn_bwd_strided_workspace_bytes.argtypes = [i64, i64, i64, i64]
     lib.attn_bwd_strided_workspace_bytes.restype = sz
     lib.attn_fwd_kvcache_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i32]
@@ -356,4 +361,32 @@ def forward_kvcache_alibi(q, k, v, alibi_slopes, scale: Optional[float] = None, 
                                        ws.numel(), _stream(stream))
     if st != ATTN_OK:
         raise AttnError(st, "attn_fwd_kvcache_alibi")
+    return o, lse
+
+
+def attn_fwd_kvcache_gqa_workspace_bytes(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int,
+                                         num_splits: int = 0) -> int:
+    return int(load().attn_fwd_kvcache_gqa_workspace_bytes(B, Hq, Hkv, Nq, Nk, d, int(num_splits)))
+
+
+def forward_kvcache_gqa(q, k, v, scale: Optional[float] = None, causal: bool = False, num_splits: int = 0,
+                        alibi_slopes=None, workspace=None, stream=None):
+    """attn_fwd_kvcache_gqa on contiguous q [B,Hq,Nq,d] and k, v [B,Hkv,Nk,d]: (o, lse)."""
+    B, Hq, Nq, d = _shape4(q)
+    Hkv, Nk = int(k.shape[1]), int(k.shape[2])
+    if tuple(k.shape) != (B, Hkv, Nk, d) or tuple(v.shape) != (B, Hkv, Nk, d):
+        raise ValueError("k and v must be [B, Hkv, Nk, d] with the batch and head size of q")
+    scale = default_scale(d) if scale is None else scale
+    sl = None if alibi_slopes is None else _slopes(alibi_slopes, Hq, q.device)
+    if workspace is None:
+        workspace = torch.empty(attn_fwd_kvcache_gqa_workspace_bytes(B, Hq, Hkv, Nq, Nk, d, num_splits),
+                                dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    st = load().attn_fwd_kvcache_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, d,
+                                     None if sl is None else _ptr(sl), float(scale), int(bool(causal)),
+                                     _dtype_code(q), int(num_splits), _ptr(workspace),
+                                     workspace.numel() * workspace.element_size(), _stream(stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fwd_kvcache_gqa")
     return o, lse

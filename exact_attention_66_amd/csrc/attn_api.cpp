@@ -128,34 +128,41 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
 }
 
 // Sizes of a KV-cache call: both lengths as in check_common (B*H*ceil(len/64)
-// units fit a launch), plus the split grid and the merge rows.
+// units fit a launch), plus the split grid and the merge rows.  Hkv KV heads
+// serve H query heads (H a multiple of Hkv; Hkv = H without grouping).
 int check_kvcache(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale, int causal, int dtype,
-                  int num_splits) {
+                  int num_splits, int64_t Hkv = -1) {
+  if (Hkv == -1) Hkv = H;   // no grouping
+  if (Hkv < 1 || H < 1 || H % Hkv != 0) return ATTN_ERR_BAD_SHAPE;
   int st = check_common(B, H, Nq, d, scale, dtype);
   if (st != ATTN_OK) return st;
-  st = check_common(B, H, Nk, d, scale, dtype);
+  st = check_common(B, Hkv, Nk, d, scale, dtype);
   if (st != ATTN_OK) return st;
   if (causal && Nk < Nq) return ATTN_ERR_BAD_SHAPE;   // rows with no visible key
   if (num_splits < 0 || num_splits > 4096) return ATTN_ERR_BAD_SHAPE;
+  const int64_t rows = (H / Hkv) * Nq;                // query rows per KV head
   int P = 1, chunk = 32;
-  attn::kv_split_plan(B * H, Nq, Nk, num_splits, &P, &chunk);
-  if (B * H * ((Nq + 31) / 32) * P > (int64_t)INT32_MAX || B * H * Nq > (int64_t)INT32_MAX - 3) return ATTN_ERR_BAD_SHAPE;
-  if (checked_elems(B * H, Nq, P, d) < 0) return ATTN_ERR_BAD_SHAPE;
+  attn::kv_split_plan(B * Hkv, rows, Nk, num_splits, &P, &chunk);
+  if (B * Hkv * ((rows + 31) / 32) * P > (int64_t)INT32_MAX || B * H * Nq > (int64_t)INT32_MAX - 3)
+    return ATTN_ERR_BAD_SHAPE;
+  if (checked_elems(B * Hkv, rows, P, d) < 0) return ATTN_ERR_BAD_SHAPE;
   return ATTN_OK;
 }
 
 // KV-cache forward with per-tensor layouts (lays: q, k, v, o); lse contiguous.
 int kv_impl(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H, int64_t Nq,
             int64_t Nk, int64_t d, const attn::Lay* lays, float scale, int causal, int dtype, int num_splits,
-            void* workspace, size_t workspace_bytes, void* stream, const float* slopes = nullptr) {
+            void* workspace, size_t workspace_bytes, void* stream, const float* slopes = nullptr,
+            int64_t Hkv = -1) {
   if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL_PTR;
-  int st = check_kvcache(B, H, Nq, Nk, d, scale, causal, dtype, num_splits);
+  if (Hkv == -1) Hkv = H;   // no grouping
+  int st = check_kvcache(B, H, Nq, Nk, d, scale, causal, dtype, num_splits, Hkv);
   if (st != ATTN_OK) return st;
   for (int i = 0; i < 4; ++i)
     if (!lay_ok(lays[i])) return ATTN_ERR_BAD_LAYOUT;
   if (!lay_injective(lays[3], B, H, Nq, d)) return ATTN_ERR_BAD_LAYOUT;
   int P = 1, chunk = 32;
-  attn::kv_split_plan(B * H, Nq, Nk, num_splits, &P, &chunk);
+  attn::kv_split_plan(B * Hkv, (H / Hkv) * Nq, Nk, num_splits, &P, &chunk);
   const size_t need = attn::kv_acc_bytes(B * H, Nq, P, d) + attn::kv_stat_bytes(B * H, Nq, P);
   if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE_TOO_SMALL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
@@ -163,8 +170,8 @@ int kv_impl(const void* q, const void* k, const void* v, void* o, float* lse, in
     return ATTN_ERR_MISALIGNED;
   const size_t lb = (size_t)(B * H * Nq) * 4;
   struct R { const void* p; size_t n; };
-  const R ins[] = {{q, lay_extent(lays[0], B, H, Nq, d)}, {k, lay_extent(lays[1], B, H, Nk, d)},
-                   {v, lay_extent(lays[2], B, H, Nk, d)}, {slopes, slopes ? (size_t)H * 4 : 0}};
+  const R ins[] = {{q, lay_extent(lays[0], B, H, Nq, d)}, {k, lay_extent(lays[1], B, Hkv, Nk, d)},
+                   {v, lay_extent(lays[2], B, Hkv, Nk, d)}, {slopes, slopes ? (size_t)H * 4 : 0}};
   const R outs[] = {{o, lay_extent(lays[3], B, H, Nq, d)}, {lse, lb}, {workspace, need}};
   for (const R& x : outs) {
     for (const R& y : ins)
@@ -175,7 +182,7 @@ int kv_impl(const void* q, const void* k, const void* v, void* o, float* lse, in
   char* ws = (char*)workspace;
   attn::KvArgs a{q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal != 0, dtype, P, chunk,
                  (float*)ws, (float*)(ws + attn::kv_acc_bytes(B * H, Nq, P, d)), (hipStream_t)stream,
-                 lays[0], lays[1], lays[2], lays[3], slopes};
+                 lays[0], lays[1], lays[2], lays[3], slopes, Hkv};
   return launch_status(attn::launch_kvcache(a));
 }
 
@@ -337,6 +344,27 @@ int attn_fwd_kvcache_alibi(const void* q, const void* k, const void* v, void* o,
   const attn::Lay lays[4] = {cq, ck, ck, cq};
   return kv_impl(q, k, v, o, lse, B, H, Nq, Nk, d, lays, scale, causal, dtype, num_splits, workspace,
                  workspace_bytes, stream, alibi_slopes);
+}
+
+size_t attn_fwd_kvcache_gqa_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d,
+                                            int num_splits) {
+  if (Hkv < 1) return 0;
+  if (check_kvcache(B, Hq, Nq, Nk, d, 1.0f, 0, ATTN_DTYPE_BF16, num_splits, Hkv) != ATTN_OK) return 0;
+  int P = 1, chunk = 32;
+  attn::kv_split_plan(B * Hkv, (Hq / Hkv) * Nq, Nk, num_splits, &P, &chunk);
+  return attn::kv_acc_bytes(B * Hq, Nq, P, d) + attn::kv_stat_bytes(B * Hq, Nq, P);
+}
+
+int attn_fwd_kvcache_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t Hq,
+                         int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, const float* alibi_slopes, float scale,
+                         int causal, int dtype, int num_splits, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  if (Hkv < 1 || checked_elems(B, Hq, Nq, d) < 0 || checked_elems(B, Hkv, Nk, d) < 0) return ATTN_ERR_BAD_SHAPE;
+  if (alibi_slopes && (reinterpret_cast<uintptr_t>(alibi_slopes) & 3u)) return ATTN_ERR_MISALIGNED;
+  const attn::Lay cq = attn::contiguous_lay(Hq, Nq, d), ck = attn::contiguous_lay(Hkv, Nk, d);
+  const attn::Lay lays[4] = {cq, ck, ck, cq};
+  return kv_impl(q, k, v, o, lse, B, Hq, Nq, Nk, d, lays, scale, causal, dtype, num_splits, workspace,
+                 workspace_bytes, stream, alibi_slopes, Hkv);
 }
 
 size_t attn_fwd_kvcache_workspace_bytes(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int num_splits) {

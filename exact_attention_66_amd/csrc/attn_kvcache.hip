@@ -62,8 +62,9 @@ __global__ __launch_bounds__(64) void kv_split_kernel(const typename E::T* __res
                                                       const typename E::T* __restrict__ K,
                                                       const typename E::T* __restrict__ V,
                                                       float* __restrict__ part_acc, float* __restrict__ part_stat,
-                                                      Lay lq, Lay lk, Lay lv, int H, int Nq, int Nk, int nqb, int P,
-                                                      int chunk, float scale_log2, const float* __restrict__ slopes) {
+                                                      Lay lq, Lay lk, Lay lv, int Hkv, int G, int Nq, int Nk, int nqb,
+                                                      int P, int chunk, float scale_log2,
+                                                      const float* __restrict__ slopes) {
   using T = typename E::T;
   using v8 = typename E::v8;
   using Tl = KvTile<D>;
@@ -80,22 +81,32 @@ __global__ __launch_bounds__(64) void kv_split_kernel(const typename E::T* __res
   const int p = (int)(blockIdx.x % (unsigned)P);
   const int rest = (int)(blockIdx.x / (unsigned)P);
   const int qb = rest % nqb;
-  const int bh = rest / nqb;
-  const int q0 = qb * 32;
-  const int q_last = min(Nq, q0 + 32) - 1;
+  const int bhk = rest / nqb;  // batch * Hkv + KV head
   const int shift = Nk - Nq;   // causal: query q sees keys <= q + shift
+  // Rows of the 32-row query tile are (query head in the group, query)
+  // pairs t = g * Nq + q, so the G query heads that share this K and V are
+  // computed from one pass over them; with G = 1 a row is just a query.
+  const int npair = G * Nq;
+  const int t0 = qb * 32, t1 = min(npair, t0 + 32) - 1;
+  const bool wraps = t1 - t0 + 1 >= Nq || t0 % Nq > t1 % Nq;
+  const int qmin = wraps ? 0 : t0 % Nq, qmax = wraps ? Nq - 1 : t1 % Nq;
+  const int trow = t0 + r;                    // this lane's pair
+  const bool row_valid = trow < npair;
+  const int qg = row_valid ? trow / Nq : 0, qq = row_valid ? trow % Nq : 0;
 
   // keys this query block may see, and this split's share of them
-  const int kvis = CAUSAL ? min(Nk, q_last + shift + 1) : Nk;
+  const int kvis = CAUSAL ? min(Nk, qmax + shift + 1) : Nk;
   const int k_beg = p * chunk;
   const int k_end = min(kvis, k_beg + chunk);
   const int nblk = k_end > k_beg ? (k_end - k_beg + 31) / 32 : 0;
 
-  const int bi = bh / H, hi = bh - bi * H;   // batch and head of this unit
-  const T* Kh = K + (bi * lk.sb + hi * lk.sh);
-  const T* Vh = V + (bi * lv.sb + hi * lv.sh);
+  const int bi = bhk / Hkv, hk = bhk - bi * Hkv;   // batch and KV head of this unit
+  const int hq = hk * G + qg;                        // this lane's query head
+  const T* Kh = K + (bi * lk.sb + hk * lk.sh);
+  const T* Vh = V + (bi * lv.sb + hk * lv.sh);
   // ALiBi: score bias -slope * |query position - key position|, in log2 units
-  const float nslope2 = ALIBI ? -slopes[hi] * kLog2e : 0.f;
+  // (the slope of this lane's query head)
+  const float nslope2 = ALIBI ? -slopes[hq] * kLog2e : 0.f;
   float alibi_k[16];   // causal ALiBi: the per-slot part of the bias, -nslope2 * (4h + c_j)
 #pragma unroll
   for (int j = 0; j < 16; ++j) alibi_k[j] = ALIBI && CAUSAL ? -nslope2 * (float)(4 * h + 8 * (j / 4) + j % 4) : 0.f;
@@ -144,16 +155,16 @@ __global__ __launch_bounds__(64) void kv_split_kernel(const typename E::T* __res
 
   if (nblk > 0) copy_block(0, 0);
 
-  // Q fragments (B operand of S^T = K Q^T): lane holds Q[q0 + r][16 ks + 8 h .. +7],
-  // zero for rows past Nq (their results are never stored)
+  // Q fragments (B operand of S^T = K Q^T): lane holds row (head hq, query
+  // qq), d = 16 ks + 8 h .. +7; zero for rows past the last pair (their
+  // results are never stored)
   v8 qf[KS];
   {
-    const bool qv = q0 + r < Nq;
-    const T* qrow = Q + (bi * lq.sb + hi * lq.sh) + (size_t)(qv ? q0 + r : 0) * lq.sn;
+    const T* qrow = Q + (bi * lq.sb + hq * lq.sh) + (size_t)qq * lq.sn;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       v8 x = *(const v8*)(qrow + ks * 16 + 8 * h);
-      qf[ks] = qv ? x : v8{};
+      qf[ks] = row_valid ? x : v8{};
     }
   }
 #pragma unroll
@@ -169,7 +180,7 @@ __global__ __launch_bounds__(64) void kv_split_kernel(const typename E::T* __res
 
   const int offK = r * LK + 8 * h;
   const int offV = (4 * h + ((lane & 15) >> 2)) * LV + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  const int qrow_lim = q0 + r + shift;   // causal: last key this lane's query sees
+  const int qrow_lim = qq + shift;   // causal: last key this lane's query sees
 
   for (int i = 0; i < nblk; ++i) {
     const int b = i & 1;
@@ -199,7 +210,7 @@ __global__ __launch_bounds__(64) void kv_split_kernel(const typename E::T* __res
     // ---- mask: keys past the split's end; causal keys after the query's position
     const int k0 = k_beg + 32 * i;
     const bool tail = k0 + 32 > k_end;
-    const bool diag = CAUSAL && k0 + 31 > q0 + shift;
+    const bool diag = CAUSAL && k0 + 31 > qmin + shift;
     if (tail || diag) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
@@ -214,11 +225,11 @@ __global__ __launch_bounds__(64) void kv_split_kernel(const typename E::T* __res
     // the row max and the exponent offset)
     float bshift = 0.f;
     if constexpr (ALIBI && CAUSAL) {
-      bshift = nslope2 * (float)(q0 + r + shift - k0);
+      bshift = nslope2 * (float)(qq + shift - k0);
 #pragma unroll
       for (int j = 0; j < 16; ++j) s[j] = fmaf(s[j], scale_log2, alibi_k[j]);
     } else if constexpr (ALIBI) {
-      const float dq = (float)(q0 + r + shift - k0 - 4 * h);
+      const float dq = (float)(qq + shift - k0 - 4 * h);
 #pragma unroll
       for (int j = 0; j < 16; ++j) s[j] = fmaf(s[j], scale_log2, nslope2 * fabsf(dq - (float)(8 * (j / 4) + j % 4)));
     }
@@ -262,9 +273,8 @@ __global__ __launch_bounds__(64) void kv_split_kernel(const typename E::T* __res
   // ---- this split's partial state of each valid query row
   const float l = xhalf_sum(l_run);
   const float lr = xhalf_sum(lr_run);
-  const int q = q0 + r;
-  if (q >= Nq) return;
-  const size_t row = ((size_t)bh * Nq + q) * P + p;
+  if (!row_valid) return;
+  const size_t row = (((size_t)bi * Hkv * G + hq) * Nq + qq) * P + p;
   float* acc_row_ptr = part_acc + row * D;
 #pragma unroll
   for (int db = 0; db < DB; ++db)
@@ -357,9 +367,10 @@ __global__ __launch_bounds__(256) void kv_merge_kernel(const float* __restrict__
 
 template <typename E, int D, bool CAUSAL, bool ALIBI>
 hipError_t launch_kv_cfg(const KvArgs& a) {
-  const int BH = (int)(a.B * a.H);
+  const int Hkv = (int)a.Hkv, G = (int)(a.H / a.Hkv);
+  const int BHk = (int)(a.B * a.Hkv);
   const int Nq = (int)a.Nq, Nk = (int)a.Nk, P = a.splits, chunk = a.chunk;
-  const int nqb = (Nq + 31) / 32;
+  const int nqb = (G * Nq + 31) / 32;   // 32-row tiles of (query head in group, query) pairs
   const float scale_log2 = a.scale * kLog2e;
   const typename E::T* q = (const typename E::T*)a.q;
   const typename E::T* k = (const typename E::T*)a.k;
@@ -370,12 +381,12 @@ hipError_t launch_kv_cfg(const KvArgs& a) {
   const int H = (int)a.H;
   const float* slopes = a.alibi_slopes;
   void* args[] = {(void*)&q, (void*)&k, (void*)&v, (void*)&pacc, (void*)&pst, (void*)&lq, (void*)&lk, (void*)&lv,
-                  (void*)&H, (void*)&Nq, (void*)&Nk, (void*)&nqb, (void*)&P, (void*)&chunk, (void*)&scale_log2,
-                  (void*)&slopes};
-  hipError_t e = launch_kernel((const void*)kv_split_kernel<E, D, CAUSAL, ALIBI>, dim3((unsigned)(BH * nqb * P)),
+                  (void*)&Hkv, (void*)&G, (void*)&Nq, (void*)&Nk, (void*)&nqb, (void*)&P, (void*)&chunk,
+                  (void*)&scale_log2, (void*)&slopes};
+  hipError_t e = launch_kernel((const void*)kv_split_kernel<E, D, CAUSAL, ALIBI>, dim3((unsigned)(BHk * nqb * P)),
                                dim3(64), args, a.stream, 4);
   if (e != hipSuccess) return e;
-  const int rows = BH * Nq;
+  const int rows = (int)(a.B * a.H) * Nq;
   typename E::T* o = (typename E::T*)a.o;
   float* lse = a.lse;
   const float* cacc = pacc;

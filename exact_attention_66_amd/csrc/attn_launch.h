@@ -93,8 +93,9 @@ struct KvArgs {
   float* part_acc;   // workspace [B,H,Nq,splits,d] fp32: unnormalised O of each split
   float* part_stat;  // workspace [B,H,Nq,splits,4] fp32: m (log2 units), l, rounded l, unused
   hipStream_t stream;
-  Lay lq, lk, lv, lo;  // q, o: [B,H,Nq,d]; k, v: [B,H,Nk,d]
+  Lay lq, lk, lv, lo;  // q, o: [B,H,Nq,d]; k, v: [B,Hkv,Nk,d]
   const float* alibi_slopes;   // [H] fp32 device array, or NULL
+  int64_t Hkv;         // KV heads; query head h uses KV head h / (H / Hkv)
 };
 
 // Split plan: `requested` splits (0: about 1024 waves in all, i.e. one per
@@ -102,6 +103,8 @@ struct KvArgs {
 // and the split count recomputed from it, so that no split is empty unless
 // the causal mask empties it.  A pure function of the sizes: the workspace
 // size and the launch agree on it.
+// For grouped heads (H query heads on Hkv KV heads) the plan is made for
+// BH = B * Hkv units of G * Nq query rows, G = H / Hkv.
 inline void kv_split_plan(int64_t BH, int64_t Nq, int64_t Nk, int requested, int* splits, int* chunk) {
   const int64_t units = BH * ((Nq + 31) / 32);
   int64_t P = requested;

@@ -188,6 +188,29 @@ int attn_fwd_kvcache_strided(const void* q, const void* k, const void* v, void* 
                              int num_splits, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * attn_fwd_kvcache_gqa - attn_fwd_kvcache with grouped heads: Hq query heads
+ * share Hkv KV heads (Hq a multiple of Hkv; query head h attends with KV
+ * head h / (Hq / Hkv)), as caches of grouped-query models are stored.  The
+ * result is the attention of each query head against its group's K and V
+ * (the same as attn_fwd_kvcache with K and V repeated per query head); the
+ * query heads of a group are packed into the rows of one query tile, so
+ * each cached byte is read once per call, not once per query head.
+ *   q, o     [B,Hq,Nq,d];  k, v [B,Hkv,Nk,d];  lse [B,Hq,Nq] (contiguous).
+ *   alibi_slopes  NULL, or Hq fp32 slopes (device array) for the ALiBi bias.
+ *   workspace  at least attn_fwd_kvcache_gqa_workspace_bytes() bytes; the
+ *            split count is attn_fwd_kvcache_splits(B, Hkv, (Hq/Hkv)*Nq, Nk,
+ *            d, num_splits).
+ * Other arguments and errors as for attn_fwd_kvcache (ATTN_ERR_BAD_SHAPE
+ * also when Hq is not a multiple of Hkv).
+ */
+int attn_fwd_kvcache_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d,
+                         const float* alibi_slopes, float scale, int causal, int dtype,
+                         int num_splits, void* workspace, size_t workspace_bytes, void* stream);
+size_t attn_fwd_kvcache_gqa_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq,
+                                            int64_t Nk, int64_t d, int num_splits);
+
+/*
  * attn_fwd_kvcache_workspace_bytes - workspace of attn_fwd_kvcache: per
  * query row and split, d fp32 partial sums plus 4 fp32 statistics, each part
  * rounded up to 256 bytes (about 4*B*H*Nq*P*(d+4) bytes for P splits).

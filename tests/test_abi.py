@@ -275,3 +275,20 @@ def test_alibi_entry_points_check_slopes(lib):
                                       1 << 20, None) == NULL
     assert lib.attn_fwd_kvcache_alibi(P[0], P[1], P[2], P[3], P[4], 1, 2, 1, 100, 64, P[3], 0.1, 1, 0, 0, P[5],
                                       1 << 20, None) == ALIAS
+
+
+def test_kvcache_grouped_heads_checks(lib):
+    # 32 query heads on 8 KV heads, one new token, 4096 keys: planned as 8 KV heads x 4 rows
+    assert ea.attn_fwd_kvcache_gqa_workspace_bytes(1, 32, 8, 1, 4096, 128, 0) == \
+        ea.attn_fwd_kvcache_splits(1, 8, 4, 4096, 128, 0) * 32 * (128 * 4 + 16)
+    assert ea.attn_fwd_kvcache_gqa_workspace_bytes(1, 32, 5, 1, 4096, 128, 0) == 0   # 32 not a multiple of 5
+    assert ea.attn_fwd_kvcache_gqa_workspace_bytes(1, 32, 0, 1, 4096, 128, 0) == 0
+
+    def call(Hq=8, Hkv=2, ws_bytes=1 << 24, sl=None, o=P[3]):
+        return lib.attn_fwd_kvcache_gqa(P[0], P[1], P[2], o, P[4], 1, Hq, Hkv, 1, 100, 64, sl, 0.1, 1, 0, 0, P[5],
+                                        ws_bytes, None)
+    assert call(Hkv=3) == SHAPE
+    assert call(Hkv=0) == SHAPE
+    assert call(ws_bytes=10) == WS
+    assert call(sl=P[6] + 2) == ALIGN
+    assert call(o=P[1]) == ALIAS

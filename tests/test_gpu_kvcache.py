@@ -96,10 +96,69 @@ def test_kvcache_square_agrees_with_attn_fwd():
     assert float((o1.float() - o2.float()).abs().max()) <= 2e-2
 
 
-@pytest.mark.parametrize("name", sorted(workloads.KV_WORKLOADS))
+@pytest.mark.parametrize("name", sorted(n for n, w in workloads.KV_WORKLOADS.items() if w.kv_heads == w.H))
 def test_kvcache_full_size_workloads(name):
     """The decoding workloads at full size, in the launch configuration the benchmark times."""
     ea = require_gpu()
     w = workloads.KV_WORKLOADS[name]
     assert ea.attn_fwd_kvcache_splits(w.B, w.H, w.Nq, w.Nk, w.d, 0) > 1
     _run_and_check(ea, w, 0)
+
+
+@pytest.mark.parametrize("name", sorted(n for n, w in workloads.KV_WORKLOADS.items() if w.kv_heads != w.H))
+def test_kvcache_full_size_grouped_workloads(name):
+    """Grouped-head decoding workloads at full size (every element against the oracle with K, V repeated)."""
+    ea = require_gpu()
+    w = workloads.KV_WORKLOADS[name]
+    x = workloads.make_kv_inputs(w)
+    G = w.H // w.kv_heads
+    log(f"kvcache {w.name}: B={w.B} H={w.H} Hkv={w.kv_heads} Nq={w.Nq} Nk={w.Nk}")
+    o, lse = ea.forward_kvcache_gqa(x["q"].cuda(), x["k"].cuda(), x["v"].cuda(), scale=w.scale, causal=w.causal)
+    torch.cuda.synchronize()
+    k_rep = np.repeat(workloads.to_f64_numpy(x["k"]), G, axis=1)
+    v_rep = np.repeat(workloads.to_f64_numpy(x["v"]), G, axis=1)
+    o_ref, lse_ref = oracle.forward(workloads.to_f64_numpy(x["q"]), k_rep, v_rep, w.scale, w.causal)
+    eo, _ = check_o(f64(o), o_ref, w.dtype)
+    el = check_lse(f64(lse), lse_ref)
+    log(f"  max|dO|={eo:.2e} max|dlse|={el:.2e}")
+
+
+GQA_CASES = [
+    # (B, Hq, Hkv, Nq, Nk, d, dtype, causal, num_splits, alibi)
+    (2, 8, 2, 1, 3000, 128, "bf16", True, 0, False),
+    (1, 32, 8, 1, 4096, 128, "bf16", True, 0, False),     # 32 query heads on 8 KV heads
+    (1, 8, 1, 5, 1000, 64, "fp16", True, 0, False),       # one KV head: 40 (head, query) rows, two tiles
+    (2, 6, 3, 7, 700, 128, "bf16", False, 3, False),
+    (1, 32, 1, 2, 2048, 128, "bf16", True, 0, True),      # ALiBi slopes per query head
+    (1, 4, 4, 3, 500, 64, "bf16", True, 0, False),        # groups of one
+    (1, 16, 2, 40, 333, 128, "fp16", True, 0, False),     # 320 rows per KV head, causal rows of many positions
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Nq,Nk,d,dt,causal,splits,alibi", GQA_CASES,
+                         ids=[f"B{c[0]}q{c[1]}kv{c[2]}n{c[3]}k{c[4]}d{c[5]}{c[6]}{'c' if c[7] else ''}s{c[8]}"
+                              f"{'alibi' if c[9] else ''}" for c in GQA_CASES])
+def test_kvcache_grouped_heads(B, Hq, Hkv, Nq, Nk, d, dt, causal, splits, alibi):
+    """Grouped heads: each query head attends with its group's K and V (the oracle repeats them per head)."""
+    ea = require_gpu()
+    g = torch.Generator(device="cpu")
+    g.manual_seed(33000 + Nk + Hq + Nq)
+    tdt = {"bf16": torch.bfloat16, "fp16": torch.float16}[dt]
+    q = torch.randn((B, Hq, Nq, d), generator=g).to(tdt)
+    k = torch.randn((B, Hkv, Nk, d), generator=g).to(tdt)
+    v = torch.randn((B, Hkv, Nk, d), generator=g).to(tdt)
+    scale = ea.default_scale(d)
+    sl = torch.tensor([2.0 ** (-8.0 * (h + 1) / Hq) for h in range(Hq)], dtype=torch.float32) if alibi else None
+    log(f"kvcache grouped heads B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nk={Nk} d={d} {dt} causal={causal} "
+        f"splits={ea.attn_fwd_kvcache_splits(B, Hkv, (Hq // Hkv) * Nq, Nk, d, splits)}")
+    o, lse = ea.forward_kvcache_gqa(q.cuda(), k.cuda(), v.cuda(), scale=scale, causal=causal, num_splits=splits,
+                                    alibi_slopes=sl)
+    torch.cuda.synchronize()
+    rep = Hq // Hkv
+    k_rep = np.repeat(workloads.to_f64_numpy(k), rep, axis=1)
+    v_rep = np.repeat(workloads.to_f64_numpy(v), rep, axis=1)
+    o_ref, lse_ref = oracle.forward(workloads.to_f64_numpy(q), k_rep, v_rep, scale, causal,
+                                    alibi_slopes=None if sl is None else sl.double().numpy())
+    eo, _ = check_o(f64(o), o_ref, dt)
+    el = check_lse(f64(lse), lse_ref)
+    log(f"  max|dO|={eo:.2e} max|dlse|={el:.2e}")

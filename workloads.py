@@ -126,6 +126,11 @@ class KvWorkload:
     seed: int
     qk_gain: float = 1.0
     description: str = ""
+    Hkv: int = 0        # KV heads (grouped heads: query head h uses KV head h // (H // Hkv)); 0 = H
+
+    @property
+    def kv_heads(self) -> int:
+        return self.Hkv or self.H
 
     @property
     def scale(self) -> float:
@@ -137,7 +142,7 @@ class KvWorkload:
 
     def kv_bytes(self) -> int:
         """K and V bytes: the one pass over the cache that bounds the call."""
-        return 2 * self.B * self.H * self.Nk * self.d * 2
+        return 2 * self.B * self.kv_heads * self.Nk * self.d * 2
 
     def io_bytes(self) -> int:
         """All algorithmic HBM bytes: K, V and Q read, O written (16-bit), lse written (fp32)."""
@@ -158,19 +163,21 @@ KV_WORKLOADS: Dict[str, KvWorkload] = {
                    description="one new token, 32K fp16 cache"),
         KvWorkload("spec_b4h32q8k4096d128", 4, 32, 8, 4096, 128, "bf16", True, 2003,
                    description="eight speculative tokens, causal within the block, 4K cache"),
+        KvWorkload("decode_gqa_b8h32kv8q1k8192d128", 8, 32, 1, 8192, 128, "bf16", True, 2004, Hkv=8,
+                   description="one new token, 32 query heads on 8 KV heads (grouped-query), 8K cache"),
     ]
 }
 
 
 def make_kv_inputs(w: KvWorkload):
-    """CPU tensors q [B,H,Nq,d], k and v [B,H,Nk,d] (I/O dtype): fp32 randn drawn
+    """CPU tensors q [B,H,Nq,d], k and v [B,Hkv,Nk,d] (I/O dtype): fp32 randn drawn
     in the order Q, K, V from the workload's seed, Q and K times qk_gain,
     rounded to nearest-even."""
     g = torch.Generator(device="cpu")
     g.manual_seed(w.seed)
     q = torch.randn((w.B, w.H, w.Nq, w.d), generator=g, dtype=torch.float32)
-    k = torch.randn((w.B, w.H, w.Nk, w.d), generator=g, dtype=torch.float32)
-    v = torch.randn((w.B, w.H, w.Nk, w.d), generator=g, dtype=torch.float32)
+    k = torch.randn((w.B, w.kv_heads, w.Nk, w.d), generator=g, dtype=torch.float32)
+    v = torch.randn((w.B, w.kv_heads, w.Nk, w.d), generator=g, dtype=torch.float32)
     if w.qk_gain != 1.0:
         q.mul_(w.qk_gain)
         k.mul_(w.qk_gain)
