@@ -32,7 +32,8 @@ to check the GPU; it exists so that the tests can pin the recurrence to the
 plain definition.
 
 Readings where the pages are silent: the causal mask is top-left aligned
-with the diagonal kept; lse is in natural log; dropout is 0; the backward pass
+with the diagonal kept; lse is in natural log; dropout is off unless asked
+for (its generator and mask layout: ``oracle/philox.py``); the backward pass
 differentiates O only (lse receives no gradient).
 
 Optional linear position bias (ALiBi) [page "FlashAttention技术解析 如何让GPT
@@ -59,6 +60,8 @@ import math
 from typing import Iterable, Optional, Tuple
 
 import numpy as np
+
+from . import philox
 
 __all__ = [
     "masked_scores",
@@ -108,16 +111,32 @@ def row_softmax(s: np.ndarray) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
     return e / l[:, None], m, l
 
 
-def forward_head_rows(q, k, v, scale: float, causal: bool, rows, alibi_slope=None) -> Tuple[np.ndarray, np.ndarray]:
-    """O and lse of the listed query rows of one head (each row is independent)."""
+def dropout_factor(rows, nq: int, nk: int, dropout) -> Optional[np.ndarray]:
+    """The factor Z * 256 / (256 - t) (0 where dropped) for the listed query rows of one head,
+    or None without dropout; ``dropout`` is ``(p, seed, offset, bh)``."""
+    if dropout is None:
+        return None
+    p, seed, offset, bh = dropout
+    z = philox.keep_mask(bh, nq, nk, p, seed, offset)[np.asarray(rows, dtype=np.int64)]
+    return z * philox.keep_scale(p)
+
+
+def forward_head_rows(q, k, v, scale: float, causal: bool, rows, alibi_slope=None,
+                      dropout=None) -> Tuple[np.ndarray, np.ndarray]:
+    """O and lse of the listed query rows of one head (each row is independent).
+
+    With dropout the probabilities are multiplied by the keep factor before
+    the product with V; lse stays that of the softmax itself."""
     s = masked_scores(q, k, scale, causal, rows, alibi_slope)
     p, m, l = row_softmax(s)
-    o = p @ _f64(v)
+    zf = dropout_factor(rows, np.shape(q)[0], np.shape(k)[0], dropout)
+    o = (p if zf is None else p * zf) @ _f64(v)
     lse = m + np.log(l)
     return o, lse
 
 
-def forward_head(q, k, v, scale: float, causal: bool, row_block: Optional[int] = None, alibi_slope=None):
+def forward_head(q, k, v, scale: float, causal: bool, row_block: Optional[int] = None, alibi_slope=None,
+                 dropout=None):
     """O [N,d] and lse [N] of one head.
 
     ``row_block`` only bounds memory for long sequences: the definition is
@@ -125,17 +144,22 @@ def forward_head(q, k, v, scale: float, causal: bool, row_block: Optional[int] =
     """
     n = np.shape(q)[0]
     if row_block is None or row_block >= n:
-        return forward_head_rows(q, k, v, scale, causal, np.arange(n), alibi_slope)
+        return forward_head_rows(q, k, v, scale, causal, np.arange(n), alibi_slope, dropout)
     o = np.empty((n, np.shape(v)[1]))
     lse = np.empty(n)
     for r0 in range(0, n, row_block):
         rows = np.arange(r0, min(n, r0 + row_block))
-        o[rows], lse[rows] = forward_head_rows(q, k, v, scale, causal, rows, alibi_slope)
+        o[rows], lse[rows] = forward_head_rows(q, k, v, scale, causal, rows, alibi_slope, dropout)
     return o, lse
 
 
-def backward_head(q, k, v, do, scale: float, causal: bool, row_block: Optional[int] = None, alibi_slope=None):
+def backward_head(q, k, v, do, scale: float, causal: bool, row_block: Optional[int] = None, alibi_slope=None,
+                  dropout=None):
     """dQ, dK, dV [N,d] of one head for upstream gradient dO (exact chain rule).
+
+    With dropout (keep factor F = Z * 256 / (256 - t), O = (P o F) V):
+    ``dV = (P o F)^T dO``, ``dP = F o (dO V^T)``, and the rest as without;
+    ``D_i = sum_j P_ij dP_ij`` still equals ``dO_i . O_i``.
 
     ``row_block`` evaluates the same sums ``dV = sum_i P_i^T dO_i`` and
     ``dK = scale * sum_i dS_i^T Q_i`` over groups of query rows, to bound
@@ -154,8 +178,11 @@ def backward_head(q, k, v, do, scale: float, causal: bool, row_block: Optional[i
         rows = np.arange(r0, min(n, r0 + rb))
         s = masked_scores(q, k, scale, causal, rows, alibi_slope)
         p, _, _ = row_softmax(s)
-        dv += p.T @ do[rows]
+        zf = dropout_factor(rows, n, k.shape[0], dropout)
+        dv += (p if zf is None else p * zf).T @ do[rows]
         dp = do[rows] @ v.T
+        if zf is not None:
+            dp = dp * zf
         dsum = (p * dp).sum(axis=1)          # D_i = sum_j P_ij dP_ij
         ds = p * (dp - dsum[:, None])
         dq[rows] = float(scale) * (ds @ k)
@@ -170,20 +197,28 @@ def _heads(x) -> Iterable[Tuple[int, int]]:
             yield bi, hi
 
 
-def forward(q, k, v, scale: float, causal: bool, row_block: Optional[int] = None, alibi_slopes=None):
-    """O [B,H,Nq,d] and lse [B,H,Nq] over all heads (K, V: [B,H,Nk,d]); alibi_slopes: [H] or None."""
+def _head_dropout(dropout, bi: int, hi: int, nh: int):
+    return None if dropout is None else (dropout[0], dropout[1], dropout[2], bi * nh + hi)
+
+
+def forward(q, k, v, scale: float, causal: bool, row_block: Optional[int] = None, alibi_slopes=None,
+            dropout=None):
+    """O [B,H,Nq,d] and lse [B,H,Nq] over all heads (K, V: [B,H,Nk,d]); alibi_slopes: [H] or None;
+    dropout: ``(p, seed, offset)`` or None (head (b, h) draws with index b * H + h)."""
     q = _f64(q)
     b, h, n, d = q.shape
     o = np.empty((b, h, n, np.shape(v)[3]))
     lse = np.empty((b, h, n))
     for bi, hi in _heads(q):
         sl = None if alibi_slopes is None else float(alibi_slopes[hi])
-        o[bi, hi], lse[bi, hi] = forward_head(q[bi, hi], k[bi, hi], v[bi, hi], scale, causal, row_block, sl)
+        o[bi, hi], lse[bi, hi] = forward_head(q[bi, hi], k[bi, hi], v[bi, hi], scale, causal, row_block, sl,
+                                              _head_dropout(dropout, bi, hi, h))
     return o, lse
 
 
-def backward(q, k, v, do, scale: float, causal: bool, row_block: Optional[int] = None, alibi_slopes=None):
-    """dQ, dK, dV [B,H,N,d] over all heads; alibi_slopes: [H] or None."""
+def backward(q, k, v, do, scale: float, causal: bool, row_block: Optional[int] = None, alibi_slopes=None,
+             dropout=None):
+    """dQ, dK, dV [B,H,N,d] over all heads; alibi_slopes: [H] or None; dropout: ``(p, seed, offset)`` or None."""
     q = _f64(q)
     dq = np.empty_like(q)
     dk = np.empty_like(q)
@@ -191,7 +226,8 @@ def backward(q, k, v, do, scale: float, causal: bool, row_block: Optional[int] =
     for bi, hi in _heads(q):
         sl = None if alibi_slopes is None else float(alibi_slopes[hi])
         dq[bi, hi], dk[bi, hi], dv[bi, hi] = backward_head(
-            q[bi, hi], k[bi, hi], v[bi, hi], do[bi, hi], scale, causal, row_block, sl)
+            q[bi, hi], k[bi, hi], v[bi, hi], do[bi, hi], scale, causal, row_block, sl,
+            _head_dropout(dropout, bi, hi, q.shape[1]))
     return dq, dk, dv
 
 
