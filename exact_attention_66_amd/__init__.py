@@ -33,5 +33,9 @@ from ._binding import (  # noqa: F401
     forward_kvcache_alibi,
     forward_kvcache_gqa,
     attn_fwd_kvcache_gqa_workspace_bytes,
+    dropout_threshold,
+    forward_dropout,
+    backward_dropout,
+    dropout_draws,
     load,
 )

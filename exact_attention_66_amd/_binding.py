@@ -23,12 +23,13 @@ STATUS_NAMES = {
     0: "ATTN_OK", 1: "ATTN_ERR_NULL_PTR", 2: "ATTN_ERR_BAD_SHAPE", 3: "ATTN_ERR_UNSUPPORTED_HEAD_DIM",
     4: "ATTN_ERR_BAD_DTYPE", 5: "ATTN_ERR_MISALIGNED", 6: "ATTN_ERR_UNSUPPORTED_SEQLEN",
     7: "ATTN_ERR_BAD_SCALE", 8: "ATTN_ERR_WORKSPACE_TOO_SMALL", 9: "ATTN_ERR_ALIASING", 10: "ATTN_ERR_HIP",
-    11: "ATTN_ERR_BAD_LAYOUT",
+    11: "ATTN_ERR_BAD_LAYOUT", 12: "ATTN_ERR_BAD_DROPOUT",
 }
 EXPORTED = ["attn_fwd", "attn_fwd_strided", "attn_bwd_workspace_bytes", "attn_bwd", "attn_fwd_kvcache",
             "attn_fwd_kvcache_strided", "attn_fwd_kvcache_workspace_bytes", "attn_fwd_kvcache_splits",
             "attn_bwd_strided", "attn_bwd_strided_workspace_bytes", "attn_fwd_alibi", "attn_bwd_alibi",
             "attn_fwd_kvcache_alibi", "attn_fwd_kvcache_gqa", "attn_fwd_kvcache_gqa_workspace_bytes",
+            "attn_dropout_threshold", "attn_fwd_dropout", "attn_bwd_dropout", "attn_dropout_draws",
             "attn_profile_start",
             "attn_profile_stop", "attn_status_string", "attn_last_hip_error"]
 # attn_kernel_kind values
@@ -93,6 +94,16 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_fwd_kvcache_workspace_bytes.restype = sz
     lib.attn_fwd_kvcache_splits.argtypes = [i64, i64, i64, i64, i64, i32]
     lib.attn_fwd_kvcache_splits.restype = i32
+    u64, u32 = ctypes.c_uint64, ctypes.c_uint32
+    lib.attn_dropout_threshold.argtypes = [f32]
+    lib.attn_dropout_threshold.restype = i32
+    lib.attn_fwd_dropout.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, f32, i32, i32, f32, u64, u32, vp]
+    lib.attn_fwd_dropout.restype = i32
+    lib.attn_bwd_dropout.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, f32, i32, i32, f32, u64,
+                                     u32, vp, sz, vp]
+    lib.attn_bwd_dropout.restype = i32
+    lib.attn_dropout_draws.argtypes = [vp, i64, i64, i64, u64, u32, vp]
+    lib.attn_dropout_draws.restype = i32
     lib.attn_profile_start.argtypes = []
     lib.attn_profile_start.restype = i32
     lib.attn_profile_stop.argtypes = [ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double)]
@@ -343,6 +354,53 @@ def backward_alibi(q, k, v, o, lse, dO, alibi_slopes, scale: Optional[float] = N
     if st != ATTN_OK:
         raise AttnError(st, "attn_bwd_alibi")
     return dq, dk, dv
+
+
+def dropout_threshold(dropout_p: float) -> int:
+    """attn_dropout_threshold: the 8-bit drop threshold t (effective probability t / 256); ValueError if invalid."""
+    t = load().attn_dropout_threshold(float(dropout_p))
+    if t < 0:
+        raise ValueError("dropout_p must lie in [0, 1)")
+    return t
+
+
+def forward_dropout(q, k, v, dropout_p: float, seed: int, offset: int = 0, scale: Optional[float] = None,
+                    causal: bool = False, stream=None):
+    """attn_fwd_dropout on contiguous [B, H, N, d] tensors: (o, lse)."""
+    B, H, N, d = _shape4(q)
+    scale = default_scale(d) if scale is None else scale
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    st = load().attn_fwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, float(scale),
+                                 int(bool(causal)), _dtype_code(q), float(dropout_p), int(seed), int(offset),
+                                 _stream(stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fwd_dropout")
+    return o, lse
+
+
+def backward_dropout(q, k, v, o, lse, dO, dropout_p: float, seed: int, offset: int = 0,
+                     scale: Optional[float] = None, causal: bool = False, stream=None):
+    """attn_bwd_dropout on contiguous tensors (same dropout arguments as the forward): (dq, dk, dv)."""
+    B, H, N, d = _shape4(q)
+    scale = default_scale(d) if scale is None else scale
+    ws = torch.empty(attn_bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    st = load().attn_bwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse), _ptr(dq), _ptr(dk),
+                                 _ptr(dv), B, H, N, d, float(scale), int(bool(causal)), _dtype_code(q),
+                                 float(dropout_p), int(seed), int(offset), _ptr(ws), ws.numel(), _stream(stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_bwd_dropout")
+    return dq, dk, dv
+
+
+def dropout_draws(BH: int, Nq: int, Nk: int, seed: int, offset: int = 0, device="cuda", stream=None):
+    """attn_dropout_draws: the [BH, Nq, Nk] uint8 draws (dropped where draw < dropout_threshold(p))."""
+    out = torch.empty((BH, Nq, Nk), dtype=torch.uint8, device=device)
+    st = load().attn_dropout_draws(_ptr(out), int(BH), int(Nq), int(Nk), int(seed), int(offset), _stream(stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_dropout_draws")
+    return out
 
 
 def forward_kvcache_alibi(q, k, v, alibi_slopes, scale: Optional[float] = None, causal: bool = False,

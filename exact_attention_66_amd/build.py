@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libattn.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
-SOURCES = ["attn_api.cpp", "attn_profile.cpp", "attn_fwd.hip", "attn_bwd.hip", "attn_kvcache.hip"]
+SOURCES = ["attn_api.cpp", "attn_profile.cpp", "attn_fwd.hip", "attn_bwd.hip", "attn_kvcache.hip", "attn_dropout.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -103,7 +103,7 @@ int launch_status(hipError_t e) {
 // Forward with per-tensor layouts (lays: q, k, v, o); lse is contiguous.
 int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H, int64_t N,
              int64_t d, const attn::Lay* lays, float scale, int causal, int dtype, void* stream,
-             const float* slopes = nullptr) {
+             const float* slopes = nullptr, const attn::DropCfg* drop = nullptr) {
   if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL_PTR;
   int st = check_common(B, H, N, d, scale, dtype);
   if (st != ATTN_OK) return st;
@@ -124,6 +124,7 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
 
   attn::FwdArgs a{q, k, v, o, lse, B, H, N, d, scale, causal != 0, dtype, (hipStream_t)stream,
                   lays[0], lays[1], lays[2], lays[3], slopes};
+  if (drop) a.drop = *drop;
   return launch_status(attn::launch_fwd(a));
 }
 
@@ -200,7 +201,7 @@ size_t bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d) {
 int bwd_impl(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
              void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N, int64_t d, const attn::Lay* lays,
              bool strided, float scale, int causal, int dtype, void* workspace, size_t workspace_bytes,
-             void* stream, const float* slopes = nullptr) {
+             void* stream, const float* slopes = nullptr, const attn::DropCfg* drop = nullptr) {
   if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv) return ATTN_ERR_NULL_PTR;
   int st = check_common(B, H, N, d, scale, dtype);
   if (st != ATTN_OK) return st;
@@ -241,6 +242,7 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const v
                   tail, tail ? tail + tlb : nullptr, tail ? tail + 2 * tlb : nullptr, tail ? tail + 3 * tlb : nullptr,
                   (hipStream_t)stream, strided, lays[0], lays[1], lays[2], lays[3], lays[4], lays[5], lays[6],
                   lays[7], nullptr, nullptr, nullptr, nullptr, slopes};
+  if (drop) a.drop = *drop;
   if (strided) {
     char* cp = ws + base_need;
     a.qc = cp;
@@ -255,6 +257,25 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const v
 int check_slopes(const float* slopes) {
   if (!slopes) return ATTN_ERR_NULL_PTR;
   if (reinterpret_cast<uintptr_t>(slopes) & 3u) return ATTN_ERR_MISALIGNED;
+  return ATTN_OK;
+}
+
+// Dropout threshold t = floor(256 p + 1/2) for p in [0, 1), else -1.
+int drop_threshold(float p) {
+  if (!(p >= 0.f && p < 1.f)) return -1;
+  const int t = (int)std::floor(256.0 * (double)p + 0.5);
+  return t > 255 ? 255 : t;
+}
+
+int make_drop(float p, uint64_t seed, uint32_t offset, attn::DropCfg* c) {
+  const int t = drop_threshold(p);
+  if (t < 0) return ATTN_ERR_BAD_DROPOUT;
+  c->t = (uint32_t)t;
+  c->key0 = (uint32_t)(seed & 0xFFFFFFFFu);
+  c->key1 = (uint32_t)(seed >> 32);
+  c->offset = offset;
+  c->keep_scale = (float)(256.0 / (256 - t));
+  c->log2_keep_scale = (float)std::log2(256.0 / (256 - t));
   return ATTN_OK;
 }
 
@@ -418,10 +439,50 @@ const char* attn_status_string(int status) {
     case ATTN_ERR_BAD_LAYOUT:
       return "strides must be >= 0 and multiples of 8 elements (token stride < 2^24), and an output's elements "
              "must not overlap";
+    case ATTN_ERR_BAD_DROPOUT: return "dropout_p must lie in [0, 1)";
     default: return "unknown status";
   }
 }
 
 int attn_last_hip_error(void) { return g_last_hip_error; }
+
+int attn_dropout_threshold(float dropout_p) { return drop_threshold(dropout_p); }
+
+int attn_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                     int64_t N, int64_t d, float scale, int causal, int dtype, float dropout_p, uint64_t seed,
+                     uint32_t offset, void* stream) {
+  if (checked_elems(B, H, N, d) < 0) return ATTN_ERR_BAD_SHAPE;
+  attn::DropCfg c{};
+  const int st = make_drop(dropout_p, seed, offset, &c);
+  if (st != ATTN_OK) return st;
+  const attn::Lay cl = attn::contiguous_lay(H, N, d);
+  const attn::Lay lays[4] = {cl, cl, cl, cl};
+  return fwd_impl(q, k, v, o, lse, B, H, N, d, lays, scale, causal, dtype, stream, nullptr, &c);
+}
+
+int attn_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
+                     void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                     int causal, int dtype, float dropout_p, uint64_t seed, uint32_t offset, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  if (checked_elems(B, H, N, d) < 0) return ATTN_ERR_BAD_SHAPE;
+  attn::DropCfg c{};
+  const int st = make_drop(dropout_p, seed, offset, &c);
+  if (st != ATTN_OK) return st;
+  const attn::Lay cl = attn::contiguous_lay(H, N, d);
+  const attn::Lay lays[8] = {cl, cl, cl, cl, cl, cl, cl, cl};
+  return bwd_impl(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, lays, false, scale, causal, dtype, workspace,
+                  workspace_bytes, stream, nullptr, &c);
+}
+
+int attn_dropout_draws(uint8_t* draws, int64_t BH, int64_t Nq, int64_t Nk, uint64_t seed, uint32_t offset,
+                       void* stream) {
+  if (!draws) return ATTN_ERR_NULL_PTR;
+  if (BH < 1 || Nq < 1 || Nk < 1 || BH > INT32_MAX || Nq > INT32_MAX - 31 || Nk > INT32_MAX - 31 ||
+      checked_elems(BH, Nq, Nk, 1) < 0)
+    return ATTN_ERR_BAD_SHAPE;
+  attn::DropCfg c{};
+  make_drop(0.f, seed, offset, &c);
+  return launch_status(attn::launch_dropout_draws(draws, BH, Nq, Nk, c, (hipStream_t)stream));
+}
 
 }  // extern "C"

@@ -52,6 +52,7 @@
 // their strides) and ALIBI (the linear position bias -m_h |i - j| added to
 // the exponent of P in (2) and (3)).  Without them the code is unchanged.
 #include "attn_device.h"
+#include "attn_dropout.h"
 #include "attn_launch.h"
 
 namespace attn {
@@ -232,7 +233,7 @@ __global__ __launch_bounds__(256) void bwd_prep(const typename E::T* __restrict_
 // tile after it starts into the buffer just released.  Tiles that reach the
 // causal diagonal come first and run the same pipeline with the mask applied
 // (sub-tiles entirely above the diagonal come out as P = 0).
-template <typename E, int D, bool CAUSAL, int NW, int BMQ, bool TAIL, bool STRIDED, bool ALIBI>
+template <typename E, int D, bool CAUSAL, int NW, int BMQ, bool TAIL, bool STRIDED, bool ALIBI, bool DROP>
 __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv(
     const typename E::T* __restrict__ Q, const typename E::T* __restrict__ K,
     const typename E::T* __restrict__ V, const typename E::T* __restrict__ dO,
@@ -240,7 +241,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv(
     const typename E::T* __restrict__ QTail, const typename E::T* __restrict__ dOTail,
     const float* __restrict__ NLSE, const float* __restrict__ Dvec, typename E::T* __restrict__ dK,
     typename E::T* __restrict__ dV, int BH, int N, int Np_arg, int nkb, float scale, float scale_log2, Lay ldk,
-    Lay ldv, int H, const float* __restrict__ slopes) {
+    Lay ldv, int H, const float* __restrict__ slopes, DropCfg drop) {
   using T = typename E::T;
   using v8 = typename E::v8;
   const int Np = TAIL ? Np_arg : N;     // padded length: N itself unless TAIL
@@ -286,8 +287,10 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv(
   float nslope2 = 0.f;                  // ALIBI: -slope * log2(e) of this unit's head
   const T *Qh, *dOh, *QTh, *dOTh, *Qtl, *dOtl;
   const float *lse_h, *dd_h;
+  int unit_bh = 0;                      // DROP: batch*head of this unit (generator counter)
   auto set_unit = [&](const int u) {
     const int bh = u / nkb;
+    unit_bh = bh;
     kb0 = (u % nkb) * BN;
     kw0 = kb0 + wu * 32;                 // first key of this wave
     head = (size_t)bh * (size_t)N * D;
@@ -455,18 +458,43 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv(
     if (spread) copy_part(it + 1, OB{}, P3{});
     v8 qbv[2][DB];
     read_t(b ? lqt1 : lqt0, qs, qbv);
-    f32x16 dpacc = join16(d4);
+    // DROP: dP' starts at -D / k (k = 256 / (256 - t)) and P is computed as
+    // k P, so that a kept element's dS = k P dP' = P (k dP - D) and a
+    // dropped one's is k P (-D / k) = -P D
+    const f32x16 dinit = DROP ? join16(d4) * (1.0f / drop.keep_scale) : join16(d4);
+    f32x16 dpacc = dinit;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       in_agpr(da[ks]);
       dpacc = E::mfma32(da[ks], vB[ks], dpacc);
     }
     float p[16];
+    // DROP: the draws of this lane's key against the sub-tile's 16 queries.
+    // Lane u of the quad makes the call for block u (queries qs0 + 8u + 4h ..,
+    // the quad's 4 keys); the bytes of its 4 words are regrouped by key
+    // (word c = byte c of words 0..3) and the quad transpose hands every lane
+    // its own key's word of each block: byte w of tw[m] is query
+    // qs0 + 8m + 4h + w.
+    u32x4 tw;
+    if constexpr (DROP) {
+      const int qu = lane & 3;
+      const u32x4 wv = philox4x32_10((uint32_t)((qs0 >> 2) + 2 * qu + h), (uint32_t)(kw0 + r) >> 2,
+                                     (uint32_t)unit_bh, drop.offset, drop.key0, drop.key1);
+      u32x4 xv;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        xv[c] = ((wv[0] >> (8 * c)) & 0xFFu) | (((wv[1] >> (8 * c)) & 0xFFu) << 8) |
+                (((wv[2] >> (8 * c)) & 0xFFu) << 16) | (((wv[3] >> (8 * c)) & 0xFFu) << 24);
+      tw = quad_transpose(xv, qu);
+    }
     if constexpr (ALIBI) {   // query qs0 + 4h + c (c = 8(j/4) + j%4) at distance dqk + c from key kw0 + r
       const float dqk = (float)(qs0 + 4 * h - kw0 - r);
 #pragma unroll
       for (int j = 0; j < 16; ++j)
         p[j] = fast_exp2(fmaf(sacc[j], scale_log2, nslope2 * fabsf(dqk + (float)(8 * (j / 4) + j % 4))));
+    } else if constexpr (DROP) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) p[j] = fast_exp2(fmaf(sacc[j], scale_log2, drop.log2_keep_scale));
     } else {
 #pragma unroll
       for (int j = 0; j < 16; ++j) p[j] = fast_exp2(sacc[j] * scale_log2);
@@ -481,6 +509,26 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv(
     for (int kk = 0; kk < 2; ++kk)
       pa[kk] = pack8<E>(p[8 * kk + 0], p[8 * kk + 1], p[8 * kk + 2], p[8 * kk + 3], p[8 * kk + 4], p[8 * kk + 5],
                         p[8 * kk + 6], p[8 * kk + 7]);
+    uint32_t km[16];   // DROP: all-ones for kept elements
+    if constexpr (DROP) {
+      const uint32_t add = (256u - drop.t) * 0x00010001u;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        u32x4 pw = __builtin_bit_cast(u32x4, pa[kk]);
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          uint32_t lo, hi;
+          keep_halves(tw[2 * kk + g], add, lo, hi);
+          pw[2 * g] &= half_masks(lo);
+          pw[2 * g + 1] &= half_masks(hi);
+          km[8 * kk + 4 * g + 0] = full_mask(lo, 0);
+          km[8 * kk + 4 * g + 1] = full_mask(lo, 1);
+          km[8 * kk + 4 * g + 2] = full_mask(hi, 0);
+          km[8 * kk + 4 * g + 3] = full_mask(hi, 1);
+        }
+        pa[kk] = __builtin_bit_cast(v8, pw);
+      }
+    }
     sched_interleave<KS, kSchedMfma, 1, kSchedDsRead, 2 * DB / KS, kSchedValu, 3>();
     sched_fence();
 
@@ -505,7 +553,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv(
       }
     float ds[16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) ds[j] = p[j] * dpacc[j];
+    for (int j = 0; j < 16; ++j) ds[j] = p[j] * (DROP ? bit_select(km[j], dpacc[j], dinit[j]) : dpacc[j]);
     v8 sa[2];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
@@ -632,14 +680,14 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv(
 // buffers, two tiles ahead of their use; a copy instruction fills 64
 // consecutive 16-byte slots, so the padding slot of each row gets a
 // duplicate of the row's last chunk and a tile is a whole number of blocks.
-template <typename E, int D, bool CAUSAL, int NW, int BN, bool TAIL, bool STRIDED, bool ALIBI>
+template <typename E, int D, bool CAUSAL, int NW, int BN, bool TAIL, bool STRIDED, bool ALIBI, bool DROP>
 __global__ __launch_bounds__(NW * 64, ATTN_DQ_MINW) void bwd_dq(
     const typename E::T* __restrict__ Q, const typename E::T* __restrict__ K,
     const typename E::T* __restrict__ V, const typename E::T* __restrict__ dO,
     const typename E::T* __restrict__ KT, const typename E::T* __restrict__ KTail,
     const typename E::T* __restrict__ VTail, const float* __restrict__ NLSE, const float* __restrict__ ND,
     typename E::T* __restrict__ dQ, int BH, int N, int Np_arg, int nqb, float scale, float scale_log2, Lay ldq,
-    int H, const float* __restrict__ slopes) {
+    int H, const float* __restrict__ slopes, DropCfg drop) {
   using T = typename E::T;
   const int Np = TAIL ? Np_arg : N;     // padded length: N itself unless TAIL
   using v8 = typename E::v8;
@@ -809,11 +857,33 @@ __global__ __launch_bounds__(NW * 64, ATTN_DQ_MINW) void bwd_dq(
       for (int db = 0; db < DB; ++db) kta[kk][db] = *(const v8*)(ktl + db * 32 * LT + 16 * kk);
 #endif
     float ds[16];
+    // DROP: the draws of this lane's query against the block's 16 keys (as in
+    // the forward: lane u of the quad calls for keys kbk0 + 8u + 4h ..)
+    uint32_t km[16];
+    if constexpr (DROP) {
+      const int qu = lane & 3;
+      const u32x4 tw = quad_transpose(philox4x32_10((uint32_t)(qw0 + r) >> 2, (uint32_t)((kbk0 >> 2) + 2 * qu + h),
+                                                    (uint32_t)bh, drop.offset, drop.key0, drop.key1),
+                                      qu);
+      const uint32_t add = (256u - drop.t) * 0x00010001u;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        uint32_t lo, hi;
+        keep_halves(tw[m], add, lo, hi);
+        km[4 * m + 0] = full_mask(lo, 0);
+        km[4 * m + 1] = full_mask(lo, 1);
+        km[4 * m + 2] = full_mask(hi, 0);
+        km[4 * m + 3] = full_mask(hi, 1);
+      }
+    }
     if constexpr (ALIBI) {   // key kbk0 + 4h + c (c = 8(j/4) + j%4) at distance dq - c from query qw0 + r
       const float dq = (float)(qw0 + r - kbk0 - 4 * h);
 #pragma unroll
       for (int j = 0; j < 16; ++j)
         ds[j] = fast_exp2(fmaf(sacc[j], scale_log2, nslope2 * fabsf(dq - (float)(8 * (j / 4) + j % 4))));
+    } else if constexpr (DROP) {   // k P with k = 256 / (256 - t); dP' started at -D / k
+#pragma unroll
+      for (int j = 0; j < 16; ++j) ds[j] = fast_exp2(fmaf(sacc[j], scale_log2, drop.log2_keep_scale));
     } else {
 #pragma unroll
       for (int j = 0; j < 16; ++j) ds[j] = fast_exp2(sacc[j] * scale_log2);
@@ -829,7 +899,7 @@ __global__ __launch_bounds__(NW * 64, ATTN_DQ_MINW) void bwd_dq(
         if (kbk0 + acc_row(j, h) > qw0 + r) ds[j] = 0.f;
     }
 #pragma unroll
-    for (int j = 0; j < 16; ++j) ds[j] = ds[j] * dpacc[j];
+    for (int j = 0; j < 16; ++j) ds[j] = ds[j] * (DROP ? bit_select(km[j], dpacc[j], dp_init[j]) : dpacc[j]);
     // dQ^T += K^T dS^T: A from the K^T tile (row d, 8 keys in slot order)
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
@@ -901,7 +971,7 @@ __global__ __launch_bounds__(NW * 64, ATTN_DQ_MINW) void bwd_dq(
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       s_init[j] = nlse;
-      dp_init[j] = ndd;
+      dp_init[j] = DROP ? ndd * (1.0f / drop.keep_scale) : ndd;
     }
     __syncthreads();
 
@@ -946,7 +1016,7 @@ __global__ __launch_bounds__(NW * 64, ATTN_DQ_MINW) void bwd_dq(
   }
 }
 
-template <typename E, int D, bool CAUSAL, bool TAIL, bool STRIDED, bool ALIBI>
+template <typename E, int D, bool CAUSAL, bool TAIL, bool STRIDED, bool ALIBI, bool DROP>
 hipError_t launch_bwd_cfg(const BwdArgs& a) {
   constexpr int NWK = 4;            // dK/dV: waves per workgroup (32 keys each)
   constexpr int NWQ = ATTN_DQ_NW;
@@ -973,6 +1043,7 @@ hipError_t launch_bwd_cfg(const BwdArgs& a) {
   Lay lq = a.lq, lk = a.lk, lv = a.lv, lo = a.lo, ldo = a.ldo, ldq = a.ldq, ldk = a.ldk, ldv = a.ldv;
   int H = (int)a.H;
   const float* slopes = a.alibi_slopes;
+  DropCfg drop = a.drop;
   const float* lse = a.lse;
   T* dq = (T*)a.dq;
   T* dk = (T*)a.dk;
@@ -1005,8 +1076,8 @@ hipError_t launch_bwd_cfg(const BwdArgs& a) {
     void* args[] = {(void*)&q2,    (void*)&k2, (void*)&v2, (void*)&dO2, (void*)&qt,  (void*)&dot,
                     (void*)&qtail, (void*)&dotail, (void*)&nlse, (void*)&delta, (void*)&dk, (void*)&dv,
                     (void*)&BH, (void*)&N, (void*)&Np, (void*)&nkb, (void*)&scale, (void*)&scale_log2,
-                    (void*)&ldk, (void*)&ldv, (void*)&H, (void*)&slopes};
-    const void* fn = (const void*)bwd_dkdv<E, D, CAUSAL, NWK, 64, TAIL, STRIDED, ALIBI>;
+                    (void*)&ldk, (void*)&ldv, (void*)&H, (void*)&slopes, (void*)&drop};
+    const void* fn = (const void*)bwd_dkdv<E, D, CAUSAL, NWK, 64, TAIL, STRIDED, ALIBI, DROP>;
     hipError_t e = launch_kernel(fn, dim3((unsigned)persistent_grid(fn, NWK * 64, nkb * BH)), dim3(NWK * 64), args,
                                  a.stream, 2);
     if (e != hipSuccess) return e;
@@ -1015,26 +1086,28 @@ hipError_t launch_bwd_cfg(const BwdArgs& a) {
     const int nqb = (N + NWQ * 32 - 1) / (NWQ * 32);
     void* args[] = {(void*)&q2,   (void*)&k2, (void*)&v2, (void*)&dO2, (void*)&kt, (void*)&ktail, (void*)&vtail,
                     (void*)&nlse, (void*)&delta, (void*)&dq, (void*)&BH, (void*)&N, (void*)&Np, (void*)&nqb,
-                    (void*)&scale, (void*)&scale_log2, (void*)&ldq, (void*)&H, (void*)&slopes};
-    const void* fn = (const void*)bwd_dq<E, D, CAUSAL, NWQ, BNQ, TAIL, STRIDED, ALIBI>;
+                    (void*)&scale, (void*)&scale_log2, (void*)&ldq, (void*)&H, (void*)&slopes, (void*)&drop};
+    const void* fn = (const void*)bwd_dq<E, D, CAUSAL, NWQ, BNQ, TAIL, STRIDED, ALIBI, DROP>;
     return launch_kernel(fn, dim3((unsigned)persistent_grid(fn, NWQ * 64, nqb * BH)), dim3(NWQ * 64), args,
                          a.stream, 3);
   }
 }
 
-template <typename E, int D, bool STRIDED, bool ALIBI>
+template <typename E, int D, bool STRIDED, bool ALIBI, bool DROP = false>
 hipError_t launch_bwd_s(const BwdArgs& a) {
   if (a.N % 64 == 0) {
-    if (a.causal) return launch_bwd_cfg<E, D, true, false, STRIDED, ALIBI>(a);
-    return launch_bwd_cfg<E, D, false, false, STRIDED, ALIBI>(a);
+    if (a.causal) return launch_bwd_cfg<E, D, true, false, STRIDED, ALIBI, DROP>(a);
+    return launch_bwd_cfg<E, D, false, false, STRIDED, ALIBI, DROP>(a);
   }
-  if (a.causal) return launch_bwd_cfg<E, D, true, true, STRIDED, ALIBI>(a);
-  return launch_bwd_cfg<E, D, false, true, STRIDED, ALIBI>(a);
+  if (a.causal) return launch_bwd_cfg<E, D, true, true, STRIDED, ALIBI, DROP>(a);
+  return launch_bwd_cfg<E, D, false, true, STRIDED, ALIBI, DROP>(a);
 }
 
-// ALiBi calls are contiguous (the C ABI has no strided ALiBi entry point)
+// ALiBi and dropout calls are contiguous and never combined (the C ABI has
+// no entry point that takes two of strides, slopes and dropout)
 template <typename E, int D>
 hipError_t launch_bwd_d(const BwdArgs& a) {
+  if (a.drop.t) return launch_bwd_s<E, D, false, false, true>(a);
   if (a.alibi_slopes) return launch_bwd_s<E, D, false, true>(a);
   return a.strided ? launch_bwd_s<E, D, true, false>(a) : launch_bwd_s<E, D, false, false>(a);
 }

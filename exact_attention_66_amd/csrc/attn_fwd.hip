@@ -35,8 +35,13 @@
 //    with a contiguous head dimension, so any such layout is read in place;
 //  * the ALIBI instantiation adds the linear position bias
 //    -m_h |i - j| (page "FlashAttention技术解析 如何让GPT训练速度提升5-9倍"
-//    §4.1 names ALiBi) to the scores before the row max.
+//    §4.1 names ALiBi) to the scores before the row max;
+//  * the DROP instantiation zeroes the dropped 16-bit weights of P after
+//    the row sums are taken (the softmax and lse are those of all keys) and
+//    scales O by 256 / (256 - t) in the epilogue; each lane draws one
+//    generator call per 32-key block (attn_dropout.h).
 #include "attn_device.h"
+#include "attn_dropout.h"
 #include "attn_launch.h"
 
 namespace attn {
@@ -69,7 +74,7 @@ constexpr float kRescaleSlack = 8.0f;
 // with ds_read_b64_tr_b16 by 32 lanes covering 4 rows x 64 bytes (rows 16
 // banks apart: the 4 rows land on 4 disjoint 16-bank groups).  Both are
 // affine, so every read is one per-lane base plus an immediate offset.
-template <typename E, int D, bool CAUSAL, int QB, int NW, int BN, bool TAIL, bool ALIBI>
+template <typename E, int D, bool CAUSAL, int QB, int NW, int BN, bool TAIL, bool ALIBI, bool DROP>
 __global__ __launch_bounds__(NW * 64, ATTN_FWD_MINW) void fwd_kernel(const typename E::T* __restrict__ Q,
                                                                      const typename E::T* __restrict__ K,
                                                                      const typename E::T* __restrict__ V,
@@ -77,7 +82,8 @@ __global__ __launch_bounds__(NW * 64, ATTN_FWD_MINW) void fwd_kernel(const typen
                                                                      float* __restrict__ LSE, Lay lq, Lay lk,
                                                                      Lay lv, Lay lo, int H, int BH, int N,
                                                                      int nqb, float scale_log2,
-                                                                     const float* __restrict__ slopes) {
+                                                                     const float* __restrict__ slopes,
+                                                                     DropCfg drop) {
   using T = typename E::T;
   using v8 = typename E::v8;
   using v4 = typename E::v4;
@@ -343,6 +349,28 @@ __global__ __launch_bounds__(NW * 64, ATTN_FWD_MINW) void fwd_kernel(const typen
         pf[kk][qb] = pack8<E>(p[8 * kk + 0], p[8 * kk + 1], p[8 * kk + 2], p[8 * kk + 3], p[8 * kk + 4],
                               p[8 * kk + 5], p[8 * kk + 6], p[8 * kk + 7]);
       lr_run[qb] += sum8<E>(pf[0][qb], 0.f) + sum8<E>(pf[1][qb], 0.f);
+      if constexpr (DROP) {
+        // this lane's generator call is block u = lane % 4 of the quad's
+        // four 4 x 4 (query, key) blocks: keys kbk0 + 8u + 4h ..
+        const int u = lane & 3;
+        const u32x4 tw = quad_transpose(
+            philox4x32_10((uint32_t)(qw0 + qb * 32 + r) >> 2, (uint32_t)((kbk0 >> 2) + 2 * u + h), (uint32_t)bh,
+                          drop.offset, drop.key0, drop.key1),
+            u);
+        const uint32_t add = (256u - drop.t) * 0x00010001u;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          u32x4 pw = __builtin_bit_cast(u32x4, pf[kk][qb]);
+          uint32_t lo, hi;
+          keep_halves(tw[2 * kk], add, lo, hi);
+          pw[0] &= half_masks(lo);
+          pw[1] &= half_masks(hi);
+          keep_halves(tw[2 * kk + 1], add, lo, hi);
+          pw[2] &= half_masks(lo);
+          pw[3] &= half_masks(hi);
+          pf[kk][qb] = __builtin_bit_cast(v8, pw);
+        }
+      }
     }
     if (kb + 1 < KB) read_k(buf, kb + 1, kf);
     sched_fence();
@@ -416,7 +444,7 @@ __global__ __launch_bounds__(NW * 64, ATTN_FWD_MINW) void fwd_kernel(const typen
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float l = xhalf_sum(l_run[qb]);
-    const float inv = 1.0f / xhalf_sum(lr_run[qb]);
+    const float inv = (DROP ? drop.keep_scale : 1.0f) / xhalf_sum(lr_run[qb]);
     const int q = qw0 + qb * 32 + r;
     if (TAIL && q >= N) continue;   // rows past the end of the sequence
     T* orow = O + (bi * lo.sb + hi * lo.sh) + (size_t)q * lo.sn;
@@ -435,7 +463,7 @@ __global__ __launch_bounds__(NW * 64, ATTN_FWD_MINW) void fwd_kernel(const typen
   }
 }
 
-template <typename E, int D, bool CAUSAL, int QB, int NW, int BN, bool TAIL, bool ALIBI>
+template <typename E, int D, bool CAUSAL, int QB, int NW, int BN, bool TAIL, bool ALIBI, bool DROP>
 hipError_t launch_fwd_cfg(const FwdArgs& a) {
   constexpr int BM = NW * 32 * QB;
   const int BH = (int)(a.B * a.H);
@@ -451,28 +479,31 @@ hipError_t launch_fwd_cfg(const FwdArgs& a) {
   Lay lq = a.lq, lk = a.lk, lv = a.lv, lo = a.lo;
   const int H = (int)a.H;
   const float* slopes = a.alibi_slopes;
+  DropCfg drop = a.drop;
   void* args[] = {(void*)&q, (void*)&k, (void*)&v, (void*)&o, (void*)&lse, (void*)&lq, (void*)&lk, (void*)&lv,
                   (void*)&lo, (void*)&H, (void*)&BH, (void*)&N, (void*)&nqb, (void*)&scale_log2,
-                  (void*)&slopes};
-  return launch_kernel((const void*)fwd_kernel<E, D, CAUSAL, QB, NW, BN, TAIL, ALIBI>, grid, block, args, a.stream,
-                       0);
+                  (void*)&slopes, (void*)&drop};
+  return launch_kernel((const void*)fwd_kernel<E, D, CAUSAL, QB, NW, BN, TAIL, ALIBI, DROP>, grid, block, args,
+                       a.stream, 0);
 }
 
-template <typename E, int D, bool ALIBI>
+template <typename E, int D, bool ALIBI, bool DROP>
 hipError_t launch_fwd_a(const FwdArgs& a) {
   constexpr int BN = ATTN_FWD_BN ? ATTN_FWD_BN : (D == 128 ? 128 : 64);
   constexpr int QB = ATTN_FWD_QB, NW = ATTN_FWD_NW;
   if (a.N % 64 == 0) {
-    if (a.causal) return launch_fwd_cfg<E, D, true, QB, NW, BN, false, ALIBI>(a);
-    return launch_fwd_cfg<E, D, false, QB, NW, BN, false, ALIBI>(a);
+    if (a.causal) return launch_fwd_cfg<E, D, true, QB, NW, BN, false, ALIBI, DROP>(a);
+    return launch_fwd_cfg<E, D, false, QB, NW, BN, false, ALIBI, DROP>(a);
   }
-  if (a.causal) return launch_fwd_cfg<E, D, true, QB, NW, BN, true, ALIBI>(a);
-  return launch_fwd_cfg<E, D, false, QB, NW, BN, true, ALIBI>(a);
+  if (a.causal) return launch_fwd_cfg<E, D, true, QB, NW, BN, true, ALIBI, DROP>(a);
+  return launch_fwd_cfg<E, D, false, QB, NW, BN, true, ALIBI, DROP>(a);
 }
 
+// Dropout and ALiBi are not combined (no entry point takes both).
 template <typename E, int D>
 hipError_t launch_fwd_d(const FwdArgs& a) {
-  return a.alibi_slopes ? launch_fwd_a<E, D, true>(a) : launch_fwd_a<E, D, false>(a);
+  if (a.drop.t) return launch_fwd_a<E, D, false, true>(a);
+  return a.alibi_slopes ? launch_fwd_a<E, D, true, false>(a) : launch_fwd_a<E, D, false, false>(a);
 }
 
 }  // namespace

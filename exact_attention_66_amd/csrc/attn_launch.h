@@ -18,6 +18,16 @@ struct Lay {
 
 inline Lay contiguous_lay(int64_t H, int64_t N, int64_t d) { return Lay{H * N * d, N * d, (int32_t)d, 0}; }
 
+// One dropout draw on P, passed to kernels by value (t == 0: no dropout).
+struct DropCfg {
+  uint32_t t;              // drop threshold in 1/256 steps: bytes below t are dropped
+  uint32_t key0;           // seed, low word
+  uint32_t key1;           // seed, high word
+  uint32_t offset;         // fourth counter word
+  float keep_scale;        // 256 / (256 - t)
+  float log2_keep_scale;   // log2 of keep_scale
+};
+
 struct FwdArgs {
   const void* q;
   const void* k;
@@ -31,6 +41,7 @@ struct FwdArgs {
   hipStream_t stream;
   Lay lq, lk, lv, lo;
   const float* alibi_slopes;   // [H] fp32 device array, or NULL: no position bias
+  DropCfg drop;                // dropout on P (drop.t == 0: none)
 };
 
 struct BwdArgs {
@@ -73,6 +84,7 @@ struct BwdArgs {
   void* vc;
   void* doc;
   const float* alibi_slopes;   // [H] fp32 device array, or NULL (contiguous calls only)
+  DropCfg drop;                // dropout on P (drop.t == 0: none; contiguous calls only)
 };
 
 // Forward for KV-cache shapes: Nq queries against Nk keys, the key axis cut
@@ -133,6 +145,8 @@ int persistent_grid(const void* fn, int block, int units);
 hipError_t launch_fwd(const FwdArgs& a);
 hipError_t launch_bwd(const BwdArgs& a);
 hipError_t launch_kvcache(const KvArgs& a);
+hipError_t launch_dropout_draws(uint8_t* out, int64_t BH, int64_t Nq, int64_t Nk, const DropCfg& drop,
+                                hipStream_t stream);
 
 // Workspace split used by attn_bwd: delta, nlse, then Q^T, K^T, dO^T, then
 // (N not a multiple of 64) the tail tiles of Q, dO, K, V, each part starting

@@ -72,6 +72,7 @@ enum attn_status {
   ATTN_ERR_HIP = 10,                  /* a kernel launch failed; see attn_last_hip_error() */
   ATTN_ERR_BAD_LAYOUT = 11,           /* strides negative, not multiples of 8 elements, token stride
                                          >= 2^24, or an output layout whose elements overlap */
+  ATTN_ERR_BAD_DROPOUT = 12,          /* dropout probability NaN, < 0 or >= 1 */
 };
 
 /*
@@ -275,6 +276,51 @@ int attn_fwd_kvcache_alibi(const void* q, const void* k, const void* v, void* o,
                            int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
                            const float* alibi_slopes, float scale, int causal, int dtype,
                            int num_splits, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Dropout on the attention probabilities, fused into the kernels.
+ *
+ * Source: dropout is one of the elementwise steps the method fuses into the
+ * attention kernel (page "FlashAttention技术解析 如何让GPT训练速度提升5-9倍"
+ * §2.2); the op of page "Flash Attention V2 大模型时代的算力救星" §4.2 takes
+ * a dropout probability.  The pages name no generator; the mask here is
+ * drawn with Philox4x32-10 (Salmon et al., SC 2011) and regenerated, never
+ * stored, by the forward and both backward kernels:
+ *   - the 4 x 4 block of (query row, key row) (4a .. 4a+3, 4b .. 4b+3) of head
+ *     bh = b * H + h is one call with counter (a, b, bh, offset) and key
+ *     (seed & 0xFFFFFFFF, seed >> 32); query 4a + u takes output word u and
+ *     key 4b + c its byte c (least significant byte first);
+ *   - t = attn_dropout_threshold(dropout_p) = floor(256 dropout_p + 1/2),
+ *     at most 255: an element whose byte is below t is dropped (its weight in
+ *     P V is 0), the others are multiplied by 256 / (256 - t).  The effective
+ *     probability is t / 256.
+ *   O = (P o M) V with M the scaled keep mask; lse is that of the softmax
+ *   over all visible keys (dropout does not change it).  The backward with
+ *   the same (dropout_p, seed, offset) differentiates that O.
+ *
+ * attn_dropout_threshold: t for dropout_p, or -1 if dropout_p is NaN, < 0
+ * or >= 1.
+ * attn_fwd_dropout / attn_bwd_dropout: as attn_fwd / attn_bwd (contiguous
+ * tensors, same workspace, same errors) plus the dropout arguments;
+ * ATTN_ERR_BAD_DROPOUT for a dropout_p outside [0, 1).  dropout_p with
+ * t = 0 runs the kernels without dropout.
+ * attn_dropout_draws: writes the 8-bit draws of heads 0 .. BH-1 for query
+ * rows 0 .. Nq-1 and key rows 0 .. Nk-1 to draws (device, uint8,
+ * [BH, Nq, Nk] contiguous, caller-owned); an element is dropped exactly when
+ * its draw is below t.  ATTN_ERR_NULL_PTR, ATTN_ERR_BAD_SHAPE (any size < 1
+ * or too large), ATTN_ERR_HIP.
+ */
+int attn_dropout_threshold(float dropout_p);
+int attn_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal,
+                     int dtype, float dropout_p, uint64_t seed, uint32_t offset, void* stream);
+int attn_bwd_dropout(const void* q, const void* k, const void* v, const void* o,
+                     const void* dO, const float* lse, void* dq, void* dk, void* dv,
+                     int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal,
+                     int dtype, float dropout_p, uint64_t seed, uint32_t offset,
+                     void* workspace, size_t workspace_bytes, void* stream);
+int attn_dropout_draws(uint8_t* draws, int64_t BH, int64_t Nq, int64_t Nk, uint64_t seed,
+                       uint32_t offset, void* stream);
 
 /* Kernels the library launches, as counted by the profiling window below. */
 enum attn_kernel_kind {

@@ -7,6 +7,13 @@ Tolerances (fixed by the parity contract of this library):
        floor of the output format plus 1e-3: |err| <= ulp(O_ref)/2 + 1e-3.
   lse  max|err| <= 1e-3.
   dQ, dK, dV  relative Frobenius error ||G - G_ref|| / ||G_ref|| <= 2e-2 each.
+  With dropout, O = k (sum_j z_j w_j V_j) / (sum_j w_j) with the keep factor
+  k = 256 / (256 - t): every rounding error made before the final
+  multiplication by k is multiplied by k, so the O bounds other than the
+  output rounding floor are scaled by k (check_o's ``gain``).  And k V_j is
+  in general not a 16-bit number (without dropout a row with one visible
+  key returns V_j exactly), so with dropout the mean bound also admits the
+  mean half-ulp of the output format at O_ref.
 """
 from __future__ import annotations
 
@@ -31,16 +38,17 @@ def half_ulp(x: np.ndarray, dtype) -> np.ndarray:
     return 0.5 * np.exp2(e - m)
 
 
-def check_o(o_gpu: np.ndarray, o_ref: np.ndarray, dtype, what: str = "O"):
+def check_o(o_gpu: np.ndarray, o_ref: np.ndarray, dtype, what: str = "O", gain: float = 1.0):
     err = np.abs(o_gpu.astype(np.float64) - o_ref)
     big = np.abs(o_ref) >= 4.0
-    bound = np.where(big, half_ulp(o_ref, dtype) + 1e-3, O_MAX)
+    bound = np.where(big, half_ulp(o_ref, dtype) + 1e-3 * gain, O_MAX * gain)
     worst = float(err.max()) if err.size else 0.0
     mean = float(err.mean()) if err.size else 0.0
     bad = np.argwhere(err > bound)
     assert bad.size == 0, (f"{what}: {len(bad)} elements over bound; worst {worst:.3e} at "
                            f"{tuple(bad[0])} gpu={o_gpu[tuple(bad[0])]} ref={o_ref[tuple(bad[0])]}")
-    assert mean <= O_MEAN, f"{what}: mean|err| {mean:.3e} > {O_MEAN}"
+    mean_bound = O_MEAN * gain + (float(half_ulp(o_ref, dtype).mean()) if gain != 1.0 and err.size else 0.0)
+    assert mean <= mean_bound, f"{what}: mean|err| {mean:.3e} > {mean_bound:.3e}"
     return worst, mean
 
 

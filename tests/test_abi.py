@@ -292,3 +292,26 @@ def test_kvcache_grouped_heads_checks(lib):
     assert call(ws_bytes=10) == WS
     assert call(sl=P[6] + 2) == ALIGN
     assert call(o=P[1]) == ALIAS
+
+
+def test_dropout_entry_points_check_arguments(lib):
+    BAD_DROPOUT = 12
+    assert lib.attn_dropout_threshold(0.0) == 0 and lib.attn_dropout_threshold(0.1) == 26
+    assert lib.attn_dropout_threshold(0.5) == 128 and lib.attn_dropout_threshold(0.9999) == 255
+    for p in (-0.01, 1.0, 2.0, float("nan"), float("inf")):
+        assert lib.attn_dropout_threshold(p) == -1
+        assert lib.attn_fwd_dropout(P[0], P[1], P[2], P[3], P[4], 1, 2, 128, 64, 0.125, 1, 0, p, 1, 0,
+                                    None) == BAD_DROPOUT
+    ws = ea.attn_bwd_workspace_bytes(1, 2, 128, 64)
+    assert lib.attn_bwd_dropout(P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7], P[8], 1, 2, 128, 64, 0.125, 1, 0,
+                                1.5, 1, 0, P[9], ws, None) == BAD_DROPOUT
+    # the checks of attn_fwd / attn_bwd still apply
+    assert lib.attn_fwd_dropout(None, P[1], P[2], P[3], P[4], 1, 2, 128, 64, 0.125, 1, 0, 0.1, 1, 0, None) == 1
+    assert lib.attn_fwd_dropout(P[0], P[1], P[2], P[3], P[4], 1, 2, 128, 48, 0.125, 1, 0, 0.1, 1, 0, None) == 3
+    assert lib.attn_fwd_dropout(P[0], P[1], P[2], P[0], P[4], 1, 2, 128, 64, 0.125, 1, 0, 0.1, 1, 0, None) == 9
+    assert lib.attn_bwd_dropout(P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7], P[8], 1, 2, 128, 64, 0.125, 1, 0,
+                                0.1, 1, 0, P[9], ws - 1, None) == 8
+    # draws: sizes and pointer
+    assert lib.attn_dropout_draws(None, 1, 4, 4, 0, 0, None) == 1
+    for bh, nq, nk in ((0, 4, 4), (1, 0, 4), (1, 4, 0), (1, 1 << 31, 4), (-1, 4, 4)):
+        assert lib.attn_dropout_draws(P[0], bh, nq, nk, 0, 0, None) == 2

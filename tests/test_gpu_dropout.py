@@ -1,0 +1,104 @@
+"""Dropout on P (GPU): the library's draws, forward and backward against the oracle.
+
+The oracle (oracle/philox.py) implements the same published generator and
+mask layout independently; its generator is pinned to the authors'
+known-answer vectors by the CPU tests.  Here:
+
+* attn_dropout_draws equals the oracle's draws byte for byte (integer work:
+  bit-exact), for ragged sizes and several seeds and offsets;
+* O and lse of attn_fwd_dropout, and dQ, dK, dV of attn_bwd_dropout, match
+  the oracle with the same (p, seed, offset) element by element, within the
+  tolerances of the tests without dropout (O's scaled by the keep factor,
+  which multiplies every rounding error made before it);
+* p = 0 gives exactly the results of attn_fwd / attn_bwd, and a different
+  seed gives a different O.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from oracle import philox
+from parity import check_grad, check_lse, check_o, f64, log, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("BH,Nq,Nk,seed,offset", [
+    (1, 1, 1, 0, 0),
+    (3, 37, 101, 12345, 0),
+    (2, 64, 64, 2**63 + 17, 7),
+    (5, 100, 33, 0xDEADBEEFCAFEF00D, 0xFFFFFFFF),
+    (1, 300, 257, 42, 1),
+])
+def test_draws_bit_exact(BH, Nq, Nk, seed, offset):
+    ea = require_gpu()
+    log(f"dropout draws BH={BH} Nq={Nq} Nk={Nk} seed={seed} offset={offset}")
+    got = ea.dropout_draws(BH, Nq, Nk, seed, offset).cpu().numpy()
+    for bh in range(BH):
+        ref = philox.draws(bh, Nq, Nk, seed, offset)
+        bad = np.argwhere(got[bh] != ref)
+        assert bad.size == 0, f"head {bh}: {len(bad)} draws differ, first at {bad[:3].tolist()}"
+
+
+def test_threshold_matches_oracle():
+    ea = require_gpu()
+    for p in (0.0, 0.001, 0.1, 0.25, 0.5, 0.9, 0.999):
+        assert ea.dropout_threshold(p) == philox.dropout_threshold(p)
+    for p in (-0.1, 1.0, float("nan")):
+        with pytest.raises(ValueError):
+            ea.dropout_threshold(p)
+
+
+CASES = [
+    # (B, H, N, d, dtype, causal, p, seed, offset)
+    (1, 2, 128, 128, "bf16", True, 0.1, 1, 0),
+    (2, 2, 256, 64, "bf16", False, 0.2, 77, 3),
+    (1, 3, 200, 128, "fp16", True, 0.5, 2**40 + 9, 0),
+    (1, 1, 77, 64, "fp16", False, 0.1, 5, 11),
+    (2, 1, 333, 128, "bf16", True, 0.3, 123456789, 2),
+    (1, 2, 1, 128, "bf16", True, 0.1, 8, 0),
+    (1, 2, 512, 128, "bf16", True, 0.9, 31, 0),
+]
+
+
+@pytest.mark.parametrize("B,H,N,d,dt,causal,p,seed,offset", CASES,
+                         ids=[f"B{c[0]}H{c[1]}N{c[2]}d{c[3]}{c[4]}{'c' if c[5] else ''}p{c[6]}" for c in CASES])
+def test_dropout_forward_backward_match_oracle(B, H, N, d, dt, causal, p, seed, offset):
+    ea = require_gpu()
+    w = workloads.Workload("drop", B, H, N, d, dt, causal, True, seed=41000 + N + d)
+    x = workloads.make_inputs(w)
+    q, k, v, do = (x[n].cuda() for n in ("q", "k", "v", "do"))
+    log(f"dropout fwd+bwd B={B} H={H} N={N} d={d} {dt} causal={causal} p={p} seed={seed} offset={offset}")
+    o, lse = ea.forward_dropout(q, k, v, p, seed, offset, scale=w.scale, causal=causal)
+    dq, dk, dv = ea.backward_dropout(q, k, v, o, lse, do, p, seed, offset, scale=w.scale, causal=causal)
+    torch.cuda.synchronize()
+    args = [workloads.to_f64_numpy(x[n]) for n in ("q", "k", "v")]
+    o_ref, lse_ref = oracle.forward(*args, w.scale, causal, dropout=(p, seed, offset))
+    eo, _ = check_o(f64(o), o_ref, dt, gain=philox.keep_scale(p))
+    el = check_lse(f64(lse), lse_ref)
+    grads = oracle.backward(*args, workloads.to_f64_numpy(x["do"]), w.scale, causal, dropout=(p, seed, offset))
+    errs = [check_grad(f64(g), gr, name) for name, g, gr in zip(("dQ", "dK", "dV"), (dq, dk, dv), grads)]
+    log(f"  max|dO|={eo:.2e} max|dlse|={el:.2e} grads {errs}")
+
+
+def test_dropout_p_zero_and_seeds():
+    ea = require_gpu()
+    w = workloads.Workload("drop0", 1, 2, 192, 128, "bf16", True, True, seed=41999)
+    x = workloads.make_inputs(w)
+    q, k, v, do = (x[n].cuda() for n in ("q", "k", "v", "do"))
+    o0, l0 = ea.forward(q, k, v, scale=w.scale, causal=True)
+    o1, l1 = ea.forward_dropout(q, k, v, 0.0, 5, 0, scale=w.scale, causal=True)
+    g0 = ea.backward(q, k, v, o0, l0, do, scale=w.scale, causal=True)
+    g1 = ea.backward_dropout(q, k, v, o1, l1, do, 0.0, 5, 0, scale=w.scale, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o0, o1) and torch.equal(l0, l1)
+    for a, b in zip(g0, g1):
+        assert torch.equal(a, b)
+    o2, l2 = ea.forward_dropout(q, k, v, 0.1, 5, 0, scale=w.scale, causal=True)
+    o3, l3 = ea.forward_dropout(q, k, v, 0.1, 6, 0, scale=w.scale, causal=True)
+    o4, _ = ea.forward_dropout(q, k, v, 0.1, 5, 0, scale=w.scale, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(l2, l0) and torch.equal(l3, l0)        # lse is the softmax's own
+    assert not torch.equal(o2, o3) and torch.equal(o2, o4)     # seeds differ; the same seed repeats
