@@ -81,8 +81,9 @@ def measured_traffic(kernel: str, workload: str):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(w: workloads.Workload, x, budget_s: float):
-    """Time the fp64 oracle (as it stands) on whole heads of the workload."""
+def cpu_baseline(w: workloads.Workload, x, budget_s: float, dropout=None):
+    """Time the fp64 oracle (as it stands) on whole heads of the workload;
+    ``dropout``: ``(p, seed, offset)`` or None."""
     import numpy as np
     import oracle
 
@@ -93,10 +94,11 @@ def cpu_baseline(w: workloads.Workload, x, budget_s: float):
     for b in range(w.B):
         for h in range(w.H):
             q, k, v = (workloads.to_f64_numpy(x[n][b, h]) for n in ("q", "k", "v"))
-            oracle.forward_head(q, k, v, w.scale, w.causal, row_block=rb)
+            hd = None if dropout is None else (*dropout, b * w.H + h)
+            oracle.forward_head(q, k, v, w.scale, w.causal, row_block=rb, dropout=hd)
             if w.backward:
                 oracle.backward_head(q, k, v, workloads.to_f64_numpy(x["do"][b, h]), w.scale, w.causal,
-                                     row_block=rb)
+                                     row_block=rb, dropout=hd)
             heads += 1
             flops += per_head
             if time.perf_counter() - t0 >= budget_s:
@@ -349,6 +351,9 @@ def main() -> int:
                          "(reference kernel for scaling the HBM byte counters)")
     ap.add_argument("--alibi", action="store_true",
                     help="run the ALiBi entry points (slopes 2^(-8(h+1)/H)) on the same workload")
+    ap.add_argument("--dropout", type=float, default=0.0, metavar="P",
+                    help="run the dropout entry points with probability P (seed --dropout-seed) on the same workload")
+    ap.add_argument("--dropout-seed", type=int, default=2026)
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU run: turn rocprofv3 FETCH_SIZE / WRITE_SIZE counter files into the "
                          "workload's HBM bytes per launch in profiles/hbm_traffic.json")
@@ -401,6 +406,22 @@ def main() -> int:
                                         ws.numel(), stream)
             if st != 0:
                 raise ea.AttnError(st, "alibi step")
+    elif args.dropout > 0:
+        lib = ea.load()
+        stream = torch.cuda.current_stream().cuda_stream or None
+        dt = ea.ATTN_DTYPE_BF16 if w.dtype == "bf16" else ea.ATTN_DTYPE_FP16
+
+        def step():
+            st = lib.attn_fwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), w.B,
+                                      w.H, w.N, w.d, w.scale, int(w.causal), dt, args.dropout, args.dropout_seed, 0,
+                                      stream)
+            if st == 0 and w.backward:
+                st = lib.attn_bwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                                          lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), w.B, w.H, w.N,
+                                          w.d, w.scale, int(w.causal), dt, args.dropout, args.dropout_seed, 0,
+                                          ws.data_ptr(), ws.numel(), stream)
+            if st != 0:
+                raise ea.AttnError(st, "dropout step")
     else:
         def step():
             ea.attn_fwd(q, k, v, o, lse, w.scale, w.causal)
@@ -433,7 +454,7 @@ def main() -> int:
         "peak": PEAK_TFLOPS,
         "unit": "TFLOP/s",
         "frac": round(achieved / PEAK_TFLOPS, 4),
-        "traffic": None if args.alibi else measured_traffic(dominant, w.name),
+        "traffic": None if (args.alibi or args.dropout > 0) else measured_traffic(dominant, w.name),
     }
 
     line = {
@@ -450,13 +471,15 @@ def main() -> int:
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
-                   "passes": "fwd+bwd" if w.backward else "fwd", "seed": w.seed, "alibi": bool(args.alibi)},
+                   "passes": "fwd+bwd" if w.backward else "fwd", "seed": w.seed, "alibi": bool(args.alibi),
+                   "dropout_p": args.dropout},
         "pct_of_peak": round(100 * value / PEAK_TFLOPS, 2),
         "kernels": kernels,
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, x, args.cpu_baseline_seconds)
+        line["cpu_baseline"] = cpu_baseline(w, x, args.cpu_baseline_seconds,
+                                            (args.dropout, args.dropout_seed, 0) if args.dropout > 0 else None)
     print(json.dumps(line), flush=True)
     return 0
 

@@ -102,3 +102,31 @@ def test_dropout_p_zero_and_seeds():
     torch.cuda.synchronize()
     assert torch.equal(l2, l0) and torch.equal(l3, l0)        # lse is the softmax's own
     assert not torch.equal(o2, o3) and torch.equal(o2, o4)     # seeds differ; the same seed repeats
+
+
+def test_dropout_full_size_headline_sampled_heads():
+    """The 4 x 32 x 4096 x 128 causal bf16 workload with p = 0.1, in the launch configuration the
+    benchmark's dropout run times: O, lse and the three gradients of three whole heads against the oracle."""
+    ea = require_gpu()
+    w = workloads.WORKLOADS[workloads.HEADLINE]
+    p, seed = 0.1, 2026
+    log(f"dropout full size {w.name} p={p} seed={seed}")
+    x = workloads.make_inputs(w)
+    q, k, v, do = (x[n].cuda() for n in ("q", "k", "v", "do"))
+    o, lse = ea.forward_dropout(q, k, v, p, seed, 0, scale=w.scale, causal=w.causal)
+    dq, dk, dv = ea.backward_dropout(q, k, v, o, lse, do, p, seed, 0, scale=w.scale, causal=w.causal)
+    torch.cuda.synchronize()
+    for t in (o, dq, dk, dv):
+        assert torch.isfinite(t).all().item()
+    # sum_j dK_j = 0 holds with dropout too (each row of dS sums to 0)
+    sk = dk.double().sum(dim=2).norm(dim=-1)
+    assert bool((sk <= 2e-2 * dk.double().norm(dim=(2, 3))).all())
+    for b, h in sorted({(0, 0), (w.B // 2, w.H // 3), (w.B - 1, w.H - 1)}):
+        hd = (p, seed, 0, b * w.H + h)
+        args = [workloads.to_f64_numpy(x[n][b, h]) for n in ("q", "k", "v")]
+        o_ref, lse_ref = oracle.forward_head(*args, w.scale, w.causal, dropout=hd)
+        eo, _ = check_o(f64(o[b, h]), o_ref, w.dtype, f"O[{b},{h}]", gain=philox.keep_scale(p))
+        el = check_lse(f64(lse[b, h]), lse_ref, f"lse[{b},{h}]")
+        ref = oracle.backward_head(*args, workloads.to_f64_numpy(x["do"][b, h]), w.scale, w.causal, dropout=hd)
+        errs = [check_grad(f64(g[b, h]), gr, f"{n}[{b},{h}]") for n, g, gr in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref)]
+        log(f"  head ({b},{h}): O {eo:.2e} lse {el:.2e} dQ {errs[0]:.2e} dK {errs[1]:.2e} dV {errs[2]:.2e}")
