@@ -50,7 +50,8 @@ def source_hash(kernel: str) -> str | None:
     path = KERNEL_SOURCES.get(kernel)
     if path is None:
         return None
-    files = [path, "exact_attention_66_amd/csrc/attn_device.h", "exact_attention_66_amd/csrc/attn_launch.h"]
+    files = [path, "exact_attention_66_amd/csrc/attn_device.h", "exact_attention_66_amd/csrc/attn_launch.h",
+             "exact_attention_66_amd/csrc/attn_dropout.h"]
     h = hashlib.sha256()
     for f in files:
         with open(os.path.join(ROOT, f), encoding="utf-8") as fh:
