@@ -269,6 +269,20 @@ __global__ __launch_bounds__(NW * 64, ATTN_FWD_MINW) void fwd_kernel(const typen
 #pragma unroll
       for (int db = 0; db < DB; ++db)
         vf[kk][db] = concat44<E>(E::tr_read(vl + kk * 16 * LV + db * 32), E::tr_read(vl + (kk * 16 + 8) * LV + db * 32));
+    // DROP: this lane's generator call, issued before the MFMAs so that it
+    // can overlap them, is block u = lane % 4 of the quad's four 4 x 4
+    // (query, key) blocks (keys kbk0 + 8u + 4h ..); the quad transpose gives
+    // each lane its own query's word of every block
+    u32x4 dtw[QB];
+    if constexpr (DROP) {
+      const int u = lane & 3;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+        dtw[qb] = quad_transpose(philox4x32_10((uint32_t)(qw0 + qb * 32 + r) >> 2,
+                                               (uint32_t)((kbk0 >> 2) + 2 * u + h), (uint32_t)bh, drop.offset,
+                                               drop.key0, drop.key1),
+                                 u);
+    }
     // ---- S^T = K Q^T
     f32x16 s[QB];
 #pragma unroll
@@ -350,13 +364,7 @@ __global__ __launch_bounds__(NW * 64, ATTN_FWD_MINW) void fwd_kernel(const typen
                               p[8 * kk + 5], p[8 * kk + 6], p[8 * kk + 7]);
       lr_run[qb] += sum8<E>(pf[0][qb], 0.f) + sum8<E>(pf[1][qb], 0.f);
       if constexpr (DROP) {
-        // this lane's generator call is block u = lane % 4 of the quad's
-        // four 4 x 4 (query, key) blocks: keys kbk0 + 8u + 4h ..
-        const int u = lane & 3;
-        const u32x4 tw = quad_transpose(
-            philox4x32_10((uint32_t)(qw0 + qb * 32 + r) >> 2, (uint32_t)((kbk0 >> 2) + 2 * u + h), (uint32_t)bh,
-                          drop.offset, drop.key0, drop.key1),
-            u);
+        const u32x4 tw = dtw[qb];
         const uint32_t add = (256u - drop.t) * 0x00010001u;
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
