@@ -318,6 +318,33 @@ def forward_kvcache(q, k, v, scale: Optional[float] = None, causal: bool = False
     return o, lse
 
 
+def _check_same(q, others, names: str):
+    """The contiguous convenience calls: every tensor of ``others`` has q's [B, H, N, d] shape and dtype."""
+    shape = _shape4(q)
+    for t in others:
+        if tuple(t.shape) != shape or t.dtype != q.dtype:
+            raise ValueError(f"{names} must share shape and dtype")
+    return shape
+
+
+def _check_lse(lse, B: int, H: int, N: int):
+    if tuple(lse.shape) != (B, H, N) or lse.dtype != torch.float32:
+        raise ValueError("lse must be a float32 [B, H, N] tensor")
+
+
+def _check_kv(q, k, v):
+    """KV-cache calls: q [B, H, Nq, d]; k, v [B, Hkv, Nk, d] with q's dtype; returns Hkv, Nk."""
+    B, H, Nq, d = _shape4(q)
+    if k.dim() != 4:
+        raise ValueError("k must be a [B, Hkv, Nk, d] tensor")
+    Hkv, Nk = int(k.shape[1]), int(k.shape[2])
+    if tuple(k.shape) != (B, Hkv, Nk, d) or tuple(v.shape) != (B, Hkv, Nk, d):
+        raise ValueError("k and v must be [B, Hkv, Nk, d] with the batch and head size of q")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k and v must share the dtype")
+    return Hkv, Nk
+
+
 def _slopes(alibi_slopes, H: int, device):
     """The [H] fp32 slopes as a contiguous device tensor."""
     t = torch.as_tensor(alibi_slopes, dtype=torch.float32, device=device).contiguous()
@@ -328,7 +355,7 @@ def _slopes(alibi_slopes, H: int, device):
 
 def forward_alibi(q, k, v, alibi_slopes, scale: Optional[float] = None, causal: bool = False, stream=None):
     """attn_fwd_alibi on contiguous [B, H, N, d] tensors: (o, lse)."""
-    B, H, N, d = _shape4(q)
+    B, H, N, d = _check_same(q, (k, v), "q, k and v")
     scale = default_scale(d) if scale is None else scale
     sl = _slopes(alibi_slopes, H, q.device)
     o = torch.empty_like(q)
@@ -343,7 +370,8 @@ def forward_alibi(q, k, v, alibi_slopes, scale: Optional[float] = None, causal: 
 def backward_alibi(q, k, v, o, lse, dO, alibi_slopes, scale: Optional[float] = None, causal: bool = False,
                    stream=None):
     """attn_bwd_alibi on contiguous tensors: (dq, dk, dv)."""
-    B, H, N, d = _shape4(q)
+    B, H, N, d = _check_same(q, (k, v, o, dO), "q, k, v, o and dO")
+    _check_lse(lse, B, H, N)
     scale = default_scale(d) if scale is None else scale
     sl = _slopes(alibi_slopes, H, q.device)
     ws = torch.empty(attn_bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=q.device)
@@ -367,7 +395,7 @@ def dropout_threshold(dropout_p: float) -> int:
 def forward_dropout(q, k, v, dropout_p: float, seed: int, offset: int = 0, scale: Optional[float] = None,
                     causal: bool = False, stream=None):
     """attn_fwd_dropout on contiguous [B, H, N, d] tensors: (o, lse)."""
-    B, H, N, d = _shape4(q)
+    B, H, N, d = _check_same(q, (k, v), "q, k and v")
     scale = default_scale(d) if scale is None else scale
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
@@ -382,7 +410,8 @@ def forward_dropout(q, k, v, dropout_p: float, seed: int, offset: int = 0, scale
 def backward_dropout(q, k, v, o, lse, dO, dropout_p: float, seed: int, offset: int = 0,
                      scale: Optional[float] = None, causal: bool = False, stream=None):
     """attn_bwd_dropout on contiguous tensors (same dropout arguments as the forward): (dq, dk, dv)."""
-    B, H, N, d = _shape4(q)
+    B, H, N, d = _check_same(q, (k, v, o, dO), "q, k, v, o and dO")
+    _check_lse(lse, B, H, N)
     scale = default_scale(d) if scale is None else scale
     ws = torch.empty(attn_bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=q.device)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
@@ -407,7 +436,9 @@ def forward_kvcache_alibi(q, k, v, alibi_slopes, scale: Optional[float] = None, 
                           num_splits: int = 0, stream=None):
     """attn_fwd_kvcache_alibi on contiguous tensors: (o, lse)."""
     B, H, Nq, d = _shape4(q)
-    Nk = int(k.shape[2])
+    Hkv, Nk = _check_kv(q, k, v)
+    if Hkv != H:
+        raise ValueError("k and v must have q's head count (grouped heads: forward_kvcache_gqa)")
     scale = default_scale(d) if scale is None else scale
     sl = _slopes(alibi_slopes, H, q.device)
     ws = torch.empty(attn_fwd_kvcache_workspace_bytes(B, H, Nq, Nk, d, num_splits), dtype=torch.uint8,
@@ -431,9 +462,7 @@ def forward_kvcache_gqa(q, k, v, scale: Optional[float] = None, causal: bool = F
                         alibi_slopes=None, workspace=None, stream=None):
     """attn_fwd_kvcache_gqa on contiguous q [B,Hq,Nq,d] and k, v [B,Hkv,Nk,d]: (o, lse)."""
     B, Hq, Nq, d = _shape4(q)
-    Hkv, Nk = int(k.shape[1]), int(k.shape[2])
-    if tuple(k.shape) != (B, Hkv, Nk, d) or tuple(v.shape) != (B, Hkv, Nk, d):
-        raise ValueError("k and v must be [B, Hkv, Nk, d] with the batch and head size of q")
+    Hkv, Nk = _check_kv(q, k, v)
     scale = default_scale(d) if scale is None else scale
     sl = None if alibi_slopes is None else _slopes(alibi_slopes, Hq, q.device)
     if workspace is None:
