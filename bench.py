@@ -360,8 +360,10 @@ def main() -> int:
                          "workload's HBM bytes per launch in profiles/hbm_traffic.json")
     args = ap.parse_args()
 
+    # counter records of the dropout instantiations are kept apart from the plain ones
+    traffic_key = args.workload + ("+dropout" if args.dropout > 0 else "")
     if args.record_traffic:
-        return record_traffic(*args.record_traffic, args.workload)
+        return record_traffic(*args.record_traffic, traffic_key)
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this library has no "
@@ -455,7 +457,7 @@ def main() -> int:
         "peak": PEAK_TFLOPS,
         "unit": "TFLOP/s",
         "frac": round(achieved / PEAK_TFLOPS, 4),
-        "traffic": None if (args.alibi or args.dropout > 0) else measured_traffic(dominant, w.name),
+        "traffic": None if args.alibi else measured_traffic(dominant, traffic_key),
     }
 
     line = {
