@@ -46,11 +46,15 @@
 // This file is compiled with MFMA results in VGPRs (the softmax reads them
 // without copies out of AGPRs); the operands read from LDS are steered into
 // AGPRs instead (in_agpr).
-// Two more instantiation flags: STRIDED (the inputs in callers' layouts:
+// Three more instantiation flags: STRIDED (the inputs in callers' layouts:
 // (1) reads them through their strides and writes contiguous copies of Q, K,
 // V, dO that (2) and (3) read, whose epilogues store dQ, dK, dV through
-// their strides) and ALIBI (the linear position bias -m_h |i - j| added to
-// the exponent of P in (2) and (3)).  Without them the code is unchanged.
+// their strides), ALIBI (the linear position bias -m_h |i - j| added to
+// the exponent of P in (2) and (3)) and DROP (dropout on P, regenerated in
+// (2) and (3) from the generator of attn_dropout.h: with the keep factor k,
+// P is computed as k P and dP starts at -D / k, so a kept score's dS is
+// P (k dP - D) and a dropped one's -P D, and dV's operand has the dropped
+// weights cleared).  Without them the code is unchanged.
 #include "attn_device.h"
 #include "attn_dropout.h"
 #include "attn_launch.h"
