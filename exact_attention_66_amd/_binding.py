@@ -30,6 +30,7 @@ EXPORTED = ["attn_fwd", "attn_fwd_strided", "attn_bwd_workspace_bytes", "attn_bw
             "attn_bwd_strided", "attn_bwd_strided_workspace_bytes", "attn_fwd_alibi", "attn_bwd_alibi",
             "attn_fwd_kvcache_alibi", "attn_fwd_kvcache_gqa", "attn_fwd_kvcache_gqa_workspace_bytes",
             "attn_dropout_threshold", "attn_fwd_dropout", "attn_bwd_dropout", "attn_dropout_draws",
+            "attn_fwd_dropout_strided", "attn_bwd_dropout_strided",
             "attn_profile_start",
             "attn_profile_stop", "attn_status_string", "attn_last_hip_error"]
 # attn_kernel_kind values
@@ -103,6 +104,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                      u32, vp, sz, vp]
     lib.attn_bwd_dropout.restype = i32
     lib.attn_dropout_draws.argtypes = [vp, i64, i64, i64, u64, u32, vp]
+    lib.attn_fwd_dropout_strided.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64p, f32, i32, i32, f32, u64,
+                                             u32, vp]
+    lib.attn_fwd_dropout_strided.restype = i32
+    lib.attn_bwd_dropout_strided.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64p, f32, i32,
+                                             i32, f32, u64, u32, vp, sz, vp]
+    lib.attn_bwd_dropout_strided.restype = i32
     lib.attn_dropout_draws.restype = i32
     lib.attn_profile_start.argtypes = []
     lib.attn_profile_start.restype = i32
@@ -319,7 +326,7 @@ def forward_kvcache(q, k, v, scale: Optional[float] = None, causal: bool = False
 
 
 def _check_same(q, others, names: str):
-    """The contiguous convenience calls: every tensor of ``others`` has q's [B, H, N, d] shape and dtype."""
+    """The convenience calls: every tensor of ``others`` has q's [B, H, N, d] shape and dtype."""
     shape = _shape4(q)
     for t in others:
         if tuple(t.shape) != shape or t.dtype != q.dtype:
@@ -394,14 +401,21 @@ def dropout_threshold(dropout_p: float) -> int:
 
 def forward_dropout(q, k, v, dropout_p: float, seed: int, offset: int = 0, scale: Optional[float] = None,
                     causal: bool = False, stream=None):
-    """attn_fwd_dropout on contiguous [B, H, N, d] tensors: (o, lse)."""
+    """attn_fwd_dropout on [B, H, N, d] tensors (other layouts, e.g. transposed [B, N, H, d] views, through
+    attn_fwd_dropout_strided; o takes q's layout): (o, lse)."""
     B, H, N, d = _check_same(q, (k, v), "q, k and v")
     scale = default_scale(d) if scale is None else scale
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    st = load().attn_fwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, float(scale),
-                                 int(bool(causal)), _dtype_code(q), float(dropout_p), int(seed), int(offset),
-                                 _stream(stream))
+    if _all_contiguous(q, k, v, o):
+        st = load().attn_fwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, float(scale),
+                                     int(bool(causal)), _dtype_code(q), float(dropout_p), int(seed), int(offset),
+                                     _stream(stream))
+    else:
+        st = load().attn_fwd_dropout_strided(_strided_ptr(q), _strided_ptr(k), _strided_ptr(v), _strided_ptr(o),
+                                             _ptr(lse), B, H, N, d, _strides12(q, k, v, o), float(scale),
+                                             int(bool(causal)), _dtype_code(q), float(dropout_p), int(seed),
+                                             int(offset), _stream(stream))
     if st != ATTN_OK:
         raise AttnError(st, "attn_fwd_dropout")
     return o, lse
@@ -409,15 +423,25 @@ def forward_dropout(q, k, v, dropout_p: float, seed: int, offset: int = 0, scale
 
 def backward_dropout(q, k, v, o, lse, dO, dropout_p: float, seed: int, offset: int = 0,
                      scale: Optional[float] = None, causal: bool = False, stream=None):
-    """attn_bwd_dropout on contiguous tensors (same dropout arguments as the forward): (dq, dk, dv)."""
+    """attn_bwd_dropout (same dropout arguments as the forward; other layouts through
+    attn_bwd_dropout_strided, gradients in the layouts of q, k, v): (dq, dk, dv)."""
     B, H, N, d = _check_same(q, (k, v, o, dO), "q, k, v, o and dO")
     _check_lse(lse, B, H, N)
     scale = default_scale(d) if scale is None else scale
-    ws = torch.empty(attn_bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=q.device)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    st = load().attn_bwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse), _ptr(dq), _ptr(dk),
-                                 _ptr(dv), B, H, N, d, float(scale), int(bool(causal)), _dtype_code(q),
-                                 float(dropout_p), int(seed), int(offset), _ptr(ws), ws.numel(), _stream(stream))
+    ts = (q, k, v, o, dO, dq, dk, dv)
+    if _all_contiguous(*ts):
+        ws = torch.empty(attn_bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=q.device)
+        st = load().attn_bwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse), _ptr(dq), _ptr(dk),
+                                     _ptr(dv), B, H, N, d, float(scale), int(bool(causal)), _dtype_code(q),
+                                     float(dropout_p), int(seed), int(offset), _ptr(ws), ws.numel(),
+                                     _stream(stream))
+    else:
+        ws = torch.empty(attn_bwd_strided_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=q.device)
+        st = load().attn_bwd_dropout_strided(*(_strided_ptr(t) for t in ts[:5]), _ptr(lse),
+                                             *(_strided_ptr(t) for t in ts[5:]), B, H, N, d, _strides12(*ts),
+                                             float(scale), int(bool(causal)), _dtype_code(q), float(dropout_p),
+                                             int(seed), int(offset), _ptr(ws), ws.numel(), _stream(stream))
     if st != ATTN_OK:
         raise AttnError(st, "attn_bwd_dropout")
     return dq, dk, dv

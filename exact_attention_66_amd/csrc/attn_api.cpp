@@ -474,6 +474,35 @@ int attn_bwd_dropout(const void* q, const void* k, const void* v, const void* o,
                   workspace_bytes, stream, nullptr, &c);
 }
 
+int attn_fwd_dropout_strided(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                             int64_t H, int64_t N, int64_t d, const int64_t* strides, float scale, int causal,
+                             int dtype, float dropout_p, uint64_t seed, uint32_t offset, void* stream) {
+  if (!strides) return ATTN_ERR_NULL_PTR;
+  for (int i = 0; i < 12; ++i)
+    if (strides[i] < 0 || strides[i] > ((int64_t)1 << 40)) return ATTN_ERR_BAD_LAYOUT;
+  attn::DropCfg c{};
+  const int st = make_drop(dropout_p, seed, offset, &c);
+  if (st != ATTN_OK) return st;
+  const attn::Lay lays[4] = {lay_from(strides), lay_from(strides + 3), lay_from(strides + 6), lay_from(strides + 9)};
+  return fwd_impl(q, k, v, o, lse, B, H, N, d, lays, scale, causal, dtype, stream, nullptr, &c);
+}
+
+int attn_bwd_dropout_strided(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                             const float* lse, void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N,
+                             int64_t d, const int64_t* strides, float scale, int causal, int dtype, float dropout_p,
+                             uint64_t seed, uint32_t offset, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!strides) return ATTN_ERR_NULL_PTR;
+  for (int i = 0; i < 24; ++i)
+    if (strides[i] < 0 || strides[i] > ((int64_t)1 << 40)) return ATTN_ERR_BAD_LAYOUT;
+  attn::DropCfg c{};
+  const int st = make_drop(dropout_p, seed, offset, &c);
+  if (st != ATTN_OK) return st;
+  attn::Lay lays[8];
+  for (int i = 0; i < 8; ++i) lays[i] = lay_from(strides + 3 * i);
+  return bwd_impl(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, lays, true, scale, causal, dtype, workspace,
+                  workspace_bytes, stream, nullptr, &c);
+}
+
 int attn_dropout_draws(uint8_t* draws, int64_t BH, int64_t Nq, int64_t Nk, uint64_t seed, uint32_t offset,
                        void* stream) {
   if (!draws) return ATTN_ERR_NULL_PTR;

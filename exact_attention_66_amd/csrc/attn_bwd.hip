@@ -1107,11 +1107,11 @@ hipError_t launch_bwd_s(const BwdArgs& a) {
   return launch_bwd_cfg<E, D, false, true, STRIDED, ALIBI, DROP>(a);
 }
 
-// ALiBi and dropout calls are contiguous and never combined (the C ABI has
-// no entry point that takes two of strides, slopes and dropout)
+// ALiBi calls are contiguous, and ALiBi and dropout are never combined (no
+// entry point of the C ABI takes both)
 template <typename E, int D>
 hipError_t launch_bwd_d(const BwdArgs& a) {
-  if (a.drop.t) return launch_bwd_s<E, D, false, false, true>(a);
+  if (a.drop.t) return a.strided ? launch_bwd_s<E, D, true, false, true>(a) : launch_bwd_s<E, D, false, false, true>(a);
   if (a.alibi_slopes) return launch_bwd_s<E, D, false, true>(a);
   return a.strided ? launch_bwd_s<E, D, true, false>(a) : launch_bwd_s<E, D, false, false>(a);
 }

@@ -84,7 +84,7 @@ struct BwdArgs {
   void* vc;
   void* doc;
   const float* alibi_slopes;   // [H] fp32 device array, or NULL (contiguous calls only)
-  DropCfg drop;                // dropout on P (drop.t == 0: none; contiguous calls only)
+  DropCfg drop;                // dropout on P (drop.t == 0: none)
 };
 
 // Forward for KV-cache shapes: Nq queries against Nk keys, the key axis cut

@@ -301,7 +301,8 @@ int attn_fwd_kvcache_alibi(const void* q, const void* k, const void* v, void* o,
  * attn_dropout_threshold: t for dropout_p, or -1 if dropout_p is NaN, < 0
  * or >= 1.
  * attn_fwd_dropout / attn_bwd_dropout: as attn_fwd / attn_bwd (contiguous
- * tensors, same workspace, same errors) plus the dropout arguments;
+ * tensors, same workspace, same errors) plus the dropout arguments; the
+ * mask depends on (batch, head, query row, key row), not on the layout;
  * ATTN_ERR_BAD_DROPOUT for a dropout_p outside [0, 1).  dropout_p with
  * t = 0 runs the kernels without dropout.
  * attn_dropout_draws: writes the 8-bit draws of heads 0 .. BH-1 for query
@@ -321,6 +322,19 @@ int attn_bwd_dropout(const void* q, const void* k, const void* v, const void* o,
                      void* workspace, size_t workspace_bytes, void* stream);
 int attn_dropout_draws(uint8_t* draws, int64_t BH, int64_t Nq, int64_t Nk, uint64_t seed,
                        uint32_t offset, void* stream);
+/* attn_fwd_dropout_strided / attn_bwd_dropout_strided: the same on tensors in
+ * any [B, H, N, d] layout with a contiguous head dimension, strides and
+ * layout rules as for attn_fwd_strided / attn_bwd_strided (12 and 24
+ * strides; the backward's workspace is attn_bwd_strided_workspace_bytes). */
+int attn_fwd_dropout_strided(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int64_t B, int64_t H, int64_t N, int64_t d, const int64_t* strides,
+                             float scale, int causal, int dtype, float dropout_p, uint64_t seed,
+                             uint32_t offset, void* stream);
+int attn_bwd_dropout_strided(const void* q, const void* k, const void* v, const void* o,
+                             const void* dO, const float* lse, void* dq, void* dk, void* dv,
+                             int64_t B, int64_t H, int64_t N, int64_t d, const int64_t* strides,
+                             float scale, int causal, int dtype, float dropout_p, uint64_t seed,
+                             uint32_t offset, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Kernels the library launches, as counted by the profiling window below. */
 enum attn_kernel_kind {

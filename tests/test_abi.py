@@ -311,6 +311,20 @@ def test_dropout_entry_points_check_arguments(lib):
     assert lib.attn_fwd_dropout(P[0], P[1], P[2], P[0], P[4], 1, 2, 128, 64, 0.125, 1, 0, 0.1, 1, 0, None) == 9
     assert lib.attn_bwd_dropout(P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7], P[8], 1, 2, 128, 64, 0.125, 1, 0,
                                 0.1, 1, 0, P[9], ws - 1, None) == 8
+    # strided variants: strides required, then the same checks
+    st12 = (ctypes.c_int64 * 12)(*([2 * 128 * 64, 128 * 64, 64] * 4))
+    st24 = (ctypes.c_int64 * 24)(*([2 * 128 * 64, 128 * 64, 64] * 8))
+    assert lib.attn_fwd_dropout_strided(P[0], P[1], P[2], P[3], P[4], 1, 2, 128, 64, None, 0.125, 1, 0, 0.1, 1, 0,
+                                        None) == 1
+    assert lib.attn_fwd_dropout_strided(P[0], P[1], P[2], P[3], P[4], 1, 2, 128, 64, st12, 0.125, 1, 0, 1.0, 1, 0,
+                                        None) == BAD_DROPOUT
+    wss = ea.attn_bwd_strided_workspace_bytes(1, 2, 128, 64)
+    assert lib.attn_bwd_dropout_strided(P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7], P[8], 1, 2, 128, 64, None,
+                                        0.125, 1, 0, 0.1, 1, 0, P[9], wss, None) == 1
+    assert lib.attn_bwd_dropout_strided(P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7], P[8], 1, 2, 128, 64, st24,
+                                        0.125, 1, 0, -0.5, 1, 0, P[9], wss, None) == BAD_DROPOUT
+    assert lib.attn_bwd_dropout_strided(P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7], P[8], 1, 2, 128, 64, st24,
+                                        0.125, 1, 0, 0.1, 1, 0, P[9], wss - 1, None) == 8
     # draws: sizes and pointer
     assert lib.attn_dropout_draws(None, 1, 4, 4, 0, 0, None) == 1
     for bh, nq, nk in ((0, 4, 4), (1, 0, 4), (1, 4, 0), (1, 1 << 31, 4), (-1, 4, 4)):

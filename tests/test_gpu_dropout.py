@@ -130,3 +130,34 @@ def test_dropout_full_size_headline_sampled_heads():
         ref = oracle.backward_head(*args, workloads.to_f64_numpy(x["do"][b, h]), w.scale, w.causal, dropout=hd)
         errs = [check_grad(f64(g[b, h]), gr, f"{n}[{b},{h}]") for n, g, gr in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref)]
         log(f"  head ({b},{h}): O {eo:.2e} lse {el:.2e} dQ {errs[0]:.2e} dK {errs[1]:.2e} dV {errs[2]:.2e}")
+
+
+@pytest.mark.parametrize("N,d,causal", [(200, 128, True), (130, 64, False)])
+def test_dropout_token_major_layout(N, d, causal):
+    """[B, N, H, d] tensors (as transposed views) through the strided entry points: the mask is that of
+    (batch, head, query, key), so the results equal the contiguous call's and match the oracle."""
+    ea = require_gpu()
+    w = workloads.Workload("drop_nhd", 2, 3, N, d, "bf16", causal, True, seed=42000 + N)
+    x = workloads.make_inputs(w)
+    p, seed, offset = 0.2, 99, 5
+    log(f"dropout token-major B=2 H=3 N={N} d={d} causal={causal}")
+    cont = {n: x[n].cuda() for n in ("q", "k", "v", "do")}
+    nhd = {n: x[n].transpose(1, 2).contiguous().cuda().transpose(1, 2) for n in ("q", "k", "v", "do")}
+    assert not nhd["q"].is_contiguous()
+    o1, l1 = ea.forward_dropout(cont["q"], cont["k"], cont["v"], p, seed, offset, scale=w.scale, causal=causal)
+    o2, l2 = ea.forward_dropout(nhd["q"], nhd["k"], nhd["v"], p, seed, offset, scale=w.scale, causal=causal)
+    g1 = ea.backward_dropout(cont["q"], cont["k"], cont["v"], o1, l1, cont["do"], p, seed, offset, scale=w.scale,
+                             causal=causal)
+    g2 = ea.backward_dropout(nhd["q"], nhd["k"], nhd["v"], o2, l2, nhd["do"], p, seed, offset, scale=w.scale,
+                             causal=causal)
+    torch.cuda.synchronize()
+    assert o2.stride() == nhd["q"].stride()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    args = [workloads.to_f64_numpy(x[n]) for n in ("q", "k", "v")]
+    o_ref, lse_ref = oracle.forward(*args, w.scale, causal, dropout=(p, seed, offset))
+    check_o(f64(o2), o_ref, "bf16", gain=philox.keep_scale(p))
+    check_lse(f64(l2), lse_ref)
+    grads = oracle.backward(*args, workloads.to_f64_numpy(x["do"]), w.scale, causal, dropout=(p, seed, offset))
+    for name, a, b, gr in zip(("dQ", "dK", "dV"), g1, g2, grads):
+        check_grad(f64(b), gr, name)
+        assert torch.equal(a, b), f"{name}: token-major result differs from the contiguous one"
