@@ -161,3 +161,32 @@ def test_dropout_token_major_layout(N, d, causal):
     for name, a, b, gr in zip(("dQ", "dK", "dV"), g1, g2, grads):
         check_grad(f64(b), gr, name)
         assert torch.equal(a, b), f"{name}: token-major result differs from the contiguous one"
+
+
+def test_dropout_extreme_probability():
+    """p = 0.999 (t = 255, keep factor 256): rows whose visible keys are all dropped give O = 0 exactly,
+    the rest match the oracle, and the gradients stay finite and match."""
+    ea = require_gpu()
+    w = workloads.Workload("drop_hi", 1, 2, 300, 64, "bf16", True, True, seed=43001)
+    x = workloads.make_inputs(w)
+    q, k, v, do = (x[n].cuda() for n in ("q", "k", "v", "do"))
+    p, seed = 0.999, 3
+    assert philox.dropout_threshold(p) == 255
+    log("dropout p=0.999 B=1 H=2 N=300 d=64 causal")
+    o, lse = ea.forward_dropout(q, k, v, p, seed, 0, scale=w.scale, causal=True)
+    dq, dk, dv = ea.backward_dropout(q, k, v, o, lse, do, p, seed, 0, scale=w.scale, causal=True)
+    torch.cuda.synchronize()
+    args = [workloads.to_f64_numpy(x[n]) for n in ("q", "k", "v")]
+    o_ref, lse_ref = oracle.forward(*args, w.scale, True, dropout=(p, seed, 0))
+    n_zero = 0
+    for h in range(2):
+        keep = np.tril(philox.keep_mask(h, 300, 300, p, seed, 0))
+        empty = ~keep.any(axis=1)
+        n_zero += int(empty.sum())
+        assert (o[0, h][torch.from_numpy(empty).cuda()] == 0).all().item()
+    assert n_zero > 0
+    check_o(f64(o), o_ref, "bf16", gain=philox.keep_scale(p))
+    check_lse(f64(lse), lse_ref)
+    grads = oracle.backward(*args, workloads.to_f64_numpy(x["do"]), w.scale, True, dropout=(p, seed, 0))
+    for name, g, gr in zip(("dQ", "dK", "dV"), (dq, dk, dv), grads):
+        check_grad(f64(g), gr, name)
