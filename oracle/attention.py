@@ -80,22 +80,25 @@ def _f64(x) -> np.ndarray:
 
 
 def masked_scores(q, k, scale: float, causal: bool, rows: Optional[np.ndarray] = None,
-                  alibi_slope: Optional[float] = None) -> np.ndarray:
+                  alibi_slope: Optional[float] = None, nk_total: Optional[int] = None) -> np.ndarray:
     """S = scale * Q K^T for the given query rows (all rows by default).
 
     Causal reading: query i sees keys j <= i + (Nk - Nq), i.e. j <= i
     (top-left, diagonal kept) when Q and K have the same number of rows, and
     the queries are the last Nq positions otherwise; every other entry is -inf.
+    ``k`` may hold only the first keys of a longer sequence of ``nk_total``
+    keys (positions are those of the whole sequence).
     """
     q = _f64(q)
     k = _f64(k)
     n = q.shape[0]
+    nk = k.shape[0] if nk_total is None else int(nk_total)
     if rows is None:
         rows = np.arange(n)
     rows = np.asarray(rows, dtype=np.int64)
     s = float(scale) * (q[rows] @ k.T)
     cols = np.arange(k.shape[0])
-    pos = rows[:, None] + (k.shape[0] - n)       # the queries' positions in the key sequence
+    pos = rows[:, None] + (nk - n)       # the queries' positions in the key sequence
     if alibi_slope is not None:
         s = s - float(alibi_slope) * np.abs(pos - cols[None, :])
     if causal:
@@ -121,16 +124,31 @@ def dropout_factor(rows, nq: int, nk: int, dropout) -> Optional[np.ndarray]:
     return z * philox.keep_scale(p)
 
 
+def visible_keys(rows, nq: int, nk: int, causal: bool) -> int:
+    """Number of leading keys any of the listed query rows may see.
+
+    Causal query i sees keys j <= i + (nk - nq), so keys past the largest such
+    bound carry weight exp(-inf) = 0 in every listed row and are left out of
+    the sums; that changes no value, only the length of zero tails.  Without
+    the mask every key is visible."""
+    if not causal or len(rows) == 0:
+        return nk
+    return int(min(nk, max(1, int(np.max(rows)) + (nk - nq) + 1)))
+
+
 def forward_head_rows(q, k, v, scale: float, causal: bool, rows, alibi_slope=None,
                       dropout=None) -> Tuple[np.ndarray, np.ndarray]:
     """O and lse of the listed query rows of one head (each row is independent).
 
     With dropout the probabilities are multiplied by the keep factor before
     the product with V; lse stays that of the softmax itself."""
-    s = masked_scores(q, k, scale, causal, rows, alibi_slope)
+    nq, nk = np.shape(q)[0], np.shape(k)[0]
+    rows = np.asarray(rows, dtype=np.int64)
+    kv = visible_keys(rows, nq, nk, causal)
+    s = masked_scores(q, _f64(k)[:kv], scale, causal, rows, alibi_slope, nk_total=nk)
     p, m, l = row_softmax(s)
-    zf = dropout_factor(rows, np.shape(q)[0], np.shape(k)[0], dropout)
-    o = (p if zf is None else p * zf) @ _f64(v)
+    zf = dropout_factor(rows, nq, nk, dropout)
+    o = (p if zf is None else p * zf[:, :kv]) @ _f64(v)[:kv]
     lse = m + np.log(l)
     return o, lse
 
@@ -174,19 +192,23 @@ def backward_head(q, k, v, do, scale: float, causal: bool, row_block: Optional[i
     dq = np.empty_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
+    nk = k.shape[0]
     for r0 in range(0, n, rb):
         rows = np.arange(r0, min(n, r0 + rb))
-        s = masked_scores(q, k, scale, causal, rows, alibi_slope)
+        kv = visible_keys(rows, n, nk, causal)   # keys past kv have P = 0 in these rows
+        s = masked_scores(q, k[:kv], scale, causal, rows, alibi_slope, nk_total=nk)
         p, _, _ = row_softmax(s)
-        zf = dropout_factor(rows, n, k.shape[0], dropout)
-        dv += (p if zf is None else p * zf).T @ do[rows]
-        dp = do[rows] @ v.T
+        zf = dropout_factor(rows, n, nk, dropout)
+        if zf is not None:
+            zf = zf[:, :kv]
+        dv[:kv] += (p if zf is None else p * zf).T @ do[rows]
+        dp = do[rows] @ v[:kv].T
         if zf is not None:
             dp = dp * zf
         dsum = (p * dp).sum(axis=1)          # D_i = sum_j P_ij dP_ij
         ds = p * (dp - dsum[:, None])
-        dq[rows] = float(scale) * (ds @ k)
-        dk += float(scale) * (ds.T @ q[rows])
+        dq[rows] = float(scale) * (ds @ k[:kv])
+        dk[:kv] += float(scale) * (ds.T @ q[rows])
     return dq, dk, dv
 
 

@@ -179,3 +179,65 @@ def _planted_bwd(kind):
 def test_planted_dropout_mistake_is_caught(kind):
     fwd = lambda q, k, v: A.forward_head(q, k, v, 0.7, False, dropout=DROP)[0]
     assert _fd_check(fwd, _planted_bwd(kind), False, 6, 7, 3) > 1e-3
+
+
+def _pin_head_index(fwd, bwd):
+    """Head (b, h) of a [B, H, ...] call draws its mask with generator index
+    b * H + h.  With V (and dO) the identity, O[i, j] = P_ij F_ij and
+    dV[j, i] = P_ij F_ij, so the zeros of O and of dV^T are exactly the
+    dropped positions; every head's pattern is compared with the generator's
+    draws at that index.  Non-causal with distinct scores, so P_ij > 0."""
+    B, H, n = 2, 3, 12
+    p, seed, off = 0.5, 0x1F2E3D4C5B6A7988, 11
+    t = philox.dropout_threshold(p)
+    rng = np.random.default_rng(21)
+    q = rng.standard_normal((B, H, n, 4))
+    k = rng.standard_normal((B, H, n, 4))
+    eye = np.broadcast_to(np.eye(n), (B, H, n, n)).copy()
+    o, _ = fwd(q, k, eye, 0.5, False, dropout=(p, seed, off))
+    _, _, dv = bwd(q, k, eye, eye, 0.5, False, dropout=(p, seed, off))
+    for b in range(B):
+        for h in range(H):
+            dropped = philox.draws(b * H + h, n, n, seed, off) < t
+            assert 0 < dropped.mean() < 1
+            assert np.array_equal(o[b, h] == 0.0, dropped), (b, h)
+            assert np.array_equal(dv[b, h].T == 0.0, dropped), (b, h)
+
+
+def test_multihead_dropout_uses_head_index_b_times_H_plus_h():
+    _pin_head_index(oracle.forward, oracle.backward)
+
+
+@pytest.mark.parametrize("index", ["h*B+b", "h", "b"])
+def test_planted_head_index_mistake_is_caught(index, monkeypatch):
+    """A wrapper that numbers heads any other way fails the pin above."""
+    def wrong(dropout, bi, hi, nh):
+        if dropout is None:
+            return None
+        nb = 2   # the pin's batch size
+        idx = {"h*B+b": hi * nb + bi, "h": hi, "b": bi}[index]
+        return (dropout[0], dropout[1], dropout[2], idx)
+    monkeypatch.setattr(A, "_head_dropout", wrong)
+    with pytest.raises(AssertionError):
+        _pin_head_index(A.forward, A.backward)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("nq,nk", [(13, 13), (9, 29)])
+@pytest.mark.parametrize("drop", [None, (0.3, 5, 1, 2)])
+def test_row_blocks_equal_unblocked_kv_shapes_and_dropout(causal, nq, nk, drop):
+    """Evaluating rows in blocks (which leaves out keys no row of a causal
+    block may see) gives the values of the unblocked evaluation."""
+    rng = np.random.default_rng(31 + nq + nk)
+    q = rng.standard_normal((nq, 5))
+    k = rng.standard_normal((nk, 5))
+    v = rng.standard_normal((nk, 3))
+    do = rng.standard_normal((nq, 3))
+    o1, l1 = A.forward_head(q, k, v, 0.6, causal, dropout=drop)
+    o2, l2 = A.forward_head(q, k, v, 0.6, causal, row_block=4, dropout=drop)
+    np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(l1, l2, rtol=0, atol=1e-13)
+    g1 = A.backward_head(q, k, v, do, 0.6, causal, dropout=drop)
+    g2 = A.backward_head(q, k, v, do, 0.6, causal, row_block=4, dropout=drop)
+    for a, b in zip(g1, g2):
+        np.testing.assert_allclose(a, b, rtol=0, atol=1e-12)
