@@ -7,6 +7,7 @@ is no fallback of any kind when the library is missing or a call fails.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from typing import Optional
@@ -281,6 +282,22 @@ def attn_fwd_kvcache(q, k, v, o, lse, scale: float, causal: bool, workspace, num
 
 
 # ------------------------------------------------------------------ conveniences
+# Each convenience call allocates its outputs and temporaries (workspace,
+# slopes) on the stream its kernels are enqueued on: torch's caching
+# allocator ties a block to the stream it was allocated on, so a temporary
+# freed when the call returns is only handed out again to work ordered after
+# the kernels on that stream.  (Allocated on the current stream while the
+# kernels ran on another, it could be reused and overwritten by work on the
+# current stream while those kernels still read it.)
+def _on_stream(stream, device):
+    """Context in which allocations and the kernel launch share the kernels' stream."""
+    if stream is None:
+        return contextlib.nullcontext()
+    if not isinstance(stream, torch.cuda.Stream):
+        stream = torch.cuda.ExternalStream(int(stream), device=device)
+    return torch.cuda.stream(stream)
+
+
 def default_scale(d: int) -> float:
     """fp32(1/sqrt(d)), the default softmax scale."""
     return float(torch.tensor(d, dtype=torch.float32).rsqrt().item())
@@ -288,41 +305,44 @@ def default_scale(d: int) -> float:
 
 def forward(q, k, v, scale: Optional[float] = None, causal: bool = False, stream=None):
     """Allocate (o, lse) with torch on q's device and run attn_fwd."""
-    B, H, N, d = _shape4(q)
-    scale = default_scale(d) if scale is None else scale
-    o = torch.empty_like(q)
-    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    attn_fwd(q, k, v, o, lse, scale, causal, stream)
-    return o, lse
+    with _on_stream(stream, q.device):
+        B, H, N, d = _shape4(q)
+        scale = default_scale(d) if scale is None else scale
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+        attn_fwd(q, k, v, o, lse, scale, causal, stream)
+        return o, lse
 
 
 def backward(q, k, v, o, lse, dO, scale: Optional[float] = None, causal: bool = False, workspace=None,
              stream=None):
     """Allocate (dq, dk, dv) and, if not given, the workspace; run attn_bwd."""
-    B, H, N, d = _shape4(q)
-    scale = default_scale(d) if scale is None else scale
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    if workspace is None:
-        nbytes = (attn_bwd_workspace_bytes(B, H, N, d) if _all_contiguous(q, k, v, o, dO, dq, dk, dv)
-                  else attn_bwd_strided_workspace_bytes(B, H, N, d))
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
-    attn_bwd(q, k, v, o, dO, lse, dq, dk, dv, scale, causal, workspace, stream)
-    return dq, dk, dv
+    with _on_stream(stream, q.device):
+        B, H, N, d = _shape4(q)
+        scale = default_scale(d) if scale is None else scale
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        if workspace is None:
+            nbytes = (attn_bwd_workspace_bytes(B, H, N, d) if _all_contiguous(q, k, v, o, dO, dq, dk, dv)
+                      else attn_bwd_strided_workspace_bytes(B, H, N, d))
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+        attn_bwd(q, k, v, o, dO, lse, dq, dk, dv, scale, causal, workspace, stream)
+        return dq, dk, dv
 
 
 def forward_kvcache(q, k, v, scale: Optional[float] = None, causal: bool = False, num_splits: int = 0,
                     workspace=None, stream=None):
     """Allocate (o, lse) and, if not given, the workspace; run attn_fwd_kvcache."""
-    B, H, Nq, d = _shape4(q)
-    Nk = int(k.shape[2])
-    scale = default_scale(d) if scale is None else scale
-    if workspace is None:
-        workspace = torch.empty(attn_fwd_kvcache_workspace_bytes(B, H, Nq, Nk, d, num_splits), dtype=torch.uint8,
-                                device=q.device)
-    o = torch.empty_like(q)
-    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
-    attn_fwd_kvcache(q, k, v, o, lse, scale, causal, workspace, num_splits, stream)
-    return o, lse
+    with _on_stream(stream, q.device):
+        B, H, Nq, d = _shape4(q)
+        Nk = int(k.shape[2])
+        scale = default_scale(d) if scale is None else scale
+        if workspace is None:
+            workspace = torch.empty(attn_fwd_kvcache_workspace_bytes(B, H, Nq, Nk, d, num_splits), dtype=torch.uint8,
+                                    device=q.device)
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+        attn_fwd_kvcache(q, k, v, o, lse, scale, causal, workspace, num_splits, stream)
+        return o, lse
 
 
 def _check_same(q, others, names: str):
@@ -362,40 +382,42 @@ def _slopes(alibi_slopes, H: int, device):
 
 def forward_alibi(q, k, v, alibi_slopes, scale: Optional[float] = None, causal: bool = False, stream=None):
     """attn_fwd_alibi on contiguous [B, H, N, d] tensors: (o, lse)."""
-    B, H, N, d = _check_same(q, (k, v), "q, k and v")
-    scale = default_scale(d) if scale is None else scale
-    sl = _slopes(alibi_slopes, H, q.device)
-    o = torch.empty_like(q)
-    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    st = load().attn_fwd_alibi(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, _ptr(sl), float(scale),
-                               int(bool(causal)), _dtype_code(q), _stream(stream))
-    if st != ATTN_OK:
-        raise AttnError(st, "attn_fwd_alibi")
-    return o, lse
+    with _on_stream(stream, q.device):
+        B, H, N, d = _check_same(q, (k, v), "q, k and v")
+        scale = default_scale(d) if scale is None else scale
+        sl = _slopes(alibi_slopes, H, q.device)
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+        st = load().attn_fwd_alibi(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, _ptr(sl), float(scale),
+                                   int(bool(causal)), _dtype_code(q), _stream(stream))
+        if st != ATTN_OK:
+            raise AttnError(st, "attn_fwd_alibi")
+        return o, lse
 
 
 def backward_alibi(q, k, v, o, lse, dO, alibi_slopes, scale: Optional[float] = None, causal: bool = False,
                    stream=None):
     """attn_bwd_alibi on contiguous tensors: (dq, dk, dv)."""
-    B, H, N, d = _check_same(q, (k, v, o, dO), "q, k, v, o and dO")
-    _check_lse(lse, B, H, N)
-    scale = default_scale(d) if scale is None else scale
-    sl = _slopes(alibi_slopes, H, q.device)
-    ws = torch.empty(attn_bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=q.device)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    st = load().attn_bwd_alibi(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
-                               B, H, N, d, _ptr(sl), float(scale), int(bool(causal)), _dtype_code(q), _ptr(ws),
-                               ws.numel(), _stream(stream))
-    if st != ATTN_OK:
-        raise AttnError(st, "attn_bwd_alibi")
-    return dq, dk, dv
+    with _on_stream(stream, q.device):
+        B, H, N, d = _check_same(q, (k, v, o, dO), "q, k, v, o and dO")
+        _check_lse(lse, B, H, N)
+        scale = default_scale(d) if scale is None else scale
+        sl = _slopes(alibi_slopes, H, q.device)
+        ws = torch.empty(attn_bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=q.device)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        st = load().attn_bwd_alibi(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                                   B, H, N, d, _ptr(sl), float(scale), int(bool(causal)), _dtype_code(q), _ptr(ws),
+                                   ws.numel(), _stream(stream))
+        if st != ATTN_OK:
+            raise AttnError(st, "attn_bwd_alibi")
+        return dq, dk, dv
 
 
 def dropout_threshold(dropout_p: float) -> int:
     """attn_dropout_threshold: the 8-bit drop threshold t (effective probability t / 256); ValueError if invalid."""
     t = load().attn_dropout_threshold(float(dropout_p))
     if t < 0:
-        raise ValueError("dropout_p must lie in [0, 1)")
+        raise ValueError("dropout_p must be 0 or lie in [1/512, 511/512) (steps of 1/256)")
     return t
 
 
@@ -403,78 +425,82 @@ def forward_dropout(q, k, v, dropout_p: float, seed: int, offset: int = 0, scale
                     causal: bool = False, stream=None):
     """attn_fwd_dropout on [B, H, N, d] tensors (other layouts, e.g. transposed [B, N, H, d] views, through
     attn_fwd_dropout_strided; o takes q's layout): (o, lse)."""
-    B, H, N, d = _check_same(q, (k, v), "q, k and v")
-    scale = default_scale(d) if scale is None else scale
-    o = torch.empty_like(q)
-    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    if _all_contiguous(q, k, v, o):
-        st = load().attn_fwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, float(scale),
-                                     int(bool(causal)), _dtype_code(q), float(dropout_p), int(seed), int(offset),
-                                     _stream(stream))
-    else:
-        st = load().attn_fwd_dropout_strided(_strided_ptr(q), _strided_ptr(k), _strided_ptr(v), _strided_ptr(o),
-                                             _ptr(lse), B, H, N, d, _strides12(q, k, v, o), float(scale),
-                                             int(bool(causal)), _dtype_code(q), float(dropout_p), int(seed),
-                                             int(offset), _stream(stream))
-    if st != ATTN_OK:
-        raise AttnError(st, "attn_fwd_dropout")
-    return o, lse
+    with _on_stream(stream, q.device):
+        B, H, N, d = _check_same(q, (k, v), "q, k and v")
+        scale = default_scale(d) if scale is None else scale
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+        if _all_contiguous(q, k, v, o):
+            st = load().attn_fwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, float(scale),
+                                         int(bool(causal)), _dtype_code(q), float(dropout_p), int(seed), int(offset),
+                                         _stream(stream))
+        else:
+            st = load().attn_fwd_dropout_strided(_strided_ptr(q), _strided_ptr(k), _strided_ptr(v), _strided_ptr(o),
+                                                 _ptr(lse), B, H, N, d, _strides12(q, k, v, o), float(scale),
+                                                 int(bool(causal)), _dtype_code(q), float(dropout_p), int(seed),
+                                                 int(offset), _stream(stream))
+        if st != ATTN_OK:
+            raise AttnError(st, "attn_fwd_dropout")
+        return o, lse
 
 
 def backward_dropout(q, k, v, o, lse, dO, dropout_p: float, seed: int, offset: int = 0,
                      scale: Optional[float] = None, causal: bool = False, stream=None):
     """attn_bwd_dropout (same dropout arguments as the forward; other layouts through
     attn_bwd_dropout_strided, gradients in the layouts of q, k, v): (dq, dk, dv)."""
-    B, H, N, d = _check_same(q, (k, v, o, dO), "q, k, v, o and dO")
-    _check_lse(lse, B, H, N)
-    scale = default_scale(d) if scale is None else scale
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ts = (q, k, v, o, dO, dq, dk, dv)
-    if _all_contiguous(*ts):
-        ws = torch.empty(attn_bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=q.device)
-        st = load().attn_bwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse), _ptr(dq), _ptr(dk),
-                                     _ptr(dv), B, H, N, d, float(scale), int(bool(causal)), _dtype_code(q),
-                                     float(dropout_p), int(seed), int(offset), _ptr(ws), ws.numel(),
-                                     _stream(stream))
-    else:
-        ws = torch.empty(attn_bwd_strided_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=q.device)
-        st = load().attn_bwd_dropout_strided(*(_strided_ptr(t) for t in ts[:5]), _ptr(lse),
-                                             *(_strided_ptr(t) for t in ts[5:]), B, H, N, d, _strides12(*ts),
-                                             float(scale), int(bool(causal)), _dtype_code(q), float(dropout_p),
-                                             int(seed), int(offset), _ptr(ws), ws.numel(), _stream(stream))
-    if st != ATTN_OK:
-        raise AttnError(st, "attn_bwd_dropout")
-    return dq, dk, dv
+    with _on_stream(stream, q.device):
+        B, H, N, d = _check_same(q, (k, v, o, dO), "q, k, v, o and dO")
+        _check_lse(lse, B, H, N)
+        scale = default_scale(d) if scale is None else scale
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ts = (q, k, v, o, dO, dq, dk, dv)
+        if _all_contiguous(*ts):
+            ws = torch.empty(attn_bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=q.device)
+            st = load().attn_bwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse), _ptr(dq), _ptr(dk),
+                                         _ptr(dv), B, H, N, d, float(scale), int(bool(causal)), _dtype_code(q),
+                                         float(dropout_p), int(seed), int(offset), _ptr(ws), ws.numel(),
+                                         _stream(stream))
+        else:
+            ws = torch.empty(attn_bwd_strided_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=q.device)
+            st = load().attn_bwd_dropout_strided(*(_strided_ptr(t) for t in ts[:5]), _ptr(lse),
+                                                 *(_strided_ptr(t) for t in ts[5:]), B, H, N, d, _strides12(*ts),
+                                                 float(scale), int(bool(causal)), _dtype_code(q), float(dropout_p),
+                                                 int(seed), int(offset), _ptr(ws), ws.numel(), _stream(stream))
+        if st != ATTN_OK:
+            raise AttnError(st, "attn_bwd_dropout")
+        return dq, dk, dv
 
 
 def dropout_draws(BH: int, Nq: int, Nk: int, seed: int, offset: int = 0, device="cuda", stream=None):
     """attn_dropout_draws: the [BH, Nq, Nk] uint8 draws (dropped where draw < dropout_threshold(p))."""
-    out = torch.empty((BH, Nq, Nk), dtype=torch.uint8, device=device)
-    st = load().attn_dropout_draws(_ptr(out), int(BH), int(Nq), int(Nk), int(seed), int(offset), _stream(stream))
-    if st != ATTN_OK:
-        raise AttnError(st, "attn_dropout_draws")
-    return out
+    with _on_stream(stream, device):
+        out = torch.empty((BH, Nq, Nk), dtype=torch.uint8, device=device)
+        st = load().attn_dropout_draws(_ptr(out), int(BH), int(Nq), int(Nk), int(seed), int(offset), _stream(stream))
+        if st != ATTN_OK:
+            raise AttnError(st, "attn_dropout_draws")
+        return out
 
 
 def forward_kvcache_alibi(q, k, v, alibi_slopes, scale: Optional[float] = None, causal: bool = False,
                           num_splits: int = 0, stream=None):
     """attn_fwd_kvcache_alibi on contiguous tensors: (o, lse)."""
-    B, H, Nq, d = _shape4(q)
-    Hkv, Nk = _check_kv(q, k, v)
-    if Hkv != H:
-        raise ValueError("k and v must have q's head count (grouped heads: forward_kvcache_gqa)")
-    scale = default_scale(d) if scale is None else scale
-    sl = _slopes(alibi_slopes, H, q.device)
-    ws = torch.empty(attn_fwd_kvcache_workspace_bytes(B, H, Nq, Nk, d, num_splits), dtype=torch.uint8,
-                     device=q.device)
-    o = torch.empty_like(q)
-    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
-    st = load().attn_fwd_kvcache_alibi(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk, d, _ptr(sl),
-                                       float(scale), int(bool(causal)), _dtype_code(q), int(num_splits), _ptr(ws),
-                                       ws.numel(), _stream(stream))
-    if st != ATTN_OK:
-        raise AttnError(st, "attn_fwd_kvcache_alibi")
-    return o, lse
+    with _on_stream(stream, q.device):
+        B, H, Nq, d = _shape4(q)
+        Hkv, Nk = _check_kv(q, k, v)
+        if Hkv != H:
+            raise ValueError("k and v must have q's head count (grouped heads: forward_kvcache_gqa)")
+        scale = default_scale(d) if scale is None else scale
+        sl = _slopes(alibi_slopes, H, q.device)
+        ws = torch.empty(attn_fwd_kvcache_workspace_bytes(B, H, Nq, Nk, d, num_splits), dtype=torch.uint8,
+                         device=q.device)
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+        st = load().attn_fwd_kvcache_alibi(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk, d, _ptr(sl),
+                                           float(scale), int(bool(causal)), _dtype_code(q), int(num_splits), _ptr(ws),
+                                           ws.numel(), _stream(stream))
+        if st != ATTN_OK:
+            raise AttnError(st, "attn_fwd_kvcache_alibi")
+        return o, lse
 
 
 def attn_fwd_kvcache_gqa_workspace_bytes(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int,
@@ -485,19 +511,20 @@ def attn_fwd_kvcache_gqa_workspace_bytes(B: int, Hq: int, Hkv: int, Nq: int, Nk:
 def forward_kvcache_gqa(q, k, v, scale: Optional[float] = None, causal: bool = False, num_splits: int = 0,
                         alibi_slopes=None, workspace=None, stream=None):
     """attn_fwd_kvcache_gqa on contiguous q [B,Hq,Nq,d] and k, v [B,Hkv,Nk,d]: (o, lse)."""
-    B, Hq, Nq, d = _shape4(q)
-    Hkv, Nk = _check_kv(q, k, v)
-    scale = default_scale(d) if scale is None else scale
-    sl = None if alibi_slopes is None else _slopes(alibi_slopes, Hq, q.device)
-    if workspace is None:
-        workspace = torch.empty(attn_fwd_kvcache_gqa_workspace_bytes(B, Hq, Hkv, Nq, Nk, d, num_splits),
-                                dtype=torch.uint8, device=q.device)
-    o = torch.empty_like(q)
-    lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
-    st = load().attn_fwd_kvcache_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, d,
-                                     None if sl is None else _ptr(sl), float(scale), int(bool(causal)),
-                                     _dtype_code(q), int(num_splits), _ptr(workspace),
-                                     workspace.numel() * workspace.element_size(), _stream(stream))
-    if st != ATTN_OK:
-        raise AttnError(st, "attn_fwd_kvcache_gqa")
-    return o, lse
+    with _on_stream(stream, q.device):
+        B, Hq, Nq, d = _shape4(q)
+        Hkv, Nk = _check_kv(q, k, v)
+        scale = default_scale(d) if scale is None else scale
+        sl = None if alibi_slopes is None else _slopes(alibi_slopes, Hq, q.device)
+        if workspace is None:
+            workspace = torch.empty(attn_fwd_kvcache_gqa_workspace_bytes(B, Hq, Hkv, Nq, Nk, d, num_splits),
+                                    dtype=torch.uint8, device=q.device)
+        o = torch.empty_like(q)
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+        st = load().attn_fwd_kvcache_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, d,
+                                         None if sl is None else _ptr(sl), float(scale), int(bool(causal)),
+                                         _dtype_code(q), int(num_splits), _ptr(workspace),
+                                         workspace.numel() * workspace.element_size(), _stream(stream))
+        if st != ATTN_OK:
+            raise AttnError(st, "attn_fwd_kvcache_gqa")
+        return o, lse

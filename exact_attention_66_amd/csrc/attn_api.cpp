@@ -260,11 +260,15 @@ int check_slopes(const float* slopes) {
   return ATTN_OK;
 }
 
-// Dropout threshold t = floor(256 p + 1/2) for p in [0, 1), else -1.
+// Dropout threshold t = floor(256 p + 1/2), or -1 when p is not one of the
+// probabilities the 8-bit draws can realise to within half a step: NaN,
+// p < 0, p > 0 that rounds to t = 0 (p < 1/512), and p that rounds to
+// t = 256 (p >= 511/512).
 int drop_threshold(float p) {
   if (!(p >= 0.f && p < 1.f)) return -1;
   const int t = (int)std::floor(256.0 * (double)p + 0.5);
-  return t > 255 ? 255 : t;
+  if (t > 255 || (t == 0 && p > 0.f)) return -1;
+  return t;
 }
 
 int make_drop(float p, uint64_t seed, uint32_t offset, attn::DropCfg* c) {
@@ -439,7 +443,7 @@ const char* attn_status_string(int status) {
     case ATTN_ERR_BAD_LAYOUT:
       return "strides must be >= 0 and multiples of 8 elements (token stride < 2^24), and an output's elements "
              "must not overlap";
-    case ATTN_ERR_BAD_DROPOUT: return "dropout_p must lie in [0, 1)";
+    case ATTN_ERR_BAD_DROPOUT: return "dropout_p must be 0 or lie in [1/512, 511/512)";
     default: return "unknown status";
   }
 }

@@ -72,7 +72,7 @@ enum attn_status {
   ATTN_ERR_HIP = 10,                  /* a kernel launch failed; see attn_last_hip_error() */
   ATTN_ERR_BAD_LAYOUT = 11,           /* strides negative, not multiples of 8 elements, token stride
                                          >= 2^24, or an output layout whose elements overlap */
-  ATTN_ERR_BAD_DROPOUT = 12,          /* dropout probability NaN, < 0 or >= 1 */
+  ATTN_ERR_BAD_DROPOUT = 12,          /* dropout probability NaN, < 0, in (0, 1/512) or >= 511/512 */
 };
 
 /*
@@ -290,21 +290,24 @@ int attn_fwd_kvcache_alibi(const void* q, const void* k, const void* v, void* o,
  *     bh = b * H + h is one call with counter (a, b, bh, offset) and key
  *     (seed & 0xFFFFFFFF, seed >> 32); query 4a + u takes output word u and
  *     key 4b + c its byte c (least significant byte first);
- *   - t = attn_dropout_threshold(dropout_p) = floor(256 dropout_p + 1/2),
- *     at most 255: an element whose byte is below t is dropped (its weight in
- *     P V is 0), the others are multiplied by 256 / (256 - t).  The effective
- *     probability is t / 256.
+ *   - t = attn_dropout_threshold(dropout_p) = floor(256 dropout_p + 1/2):
+ *     an element whose byte is below t is dropped (its weight in P V is 0),
+ *     the others are multiplied by 256 / (256 - t).  The effective
+ *     probability is t / 256, within 1/512 of dropout_p; a dropout_p that
+ *     would round to t = 0 while positive (below 1/512) or to t = 256
+ *     (511/512 and above) is rejected rather than run at another
+ *     probability.
  *   O = (P o M) V with M the scaled keep mask; lse is that of the softmax
  *   over all visible keys (dropout does not change it).  The backward with
  *   the same (dropout_p, seed, offset) differentiates that O.
  *
- * attn_dropout_threshold: t for dropout_p, or -1 if dropout_p is NaN, < 0
- * or >= 1.
+ * attn_dropout_threshold: t for dropout_p, or -1 if dropout_p is NaN, < 0,
+ * in (0, 1/512) or >= 511/512.
  * attn_fwd_dropout / attn_bwd_dropout: as attn_fwd / attn_bwd (contiguous
  * tensors, same workspace, same errors) plus the dropout arguments; the
  * mask depends on (batch, head, query row, key row), not on the layout;
- * ATTN_ERR_BAD_DROPOUT for a dropout_p outside [0, 1).  dropout_p with
- * t = 0 runs the kernels without dropout.
+ * ATTN_ERR_BAD_DROPOUT for a dropout_p that attn_dropout_threshold rejects.
+ * dropout_p = 0 runs the kernels without dropout.
  * attn_dropout_draws: writes the 8-bit draws of heads 0 .. BH-1 for query
  * rows 0 .. Nq-1 and key rows 0 .. Nk-1 to draws (device, uint8,
  * [BH, Nq, Nk] contiguous, caller-owned); an element is dropped exactly when

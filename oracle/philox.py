@@ -18,7 +18,9 @@ into the attention kernel; page "Flash Attention V2 å¤§æ¨¡åž‹æ—¶ä»£çš„ç®—åŠ›æ•‘æ
 layout; the reading here:
 
 * the probability ``p`` is taken in steps of 1/256: ``t = floor(256 p + 1/2)``
-  (0 <= t <= 255), an element is dropped when its 8-bit draw is below ``t``,
+  (0 <= t <= 255; a positive ``p`` that would give ``t = 0``, or a ``p`` that
+  would give ``t = 256``, is rejected), an element is dropped when its 8-bit
+  draw is below ``t``,
   and kept elements are scaled by ``256 / (256 - t)``;
 * the draws of the 4 x 4 block of (query, key) positions
   ``(4a .. 4a+3, 4b .. 4b+3)`` of head ``bh = b * H + h`` come from one
@@ -58,10 +60,17 @@ def philox4x32_10(counter, key):
 
 
 def dropout_threshold(p: float) -> int:
-    """The 8-bit drop threshold t for probability p (elements with draw < t are dropped)."""
+    """The 8-bit drop threshold t for probability p (elements with draw < t are dropped).
+
+    p is taken to the nearest step of 1/256; a p the 8-bit draws cannot
+    realise within half a step (a positive p below 1/512, which would give
+    t = 0, or p >= 511/512, which would give t = 256) is rejected."""
     if not (0.0 <= p < 1.0):
         raise ValueError("dropout probability must lie in [0, 1)")
-    return min(255, int(np.floor(256.0 * p + 0.5)))
+    t = int(np.floor(256.0 * p + 0.5))
+    if t > 255 or (t == 0 and p > 0.0):
+        raise ValueError("dropout probability must be 0 or lie in [1/512, 511/512)")
+    return t
 
 
 def keep_scale(p: float) -> float:

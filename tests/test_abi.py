@@ -297,8 +297,9 @@ def test_kvcache_grouped_heads_checks(lib):
 def test_dropout_entry_points_check_arguments(lib):
     BAD_DROPOUT = 12
     assert lib.attn_dropout_threshold(0.0) == 0 and lib.attn_dropout_threshold(0.1) == 26
-    assert lib.attn_dropout_threshold(0.5) == 128 and lib.attn_dropout_threshold(0.9999) == 255
-    for p in (-0.01, 1.0, 2.0, float("nan"), float("inf")):
+    assert lib.attn_dropout_threshold(0.5) == 128 and lib.attn_dropout_threshold(255 / 256) == 255
+    assert lib.attn_dropout_threshold(1 / 512) == 1
+    for p in (-0.01, 1.0, 2.0, float("nan"), float("inf"), 0.001, 0.9999, 511 / 512):
         assert lib.attn_dropout_threshold(p) == -1
         assert lib.attn_fwd_dropout(P[0], P[1], P[2], P[3], P[4], 1, 2, 128, 64, 0.125, 1, 0, p, 1, 0,
                                     None) == BAD_DROPOUT

@@ -2,9 +2,9 @@
 
 The GPU forward output (O, lse) feeds the GPU backward exactly as in
 training; the oracle computes its gradients from the same rounded inputs.
-Small shapes are compared over every head; the full workload sizes over
-whole sampled heads (the oracle evaluates one head at a time), plus
-invariants that hold at any size on every head.
+Small shapes are compared over every head; the full workload sizes are
+compared over every element, with the gradient invariants on every head, in
+test_gpu_fullsize.py.
 """
 import numpy as np
 import pytest
@@ -12,7 +12,7 @@ import torch
 
 import oracle
 import workloads
-from parity import GRAD_REL_FRO, check_grad, f64, log, require_gpu
+from parity import check_grad, f64, log, require_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -49,38 +49,6 @@ def test_backward_small_all_elements(B, H, N, d, dt, causal):
     ref = oracle.backward(*(workloads.to_f64_numpy(x[n]) for n in ("q", "k", "v", "do")), w.scale, causal)
     for name, g, gr in zip(("dQ", "dK", "dV"), grads, ref):
         check_grad(f64(g), gr, name)
-
-
-def _invariants(dk, dv, do, what):
-    """Rows of dS sum to 0, so sum_j dK_j = 0; rows of P sum to 1, so
-    sum_j dV_j = sum_i dO_i.  Checked per head, relative to the head's
-    Frobenius norm (each of the N summed values carries its own rounding)."""
-    sk = dk.double().sum(dim=2).norm(dim=-1)
-    nk = dk.double().norm(dim=(2, 3))
-    assert bool((sk <= 2e-2 * nk).all()), f"{what}: |sum_j dK_j| / |dK| = {(sk / nk).max().item():.3e}"
-    sv = (dv.double().sum(dim=2) - do.double().sum(dim=2)).norm(dim=-1)
-    nv = dv.double().norm(dim=(2, 3))
-    assert bool((sv <= 2e-2 * nv).all()), f"{what}: |sum dV - sum dO| / |dV| = {(sv / nv).max().item():.3e}"
-
-
-@pytest.mark.parametrize("name", [n for n, w in workloads.WORKLOADS.items() if w.backward])
-def test_backward_full_size_sampled_heads(name):
-    ea = require_gpu()
-    w = workloads.WORKLOADS[name]
-    log(f"backward full size {w.name}")
-    x = workloads.make_inputs(w)
-    (q, k, v, do, o, lse), (dq, dk, dv) = _run(ea, x, w.scale, w.causal)
-    for t in (dq, dk, dv):
-        assert torch.isfinite(t).all().item()
-    _invariants(dk, dv, do, w.name)
-    heads = [(0, 0), (w.B - 1, w.H - 1)] if w.N >= 16384 else sorted({(0, 0), (w.B // 2, w.H // 3), (w.B - 1, w.H - 1)})
-    rb = 2048 if w.N > 4096 else None
-    for b, h in heads:
-        log(f"  oracle head ({b},{h})")
-        ref = oracle.backward_head(*(workloads.to_f64_numpy(x[n][b, h]) for n in ("q", "k", "v", "do")),
-                                   w.scale, w.causal, row_block=rb)
-        errs = [check_grad(f64(g[b, h]), gr, f"{gname}[{b},{h}]") for gname, g, gr in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref)]
-        log(f"  head ({b},{h}): relative Frobenius error dQ {errs[0]:.2e} dK {errs[1]:.2e} dV {errs[2]:.2e}")
 
 
 def test_backward_deterministic():

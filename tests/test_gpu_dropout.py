@@ -44,9 +44,11 @@ def test_draws_bit_exact(BH, Nq, Nk, seed, offset):
 
 def test_threshold_matches_oracle():
     ea = require_gpu()
-    for p in (0.0, 0.001, 0.1, 0.25, 0.5, 0.9, 0.999):
+    for p in (0.0, 1 / 512, 0.1, 0.25, 0.5, 0.9, 255 / 256):
         assert ea.dropout_threshold(p) == philox.dropout_threshold(p)
-    for p in (-0.1, 1.0, float("nan")):
+    for p in (-0.1, 1.0, float("nan"), 0.001, 0.999):
+        with pytest.raises(ValueError):
+            philox.dropout_threshold(p)
         with pytest.raises(ValueError):
             ea.dropout_threshold(p)
 
@@ -164,15 +166,15 @@ def test_dropout_token_major_layout(N, d, causal):
 
 
 def test_dropout_extreme_probability():
-    """p = 0.999 (t = 255, keep factor 256): rows whose visible keys are all dropped give O = 0 exactly,
+    """p = 255/256 (t = 255, keep factor 256): rows whose visible keys are all dropped give O = 0 exactly,
     the rest match the oracle, and the gradients stay finite and match."""
     ea = require_gpu()
     w = workloads.Workload("drop_hi", 1, 2, 300, 64, "bf16", True, True, seed=43001)
     x = workloads.make_inputs(w)
     q, k, v, do = (x[n].cuda() for n in ("q", "k", "v", "do"))
-    p, seed = 0.999, 3
+    p, seed = 255 / 256, 3
     assert philox.dropout_threshold(p) == 255
-    log("dropout p=0.999 B=1 H=2 N=300 d=64 causal")
+    log("dropout p=255/256 B=1 H=2 N=300 d=64 causal")
     o, lse = ea.forward_dropout(q, k, v, p, seed, 0, scale=w.scale, causal=True)
     dq, dk, dv = ea.backward_dropout(q, k, v, o, lse, do, p, seed, 0, scale=w.scale, causal=True)
     torch.cuda.synchronize()

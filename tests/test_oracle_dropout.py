@@ -50,11 +50,11 @@ def test_threshold_and_scale():
     assert philox.dropout_threshold(0.0) == 0 and philox.keep_scale(0.0) == 1.0
     assert philox.dropout_threshold(0.1) == 26 and philox.keep_scale(0.1) == 256 / 230
     assert philox.dropout_threshold(0.5) == 128 and philox.keep_scale(0.5) == 2.0
-    assert philox.dropout_threshold(0.999) == 255
-    with pytest.raises(ValueError):
-        philox.dropout_threshold(1.0)
-    with pytest.raises(ValueError):
-        philox.dropout_threshold(-0.1)
+    assert philox.dropout_threshold(255 / 256) == 255 and philox.keep_scale(255 / 256) == 256.0
+    assert philox.dropout_threshold(1 / 512) == 1
+    for bad in (1.0, -0.1, float("nan"), 0.001, 1 / 512 - 1e-9, 511 / 512, 0.999):
+        with pytest.raises(ValueError):
+            philox.dropout_threshold(bad)
 
 
 @pytest.mark.parametrize("p", [0.1, 0.5])
