@@ -22,6 +22,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace attn {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));

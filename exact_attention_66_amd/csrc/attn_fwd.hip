@@ -25,8 +25,10 @@
 //    fragments before its P V product, so the LDS latency hides under MFMAs;
 //  * exponentials use exp2 with scale*log2(e) folded into one FMA, and the
 //    O rescale is skipped while the running max grows by less than 2^8
-//    (exact: the same stale max is used for O, l and lse); row max and sums
-//    are trees rather than dependent chains;
+//    (exact: the same stale max is used for O, l and lse) unless, with bf16
+//    weights, the new largest weight would carry a large share of the row
+//    (kDominantFraction); row max and sums are trees rather than dependent
+//    chains;
 //  * causal launches order work units heaviest query block first;
 //  * any N: rows past the end are neither read nor stored, and the last
 //    tile's keys past the end are masked (the TAIL instantiation, chosen
@@ -50,8 +52,35 @@ namespace {
 
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
-// Rescale O only when the running max grows by more than this (log2 units).
-constexpr float kRescaleSlack = 8.0f;
+// Lazy rescale.  The running max m may trail the true row max by up to
+// kRescaleSlack (log2 units) before O, l and lse are rescaled: the same
+// stale max serves all three, so the result is exact up to rounding.  But a
+// weight exp2(s - m) taken against a stale max is no longer exactly 1 at
+// the row's largest score, and rounding it to 16 bits for the P V product
+// costs up to half an ulp of that weight; where one key carries most of a
+// row's weight this shows up in O (at bf16, on top of the output's own
+// rounding, enough to exceed 1e-2 at |O| in [2, 4)).  So with bf16 weights
+// (8 significant bits) the max is also made exact whenever the block's
+// largest weight against the stale max would exceed kDominantFraction (1/8) of
+// the row's sum so far: every key that is not rounded as exactly 1 then
+// ends up with less than that fraction of the row's weight, and its
+// rounding error in O stays below 2^-9 kDominantFraction |V - O|.  The
+// test compares the growth of the max, log2 of that weight, with a lower
+// bound of log2(kDominantFraction l) taken from the exponent bits of l (full-
+// rate instructions; the bound only makes the rescale more frequent).  fp16
+// weights (11 bits) make the effect 8x smaller and skip the check.
+#ifndef ATTN_FWD_SLACK
+#define ATTN_FWD_SLACK 8.0f
+#endif
+#ifndef ATTN_FWD_DOMINANT_LOG2
+#define ATTN_FWD_DOMINANT_LOG2 (-3.0f)   // kDominantFraction = 1/8
+#endif
+constexpr float kRescaleSlack = ATTN_FWD_SLACK;
+constexpr float kLog2DominantFraction = ATTN_FWD_DOMINANT_LOG2;
+template <typename E>
+constexpr bool exact_dominant_weight() {
+  return !std::is_same<E, f16_t>::value && kLog2DominantFraction < 0.0f;
+}
 
 #ifndef ATTN_FWD_QB
 #define ATTN_FWD_QB 1    // 32-query blocks per wave
@@ -340,7 +369,13 @@ __global__ __launch_bounds__(NW * 64, ATTN_FWD_MINW) void fwd_kernel(const typen
       float mx = fmax3(fmax3(m0, m1, m2), fmax3(m3, m4, x[15]), -__builtin_inff());
       mx = xhalf_max(mx);
       const float mt = ALIBI ? mx + bshift : mx * scale_log2;
-      const bool need = mt > m_run[qb] + kRescaleSlack;
+      const float grow = mt - m_run[qb];
+      bool need = grow > kRescaleSlack;
+      if constexpr (exact_dominant_weight<E>()) {
+        // l = f 2^e with f in [0.5, 1), so log2 l >= e - 1
+        const int e = __builtin_amdgcn_frexp_expf(l_run[qb]);
+        need = need || (grow > 0.f && grow > kLog2DominantFraction + (float)(e - 1));
+      }
       if (__builtin_amdgcn_ballot_w64(need) != 0) {
         const float mn = fmaxf(m_run[qb], mt);
         const float alpha = fast_exp2(m_run[qb] - mn);

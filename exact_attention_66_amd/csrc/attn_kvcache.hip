@@ -36,8 +36,15 @@ namespace {
 
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
-// Rescale O only when the running max grows by more than this (log2 units).
-constexpr float kRescaleSlack = 8.0f;
+// How far the running max may trail the row max (log2 units) before O, l
+// and lse are rescaled.  A weight taken against a stale max is not exactly 1
+// at the row's largest score, and rounding it to 16 bits for the P V product
+// then puts up to half an ulp of the dominant weight into O; bf16 weights
+// keep the max exact, fp16 weights (three more bits) take a slack of 2^8.
+template <typename E>
+constexpr float rescale_slack() {
+  return std::is_same<E, f16_t>::value ? 8.0f : 0.0f;
+}
 
 template <int D>
 struct KvTile {
@@ -173,7 +180,7 @@ __global__ __launch_bounds__(64) void kv_split_kernel(const typename E::T* __res
   f32x16 oacc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
-  // m_run: running max (log2 units, may trail the true max by < kRescaleSlack;
+  // m_run: running max (log2 units, may trail the true max by < rescale_slack<E>(),
   // -inf while the row has seen no key); l_run: sum of the fp32 weights;
   // lr_run: sum of the same weights rounded to 16 bits (those the P V product used)
   float m_run = -__builtin_inff(), l_run = 0.f, lr_run = 0.f;
@@ -237,7 +244,7 @@ __global__ __launch_bounds__(64) void kv_split_kernel(const typename E::T* __res
                      fmax3(fmax3(s[9], s[10], s[11]), fmax3(s[12], s[13], s[14]), s[15]), -__builtin_inff());
     mx = xhalf_max(mx);
     const float mt = ALIBI ? mx + bshift : mx * scale_log2;   // -inf when every key of the block is masked for this row
-    if (__builtin_amdgcn_ballot_w64(mt > m_run + kRescaleSlack) != 0) {
+    if (__builtin_amdgcn_ballot_w64(mt > m_run + rescale_slack<E>()) != 0) {
       const float mn = fmaxf(m_run, mt);
       // equal maxima (also both -inf: a row that has seen no key yet) need no rescale
       const float alpha = mn == m_run ? 1.0f : fast_exp2(m_run - mn);
