@@ -18,6 +18,8 @@ from ._binding import (  # noqa: F401
     attn_bwd_workspace_bytes,
     attn_fwd,
     attn_fwd_kvcache,
+    attn_fwd_kvcache_noalloc,
+    ATTN_KV_SCRATCH_BYTES,
     attn_fwd_kvcache_splits,
     attn_fwd_kvcache_workspace_bytes,
     attn_last_hip_error,

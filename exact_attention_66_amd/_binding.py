@@ -24,9 +24,12 @@ STATUS_NAMES = {
     0: "ATTN_OK", 1: "ATTN_ERR_NULL_PTR", 2: "ATTN_ERR_BAD_SHAPE", 3: "ATTN_ERR_UNSUPPORTED_HEAD_DIM",
     4: "ATTN_ERR_BAD_DTYPE", 5: "ATTN_ERR_MISALIGNED", 6: "ATTN_ERR_UNSUPPORTED_SEQLEN",
     7: "ATTN_ERR_BAD_SCALE", 8: "ATTN_ERR_WORKSPACE_TOO_SMALL", 9: "ATTN_ERR_ALIASING", 10: "ATTN_ERR_HIP",
-    11: "ATTN_ERR_BAD_LAYOUT", 12: "ATTN_ERR_BAD_DROPOUT",
+    11: "ATTN_ERR_BAD_LAYOUT", 12: "ATTN_ERR_BAD_DROPOUT", 13: "ATTN_ERR_SCRATCH_TOO_SMALL",
 }
+# ATTN_KV_SCRATCH_BYTES of include/attn.h: the static buffer of attn_fwd_kvcache_noalloc
+ATTN_KV_SCRATCH_BYTES = 32 << 20
 EXPORTED = ["attn_fwd", "attn_fwd_strided", "attn_bwd_workspace_bytes", "attn_bwd", "attn_fwd_kvcache",
+            "attn_fwd_kvcache_noalloc",
             "attn_fwd_kvcache_strided", "attn_fwd_kvcache_workspace_bytes", "attn_fwd_kvcache_splits",
             "attn_bwd_strided", "attn_bwd_strided_workspace_bytes", "attn_fwd_alibi", "attn_bwd_alibi",
             "attn_fwd_kvcache_alibi", "attn_fwd_kvcache_gqa", "attn_fwd_kvcache_gqa_workspace_bytes",
@@ -68,6 +71,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_bwd.restype = i32
     lib.attn_fwd_kvcache.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, f32, i32, i32, i32, vp, sz, vp]
     lib.attn_fwd_kvcache.restype = i32
+    lib.attn_fwd_kvcache_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, f32, i32, i32, i32, vp]
+    lib.attn_fwd_kvcache_noalloc.restype = i32
     i64p = ctypes.POINTER(ctypes.c_int64)
     lib.attn_fwd_strided.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64p, f32, i32, i32, vp]
     lib.attn_fwd_strided.restype = i32
@@ -279,6 +284,24 @@ def attn_fwd_kvcache(q, k, v, o, lse, scale: float, causal: bool, workspace, num
                                              ws_bytes, _stream(stream))
     if st != ATTN_OK:
         raise AttnError(st, "attn_fwd_kvcache")
+
+
+def attn_fwd_kvcache_noalloc(q, k, v, o, lse, scale: float, causal: bool, num_splits: int = 0, stream=None) -> None:
+    """Enqueue the KV-cache forward with the split partials in the library's static buffer (no workspace, no
+    allocation): contiguous q, o [B,H,Nq,d], k, v [B,H,Nk,d], lse [B,H,Nq] fp32, all caller-allocated."""
+    B, H, Nq, d = _shape4(q)
+    Nk = int(k.shape[2]) if k.dim() == 4 else -1
+    if tuple(k.shape) != (B, H, Nk, d) or tuple(v.shape) != (B, H, Nk, d) or tuple(o.shape) != (B, H, Nq, d):
+        raise ValueError("q, o must be [B,H,Nq,d] and k, v [B,H,Nk,d]")
+    if any(t.dtype != q.dtype for t in (k, v, o)):
+        raise ValueError("q, k, v and o must share the dtype")
+    if tuple(lse.shape) != (B, H, Nq) or lse.dtype != torch.float32:
+        raise ValueError("lse must be a float32 [B, H, Nq] tensor")
+    st = load().attn_fwd_kvcache_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk, d,
+                                         float(scale), int(bool(causal)), _dtype_code(q), int(num_splits),
+                                         _stream(stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fwd_kvcache_noalloc")
 
 
 # ------------------------------------------------------------------ conveniences

@@ -154,7 +154,7 @@ int check_kvcache(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, float
 int kv_impl(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H, int64_t Nq,
             int64_t Nk, int64_t d, const attn::Lay* lays, float scale, int causal, int dtype, int num_splits,
             void* workspace, size_t workspace_bytes, void* stream, const float* slopes = nullptr,
-            int64_t Hkv = -1) {
+            int64_t Hkv = -1, bool noalloc = false) {
   if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL_PTR;
   if (Hkv == -1) Hkv = H;   // no grouping
   int st = check_kvcache(B, H, Nq, Nk, d, scale, causal, dtype, num_splits, Hkv);
@@ -165,20 +165,30 @@ int kv_impl(const void* q, const void* k, const void* v, void* o, float* lse, in
   int P = 1, chunk = 32;
   attn::kv_split_plan(B * Hkv, (H / Hkv) * Nq, Nk, num_splits, &P, &chunk);
   const size_t need = attn::kv_acc_bytes(B * H, Nq, P, d) + attn::kv_stat_bytes(B * H, Nq, P);
-  if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE_TOO_SMALL;
+  if (noalloc) {
+    // the library's static buffer stands in for the workspace (no caller
+    // memory to check it against)
+    if (need > ATTN_KV_SCRATCH_BYTES) return ATTN_ERR_SCRATCH_TOO_SMALL;
+  } else if (!workspace || workspace_bytes < need) {
+    return ATTN_ERR_WORKSPACE_TOO_SMALL;
+  }
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
-      (reinterpret_cast<uintptr_t>(workspace) & 255u))
+      (!noalloc && (reinterpret_cast<uintptr_t>(workspace) & 255u)))
     return ATTN_ERR_MISALIGNED;
   const size_t lb = (size_t)(B * H * Nq) * 4;
   struct R { const void* p; size_t n; };
   const R ins[] = {{q, lay_extent(lays[0], B, H, Nq, d)}, {k, lay_extent(lays[1], B, Hkv, Nk, d)},
                    {v, lay_extent(lays[2], B, Hkv, Nk, d)}, {slopes, slopes ? (size_t)H * 4 : 0}};
-  const R outs[] = {{o, lay_extent(lays[3], B, H, Nq, d)}, {lse, lb}, {workspace, need}};
+  const R outs[] = {{o, lay_extent(lays[3], B, H, Nq, d)}, {lse, lb}, {noalloc ? nullptr : workspace, noalloc ? 0 : need}};
   for (const R& x : outs) {
     for (const R& y : ins)
       if (overlaps(x.p, x.n, y.p, y.n)) return ATTN_ERR_ALIASING;
     for (const R& y : outs)
       if (&x != &y && overlaps(x.p, x.n, y.p, y.n)) return ATTN_ERR_ALIASING;
+  }
+  if (noalloc) {   // every check has passed: now the first HIP call
+    const hipError_t e = attn::kv_scratch_address(&workspace);
+    if (e != hipSuccess) return launch_status(e);
   }
   char* ws = (char*)workspace;
   attn::KvArgs a{q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal != 0, dtype, P, chunk,
@@ -416,6 +426,16 @@ int attn_fwd_kvcache(const void* q, const void* k, const void* v, void* o, float
                  workspace_bytes, stream);
 }
 
+int attn_fwd_kvcache_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                             int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale, int causal, int dtype,
+                             int num_splits, void* stream) {
+  if (checked_elems(B, H, Nq, d) < 0 || checked_elems(B, H, Nk, d) < 0) return ATTN_ERR_BAD_SHAPE;
+  const attn::Lay cq = attn::contiguous_lay(H, Nq, d), ck = attn::contiguous_lay(H, Nk, d);
+  const attn::Lay lays[4] = {cq, ck, ck, cq};
+  return kv_impl(q, k, v, o, lse, B, H, Nq, Nk, d, lays, scale, causal, dtype, num_splits, nullptr, 0, stream,
+                 nullptr, -1, true);
+}
+
 int attn_fwd_kvcache_strided(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
                              int64_t Nq, int64_t Nk, int64_t d, const int64_t* strides, float scale, int causal,
                              int dtype, int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
@@ -444,6 +464,7 @@ const char* attn_status_string(int status) {
       return "strides must be >= 0 and multiples of 8 elements (token stride < 2^24), and an output's elements "
              "must not overlap";
     case ATTN_ERR_BAD_DROPOUT: return "dropout_p must be 0 or lie in [1/512, 511/512)";
+    case ATTN_ERR_SCRATCH_TOO_SMALL: return "the call needs more split partials than ATTN_KV_SCRATCH_BYTES holds";
     default: return "unknown status";
   }
 }

@@ -27,6 +27,9 @@
 // sequence, so it sees keys j <= i + Nk - Nq.  The ALIBI instantiation adds
 // the linear position bias -m_h |position - j| to the scores before the row
 // max (the ALiBi entry point of the C ABI).
+#include <mutex>
+
+#include "../../include/attn.h"
 #include "attn_device.h"
 #include "attn_launch.h"
 
@@ -413,6 +416,33 @@ hipError_t launch_kv_d(const KvArgs& a) {
 hipError_t launch_kvcache(const KvArgs& a) {
   if (a.dtype == 0) return a.d == 64 ? launch_kv_d<bf16_t, 64>(a) : launch_kv_d<bf16_t, 128>(a);
   return a.d == 64 ? launch_kv_d<f16_t, 64>(a) : launch_kv_d<f16_t, 128>(a);
+}
+
+// Split partials of attn_fwd_kvcache_noalloc.  Each device that runs the
+// library holds its own copy of this array for the life of the process.  In
+// host code the name stands for a host-side shadow, not a device address:
+// kernels receive the address hipGetSymbolAddress returns for the current
+// device, cached per device below.
+static __device__ __align__(256) unsigned char scratch[ATTN_KV_SCRATCH_BYTES];
+
+hipError_t kv_scratch_address(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p || (reinterpret_cast<uintptr_t>(p) & 255u)) return hipErrorInvalidValue;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 }  // namespace attn

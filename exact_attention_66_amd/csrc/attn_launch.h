@@ -145,6 +145,10 @@ int persistent_grid(const void* fn, int block, int units);
 hipError_t launch_fwd(const FwdArgs& a);
 hipError_t launch_bwd(const BwdArgs& a);
 hipError_t launch_kvcache(const KvArgs& a);
+// Device address, on the current device, of the library's static scratch
+// buffer (ATTN_KV_SCRATCH_BYTES bytes, 256-byte aligned) for the
+// no-allocation KV-cache entry point; looked up once per device.
+hipError_t kv_scratch_address(void** ptr);
 hipError_t launch_dropout_draws(uint8_t* out, int64_t BH, int64_t Nq, int64_t Nk, const DropCfg& drop,
                                 hipStream_t stream);
 

@@ -73,6 +73,8 @@ enum attn_status {
   ATTN_ERR_BAD_LAYOUT = 11,           /* strides negative, not multiples of 8 elements, token stride
                                          >= 2^24, or an output layout whose elements overlap */
   ATTN_ERR_BAD_DROPOUT = 12,          /* dropout probability NaN, < 0, in (0, 1/512) or >= 511/512 */
+  ATTN_ERR_SCRATCH_TOO_SMALL = 13,    /* attn_fwd_kvcache_noalloc: the call needs more than
+                                         ATTN_KV_SCRATCH_BYTES of split partials */
 };
 
 /*
@@ -175,6 +177,32 @@ int attn_fwd_kvcache(const void* q, const void* k, const void* v, void* o, float
                      int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale,
                      int causal, int dtype, int num_splits, void* workspace,
                      size_t workspace_bytes, void* stream);
+
+/*
+ * attn_fwd_kvcache_noalloc - attn_fwd_kvcache for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same arguments without the
+ * workspace.  The split partials go to a static buffer of the library
+ * (ATTN_KV_SCRATCH_BYTES per device, held until the process ends); the
+ * call allocates nothing.
+ *   Limit: attn_fwd_kvcache_workspace_bytes(B, H, Nq, Nk, d, num_splits)
+ *   must not exceed ATTN_KV_SCRATCH_BYTES, else ATTN_ERR_SCRATCH_TOO_SMALL
+ *   (checked, like every argument, before any HIP call).  At the default
+ *   split plan this admits up to about 60,000 (query row, key range) pairs at
+ *   d = 128, e.g. B * H * Nq = 7,500 query rows at 8 ranges.
+ *   Sharing: every call on one device uses that device's one buffer, and the
+ *   merge of a call reads what its own split pass wrote there.  Calls that
+ *   overlap on one GPU (different streams with no ordering between them, or
+ *   different threads) race on the buffer and give wrong results; calls on
+ *   one stream are ordered and safe.  No part of the buffer needs clearing:
+ *   each call writes every partial it later reads.
+ *   Returns ATTN_ERR_HIP (attn_last_hip_error) if the buffer's device address
+ *   cannot be obtained on the current device.
+ */
+#define ATTN_KV_SCRATCH_BYTES ((size_t)32 << 20)
+int attn_fwd_kvcache_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale,
+                             int causal, int dtype, int num_splits, void* stream);
 
 /*
  * attn_fwd_kvcache_strided - attn_fwd_kvcache for tensors in any layout with

@@ -172,6 +172,29 @@ def test_kvcache_noncausal_allows_more_queries_than_keys(lib):
     assert kvf(lib, Nq=500, Nk=300, causal=0, ws_bytes=16) == WS
 
 
+def kvn(lib, q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=1, H=2, Nq=4, Nk=300, d=64, scale=0.125, causal=1,
+        dtype=0, splits=0):
+    return lib.attn_fwd_kvcache_noalloc(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, dtype, splits, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(lse=None), NULL), (dict(B=0), SHAPE), (dict(Nq=301, Nk=300), SHAPE),
+    (dict(splits=5000), SHAPE), (dict(d=32), HEADDIM), (dict(dtype=3), DTYPE), (dict(scale=0.0), SCALE),
+    (dict(q=P[0] + 2), ALIGN), (dict(o=P[0]), ALIAS), (dict(lse=P[2] + 32), ALIAS),
+    # 8 x 64 x 64 query rows at 64 key ranges: 1 GiB of partials > the 32 MiB buffer
+    (dict(B=8, H=64, Nq=64, Nk=8192, d=128, splits=64), 13),
+])
+def test_kvcache_noalloc_rejects_before_any_hip_call(lib, kw, code):
+    assert kvn(lib, **kw) == code
+
+
+def test_kvcache_noalloc_limit_is_the_workspace_size(lib):
+    # the largest call the static buffer admits needs at most ATTN_KV_SCRATCH_BYTES of partials
+    assert ea.ATTN_KV_SCRATCH_BYTES == 32 << 20
+    assert ea.attn_fwd_kvcache_workspace_bytes(4, 32, 8, 4096, 128, 0) <= ea.ATTN_KV_SCRATCH_BYTES
+    assert ea.attn_fwd_kvcache_workspace_bytes(8, 64, 64, 8192, 128, 64) > ea.ATTN_KV_SCRATCH_BYTES
+
+
 # ---------------------------------------------------------------- strided layouts
 LAYOUT = 11
 
