@@ -14,7 +14,9 @@ from typing import Optional
 
 import torch
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
+# The in-tree build; ATTN_LIBRARY names another build of the same library
+# (the host-sanitizer build of the argument checks uses it).
+LIB_PATH = os.environ.get("ATTN_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
 
 # attn_status / attn_dtype values of include/attn.h
 ATTN_OK = 0

@@ -91,8 +91,26 @@ int persistent_grid(const void* fn, int block, int units) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
     if (dev >= 0 && dev < kMaxDev) cus[dev].store(n, std::memory_order_relaxed);
   }
-  int per_cu = 1;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, block, 0) != hipSuccess || per_cu < 1) per_cu = 1;
+  // resident workgroups per CU of this kernel: asked once per (device, kernel, block size)
+  struct Occ {
+    int dev;
+    const void* fn;
+    int block;
+    int per_cu;
+  };
+  static std::mutex occ_mu;
+  static std::vector<Occ> occ;
+  int per_cu = 0;
+  {
+    std::lock_guard<std::mutex> lk(occ_mu);
+    for (const Occ& o : occ)
+      if (o.dev == dev && o.fn == fn && o.block == block) per_cu = o.per_cu;
+  }
+  if (per_cu <= 0) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, block, 0) != hipSuccess || per_cu < 1) per_cu = 1;
+    std::lock_guard<std::mutex> lk(occ_mu);
+    occ.push_back({dev, fn, block, per_cu});
+  }
   const int per_xcd = (n * per_cu + 7) / 8;
   const int need = (units + 7) / 8;
   return 8 * (need < per_xcd ? need : per_xcd);
