@@ -374,7 +374,7 @@ __global__ __launch_bounds__(NW * 64, ATTN_FWD_MINW) void fwd_kernel(const typen
       if constexpr (exact_dominant_weight<E>()) {
         // l = f 2^e with f in [0.5, 1), so log2 l >= e - 1
         const int e = __builtin_amdgcn_frexp_expf(l_run[qb]);
-        need = need || (grow > 0.f && grow > kLog2DominantFraction + (float)(e - 1));
+        need = need | ((grow > 0.f) & (grow > kLog2DominantFraction + (float)(e - 1)));
       }
       if (__builtin_amdgcn_ballot_w64(need) != 0) {
         const float mn = fmaxf(m_run[qb], mt);
