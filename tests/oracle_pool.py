@@ -55,14 +55,14 @@ def _head_task(task):
     """Oracle of one head and its comparison with the GPU result (in a worker)."""
     from oracle import attention as A
 
-    (b, h, scale, causal, dtype, row_block, q, k, v, do, o_gpu, lse_gpu, grads) = task
+    (b, h, scale, causal, dtype, row_block, q, k, v, do, o_gpu, lse_gpu, grads, dropout, gain) = task
     q, k, v = (np.asarray(a, dtype=np.float64) for a in (q, k, v))
     out = {"b": b, "h": h}
     if o_gpu is not None:
-        o_ref, lse_ref = A.forward_head(q, k, v, scale, causal, row_block=row_block)
+        o_ref, lse_ref = A.forward_head(q, k, v, scale, causal, row_block=row_block, dropout=dropout)
         err = np.abs(o_gpu.astype(np.float64) - o_ref)
         big = np.abs(o_ref) >= 4.0
-        bound = np.where(big, half_ulp(o_ref, dtype) + 1e-3, 1e-2)
+        bound = np.where(big, half_ulp(o_ref, dtype) + 1e-3 * gain, 1e-2 * gain)
         over = err > bound
         out["o_max"] = float(err.max())
         out["o_sum"] = float(err.sum())
@@ -70,13 +70,17 @@ def _head_task(task):
         out["o_over"] = int(over.sum())
         out["o_big"] = int(big.sum())
         out["o_floor"] = float(np.abs(round_to(o_ref, dtype) - o_ref).max())
+        out["o_half_ulp_sum"] = float(half_ulp(o_ref, dtype).sum())
+        out["o_err_sq"] = float(np.sum(err ** 2))
+        out["o_ref_sq"] = float(np.sum(o_ref ** 2))
         if out["o_over"]:
             i = np.unravel_index(int(np.argmax(np.where(over, err - bound, -np.inf))), err.shape)
             out["o_worst_over"] = (int(i[0]), int(i[1]), float(o_gpu[i]), float(o_ref[i]))
         out["lse_max"] = float(np.abs(lse_gpu.astype(np.float64) - lse_ref).max())
         out["finite"] = bool(np.isfinite(o_gpu).all() and np.isfinite(lse_gpu).all())
     if grads is not None:
-        ref = A.backward_head(q, k, v, np.asarray(do, dtype=np.float64), scale, causal, row_block=row_block)
+        ref = A.backward_head(q, k, v, np.asarray(do, dtype=np.float64), scale, causal, row_block=row_block,
+                              dropout=dropout)
         for name, g, gr in zip(("dq", "dk", "dv"), grads, ref):
             g = g.astype(np.float64)
             out[name + "_num"] = float(np.sum((g - gr) ** 2))
@@ -91,11 +95,17 @@ def _f32(t) -> np.ndarray:
 
 
 def compare_full(w, x, o=None, lse=None, grads=None, workers: Optional[int] = None,
-                 row_block: int = 512) -> Dict[str, float]:
+                 row_block: int = 512, dropout=None) -> Dict[str, float]:
     """Compare GPU outputs of workload ``w`` (inputs ``x``: CPU tensors of the I/O dtype) with the oracle
     over every head.  ``o``, ``lse``: the forward outputs (CPU tensors) or None; ``grads``: (dq, dk, dv)
-    CPU tensors or None.  Returns the whole-tensor metrics (see the module docstring)."""
+    CPU tensors or None; ``dropout``: ``(p, seed, offset)`` or None (head (b, h) draws with index
+    b * H + h).  With dropout the O bounds other than the output rounding floor grow by the keep factor
+    k = 256 / (256 - t) (every rounding made before the final multiplication by k is multiplied by it).
+    Returns the whole-tensor metrics (see the module docstring)."""
+    from oracle import philox
+
     workers = workers or default_workers()
+    gain = 1.0 if dropout is None else philox.keep_scale(dropout[0])
 
     def tasks() -> Iterator[Tuple]:
         for b in range(w.B):
@@ -104,7 +114,8 @@ def compare_full(w, x, o=None, lse=None, grads=None, workers: Optional[int] = No
                        _f32(x["q"][b, h]), _f32(x["k"][b, h]), _f32(x["v"][b, h]),
                        None if grads is None else _f32(x["do"][b, h]),
                        None if o is None else _f32(o[b, h]), None if lse is None else lse[b, h].numpy(),
-                       None if grads is None else tuple(_f32(g[b, h]) for g in grads))
+                       None if grads is None else tuple(_f32(g[b, h]) for g in grads),
+                       None if dropout is None else (dropout[0], dropout[1], dropout[2], b * w.H + h), gain)
 
     saved = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")}
     for k in saved:
@@ -129,6 +140,8 @@ def compare_full(w, x, o=None, lse=None, grads=None, workers: Optional[int] = No
         m["o_over"] = sum(r["o_over"] for r in results)
         m["o_big"] = sum(r["o_big"] for r in results)
         m["o_floor"] = max(r["o_floor"] for r in results)
+        m["o_mean_half_ulp"] = sum(r["o_half_ulp_sum"] for r in results) / n
+        m["o_rel_fro"] = float(np.sqrt(sum(r["o_err_sq"] for r in results) / sum(r["o_ref_sq"] for r in results)))
         m["lse_max"] = max(r["lse_max"] for r in results)
         m["finite"] = all(r["finite"] for r in results)
         over = [r for r in results if r.get("o_worst_over")]
