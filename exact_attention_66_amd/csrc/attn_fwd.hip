@@ -370,11 +370,14 @@ __global__ __launch_bounds__(NW * 64, ATTN_FWD_MINW) void fwd_kernel(const typen
       mx = xhalf_max(mx);
       const float mt = ALIBI ? mx + bshift : mx * scale_log2;
       const float grow = mt - m_run[qb];
-      bool need = grow > kRescaleSlack;
+      bool need;
       if constexpr (exact_dominant_weight<E>()) {
-        // l = f 2^e with f in [0.5, 1), so log2 l >= e - 1
+        // l = f 2^e with f in [0.5, 1), so log2 l >= e - 1.  Both tests as one
+        // threshold: grow > slack, or grow > 0 and grow > log2(theta) + e - 1
         const int e = __builtin_amdgcn_frexp_expf(l_run[qb]);
-        need = need | ((grow > 0.f) & (grow > kLog2DominantFraction + (float)(e - 1)));
+        need = grow > __builtin_amdgcn_fmed3f((kLog2DominantFraction - 1.0f) + (float)e, 0.0f, kRescaleSlack);
+      } else {
+        need = grow > kRescaleSlack;
       }
       if (__builtin_amdgcn_ballot_w64(need) != 0) {
         const float mn = fmaxf(m_run[qb], mt);
