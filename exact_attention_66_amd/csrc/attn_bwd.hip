@@ -80,9 +80,6 @@ constexpr float kLog2e = 1.44269504088896340736f;
 #ifndef ATTN_DQ_KSTAGE
 #define ATTN_DQ_KSTAGE 2  // K and V operand fragments read ahead per batch
 #endif
-#ifndef ATTN_DKDV16
-#define ATTN_DKDV16 0     // dK/dV with 16x16 products, two waves per SIMD (contiguous, no ALiBi or dropout)
-#endif
 
 // ---------------------------------------------------------------- prep
 // One workgroup per (batch*head, 64-token block) of the padded length
@@ -97,12 +94,8 @@ constexpr float kLog2e = 1.44269504088896340736f;
 // dO, K and V ([B*H][64][d]): the main kernels take their last partial tile
 // from there and never read past the end of an input.  TAIL (N not a
 // multiple of 64) is a template flag, so that the checks cost nothing when
-// there is no padding.  Column order of the transposed copies: within each
-// 16 tokens, the 16-byte chunk 8h + i holds tokens 8 (i / 4) + 4h + i % 4;
-// with ORDER16 (the dK/dV kernel with 16x16 products), Q^T and dO^T instead
-// hold, within each 32 tokens, tokens 16 (i / 4) + 4g + i % 4 in chunk
-// 8g + i.
-template <typename E, int D, bool TAIL, bool STRIDED, bool ORDER16>
+// there is no padding.
+template <typename E, int D, bool TAIL, bool STRIDED>
 __global__ __launch_bounds__(256) void bwd_prep(const typename E::T* __restrict__ Q,
                                                 const typename E::T* __restrict__ K,
                                                 const typename E::T* __restrict__ V,
@@ -203,15 +196,10 @@ __global__ __launch_bounds__(256) void bwd_prep(const typename E::T* __restrict_
     for (int st = w; st < STEPS; st += 4) {
       const int pg = st / (D / 32);
       const int db = st % (D / 32);
-      // the two 4-token halves of this lane's chunk and the chunk's column
-      // (K^T, read by the dQ kernel, keeps the first order)
-      const bool o16 = ORDER16 && t != 1;
-      const int rr = o16 ? 32 * (pg >> 1) + 8 * (pg & 1) + tr_row : pg * 16 + tr_row;
-      const int second = o16 ? 16 : 8;
-      const int col = o16 ? 32 * (pg >> 1) + 16 * (pg & 1) + 8 * h : pg * 16 + 8 * h;
+      const int rr = pg * 16 + tr_row;
       const v8 val = concat44<E>(E::tr_read(&tile[t][swz<D>(rr, db * 32 + tr_col)]),
-                                 E::tr_read(&tile[t][swz<D>(rr + second, db * 32 + tr_col)]));
-      *(v8*)(outs[t] + headp + (size_t)(db * 32 + r) * Np + row0 + col) = val;
+                                 E::tr_read(&tile[t][swz<D>(rr + 8, db * 32 + tr_col)]));
+      *(v8*)(outs[t] + headp + (size_t)(db * 32 + r) * Np + row0 + pg * 16 + 8 * h) = val;
     }
   }
 }
@@ -682,321 +670,6 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv(
   }
 }
 
-// ---------------------------------------------------------------- dK, dV with 16x16 products
-// Two waves per SIMD: 8 waves of 16 keys each, over the same units
-// (batch*head, 128 keys) and the same double-buffered LDS tiles as the
-// kernel above.  The products are v_mfma_f32_16x16x32, so a wave's dK, dV
-// accumulators take 64 registers and two waves share a SIMD, each covering
-// the other's LDS waits and softmax work.  Per 32-query sub-tile a wave
-// computes, in two 16-query halves t (queries 16t .. 16t + 15),
-//   S  = -lse / scale + Q K^T      (A: Q rows from LDS, B: the wave's K rows)
-//   dP = -D + dO V^T
-// so that lane (c = lane % 16, g = lane / 16) holds key kw0 + c against
-// queries 16t + 4g + j, j = 0..3.  Its 8 values, P and dS, are directly the
-// B operands of
-//   dV^T += dO^T P   and   dK^T += Q^T dS
-// with reduction slot 8g + i standing for query 16 (i / 4) + 4g + i % 4:
-// the column order the preprocess writes with ORDER16, so that each A
-// operand is one 16-byte row read of a transposed tile.  The accumulators
-// hold dK^T and dV^T: a lane keeps its key's 4 consecutive d of every
-// 16-wide d block, which go out as 8-byte stores.  A tile's copies go out at
-// the barrier that releases its buffer, one tile ahead of its use.
-template <typename E, int D, bool CAUSAL, bool TAIL>
-__global__ __launch_bounds__(512, 2) void bwd_dkdv16(
-    const typename E::T* __restrict__ Q, const typename E::T* __restrict__ K,
-    const typename E::T* __restrict__ V, const typename E::T* __restrict__ dO,
-    const typename E::T* __restrict__ QT, const typename E::T* __restrict__ dOT,
-    const typename E::T* __restrict__ QTail, const typename E::T* __restrict__ dOTail,
-    const float* __restrict__ NLSE, const float* __restrict__ Dvec, typename E::T* __restrict__ dK,
-    typename E::T* __restrict__ dV, int BH, int N, int Np_arg, int nkb, float scale, float scale_log2) {
-  using T = typename E::T;
-  using v8 = typename E::v8;
-  using v4 = typename E::v4;
-  constexpr int NW = 8;                // waves per workgroup
-  constexpr int BMQ = 64;              // queries per tile
-  constexpr int BN = NW * 16;          // keys per workgroup
-  const int Np = TAIL ? Np_arg : N;    // padded length: N itself unless TAIL
-  static_assert(!CAUSAL || BN == 2 * BMQ, "causal: exactly two diagonal tiles per workgroup");
-  constexpr int KS = D / 32;           // 32-deep reduction steps over d
-  constexpr int DB = D / 16;           // 16-wide d blocks of dK^T, dV^T
-  constexpr int LR = D + 8;            // padded row-major row (elements)
-  constexpr int LT = BMQ + 8;          // padded transposed row (elements)
-  constexpr int RSL = LR / 8;          // 16-byte slots per row-major row
-  constexpr int TSL = LT / 8;          // 16-byte slots per transposed row
-  constexpr int RI = (BMQ * RSL + 63) / 64;  // 64-slot copy blocks per row-major tile
-  constexpr int TI = (D * TSL + 63) / 64;    // per transposed tile
-  constexpr int RC = (RI + NW - 1) / NW;     // blocks per wave
-  constexpr int TC = (TI + NW - 1) / NW;
-  constexpr int RSZ = RI * 64 * 8;     // elements per row-major tile buffer
-  constexpr int TSZ = TI * 64 * 8;
-
-  __shared__ __attribute__((aligned(16))) T lq0[RSZ], lq1[RSZ], ldo0[RSZ], ldo1[RSZ];
-  __shared__ __attribute__((aligned(16))) T lqt0[TSZ], lqt1[TSZ], ldot0[TSZ], ldot1[TSZ];
-  __shared__ __attribute__((aligned(16))) float ll0[64], ll1[64], ld0[64], ld1[64];
-
-  const int lane = threadIdx.x & 63;
-  const int wu = wave_id();
-  const int c = lane & 15;
-  const int g = lane >> 4;
-
-  int round = 0;
-  int unit = xcd_snake_unit((int)blockIdx.x, (int)gridDim.x, BH * nkb, 0);
-  if (unit < 0) return;
-  const int nqt = Np / BMQ;             // query tiles (the last may be padded)
-  const int nfull = N / BMQ;            // tiles wholly inside the sequence
-  int kb0, kw0, it0, ntile, nmask;
-  size_t head;
-  const T *Qh, *dOh, *QTh, *dOTh, *Qtl, *dOtl;
-  const float *lse_h, *dd_h;
-  auto set_unit = [&](const int u) {
-    const int bh = u / nkb;
-    kb0 = (u % nkb) * BN;
-    kw0 = kb0 + wu * 16;                 // first key of this wave
-    head = (size_t)bh * (size_t)N * D;
-    const size_t headp = (size_t)bh * (size_t)Np * D;
-    Qh = Q + head;
-    dOh = dO + head;
-    QTh = QT + headp;
-    dOTh = dOT + headp;
-    Qtl = QTail + (size_t)bh * BMQ * D;
-    dOtl = dOTail + (size_t)bh * BMQ * D;
-    lse_h = NLSE + (size_t)bh * Np;
-    dd_h = Dvec + (size_t)bh * Np;
-    it0 = CAUSAL ? kb0 / BMQ : 0;        // earlier tiles lie entirely above the diagonal
-    ntile = nqt - it0;
-    nmask = CAUSAL ? min(2, ntile) : 0;  // the first two tiles reach the diagonal
-  };
-  set_unit(unit);
-
-  f32x4 dk_acc[DB], dv_acc[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) {
-    dk_acc[db] = f32x4{};
-    dv_acc[db] = f32x4{};
-  }
-
-  // per-lane byte offsets of the tile copies, the same for every tile (the
-  // padding slot of a row gets a duplicate of the row's last chunk)
-  unsigned roff[RC], toff[TC];
-#pragma unroll
-  for (int cc = 0; cc < RC; ++cc) {
-    const int s = 64 * (wu + NW * cc) + lane;
-    const int row = min(s / RSL, BMQ - 1);
-    const int col = min(s % RSL, RSL - 2);
-    roff[cc] = (unsigned)(row * D + col * 8) * 2u;
-  }
-#pragma unroll
-  for (int cc = 0; cc < TC; ++cc) {
-    const int s = 64 * (wu + NW * cc) + lane;
-    const int row = min(s / TSL, D - 1);
-    const int col = min(s % TSL, TSL - 2);
-    toff[cc] = ((unsigned)row * (unsigned)Np + (unsigned)(col * 8)) * 2u;
-  }
-  // a whole tile: Q, dO rows (a padded last tile from the zero-padded tail
-  // tiles), Q^T, dO^T columns and the statistics
-  auto copy_tile = [&](const int it, auto bufc) {
-    constexpr int b = decltype(bufc)::value;
-    const bool tl = TAIL && it >= nfull;
-    const char* gq = (const char*)(tl ? Qtl : Qh + (size_t)it * BMQ * D);
-    const char* gd = (const char*)(tl ? dOtl : dOh + (size_t)it * BMQ * D);
-    const char* gqt = (const char*)(QTh + (size_t)it * BMQ);
-    const char* gdt = (const char*)(dOTh + (size_t)it * BMQ);
-#pragma unroll
-    for (int cc = 0; cc < RC; ++cc)
-      if (wu + NW * cc < RI) {
-        lds_copy16(gq, roff[cc], (b ? lq1 : lq0) + (wu + NW * cc) * 512);
-        lds_copy16(gd, roff[cc], (b ? ldo1 : ldo0) + (wu + NW * cc) * 512);
-      }
-#pragma unroll
-    for (int cc = 0; cc < TC; ++cc)
-      if (wu + NW * cc < TI) {
-        lds_copy16(gqt, toff[cc], (b ? lqt1 : lqt0) + (wu + NW * cc) * 512);
-        lds_copy16(gdt, toff[cc], (b ? ldot1 : ldot0) + (wu + NW * cc) * 512);
-      }
-    if (wu == 0) lds_copy4(lse_h + (size_t)it * BMQ, 4u * lane, b ? ll1 : ll0);
-    if (wu == NW - 1) lds_copy4(dd_h + (size_t)it * BMQ, 4u * lane, b ? ld1 : ld0);
-  };
-
-  // per-lane parts of the LDS read addresses; the rest is an immediate
-  const int offA = opaque(c * LR + 8 * g);   // row-major tiles: row c, d 8g
-  const int offT = opaque(c * LT + 8 * g);   // transposed tiles: row (d) c, column 8g
-  const int offS = opaque(g);                // statistics: queries 4g .. 4g + 3 (16-byte units)
-
-  // this wave's K and V as B operands: lane holds key kw0 + c, d = 32ks + 8g .. +7
-  v8 kB[KS], vB[KS];
-  auto load_kv = [&]() {
-    const int key = min(kw0 + c, N - 1);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      kB[ks] = *(const v8*)(K + head + (size_t)key * D + ks * 32 + 8 * g);
-      vB[ks] = *(const v8*)(V + head + (size_t)key * D + ks * 32 + 8 * g);
-    }
-  };
-
-  // Q, dO rows (A operands of S, dP) and the statistics of a sub-tile, read
-  // one sub-tile ahead of their use
-  v8 qa[2][KS], da[2][KS];
-  f32x4 ls[2], dls[2];
-  auto read_q = [&](auto bufc, const int qs) {
-    constexpr int b = decltype(bufc)::value;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        qa[t][ks] = *(const v8*)((b ? lq1 : lq0) + offA + (qs * 32 + 16 * t) * LR + 32 * ks);
-  };
-  auto read_do = [&](auto bufc, const int qs) {
-    constexpr int b = decltype(bufc)::value;
-    const f32x4* const lp = (const f32x4*)(b ? ll1 : ll0) + offS;
-    const f32x4* const dp = (const f32x4*)(b ? ld1 : ld0) + offS;
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        da[t][ks] = *(const v8*)((b ? ldo1 : ldo0) + offA + (qs * 32 + 16 * t) * LR + 32 * ks);
-      ls[t] = lp[qs * 8 + 4 * t];
-      dls[t] = dp[qs * 8 + 4 * t];
-    }
-  };
-
-  // One 32-query sub-tile in four MFMA groups, each with the LDS reads or
-  // the softmax work of a later group interleaved:
-  //   S  = Q K^T     | dO^T fragments (A of dV^T)
-  //   dP = dO V^T    | P; Q^T fragments (A of dK^T)
-  //   dV^T += dO^T P | dS; next sub-tile's Q rows
-  //   dK^T += Q^T dS | next sub-tile's dO rows and statistics
-  // The second sub-tile of a tile meets the other waves between dP and dV:
-  // every read of the tile has then completed, the tile after it (other
-  // buffer) has arrived, and the copy of the tile after that goes into the
-  // buffer just released.
-  auto sub_tile = [&](const int it, auto maskc, auto bufc, auto qsc) {
-    constexpr int b = decltype(bufc)::value;
-    constexpr int qs = decltype(qsc)::value;
-    using NB = std::integral_constant<int, qs == 0 ? b : (b ^ 1)>;   // buffer of the next sub-tile
-    constexpr int nqs = qs ^ 1;
-    const T* const lqt = b ? lqt1 : lqt0;
-    const T* const ldot = b ? ldot1 : ldot0;
-    const int q0s = it * BMQ + qs * 32;  // first query of the sub-tile
-
-    f32x4 sacc[2] = {ls[0], ls[1]}, dpacc[2] = {dls[0], dls[1]};
-    v8 doa[DB];
-#pragma unroll
-    for (int db = 0; db < DB; ++db) doa[db] = *(const v8*)(ldot + offT + 16 * db * LT + qs * 32);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) sacc[t] = E::mfma16(qa[t][ks], kB[ks], sacc[t]);
-    sched_interleave<2 * KS, kSchedMfma, 1, kSchedDsRead, DB / (2 * KS)>();
-    sched_fence();
-
-    v8 qta[DB];
-#pragma unroll
-    for (int db = 0; db < DB; ++db) qta[db] = *(const v8*)(lqt + offT + 16 * db * LT + qs * 32);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) dpacc[t] = E::mfma16(da[t][ks], vB[ks], dpacc[t]);
-    float p[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) p[i] = fast_exp2(sacc[i >> 2][i & 3] * scale_log2);
-    if constexpr (decltype(maskc)::value) {  // key > query -> P = 0
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if (kw0 + c > q0s + 16 * (i >> 2) + 4 * g + (i & 3)) p[i] = 0.f;
-    }
-    const v8 pb = pack8<E>(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
-    sched_interleave<2 * KS, kSchedMfma, 1, kSchedDsRead, DB / (2 * KS), kSchedValu, 3>();
-    sched_fence();
-
-    if constexpr (qs == 1) {
-      mfma_drain();
-      wait_all_vmem_loads();
-      __syncthreads();
-      sched_fence();
-      if (it + 2 < nqt) copy_tile(it + 2, bufc);
-    }
-
-    // (after the last sub-tile the reads ahead are stale but in bounds and unused)
-    read_q(NB{}, nqs);
-#pragma unroll
-    for (int db = 0; db < DB; ++db) dv_acc[db] = E::mfma16(doa[db], pb, dv_acc[db]);
-    float ds[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) ds[i] = p[i] * dpacc[i >> 2][i & 3];
-    const v8 sb = pack8<E>(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
-    sched_interleave<DB, kSchedMfma, 1, kSchedDsRead, 2 * KS / DB, kSchedValu, 2>();
-    sched_fence();
-
-    read_do(NB{}, nqs);
-#pragma unroll
-    for (int db = 0; db < DB; ++db) dk_acc[db] = E::mfma16(qta[db], sb, dk_acc[db]);
-    sched_interleave<DB, kSchedMfma, 1, kSchedDsRead, (2 * KS + 2) / DB>();
-    sched_fence();
-  };
-  using Q0 = std::integral_constant<int, 0>;
-  using Q1 = std::integral_constant<int, 1>;
-  auto tile = [&](const int it, auto maskc, auto bufc) {
-    sub_tile(it, maskc, bufc, Q0{});
-    sub_tile(it, maskc, bufc, Q1{});
-  };
-
-  using B0 = std::integral_constant<int, 0>;
-  using B1 = std::integral_constant<int, 1>;
-  using MaskOn = std::integral_constant<bool, true>;
-  using MaskOff = std::integral_constant<bool, false>;
-
-  copy_tile(it0, B0{});
-  load_kv();
-  for (;;) {
-    wait_all_vmem_loads();
-    __syncthreads();
-    read_q(B0{}, 0);
-    read_do(B0{}, 0);
-    if (ntile > 1) copy_tile(it0 + 1, B1{});
-
-    // tiles it0 .. nqt-1 on buffers 0, 1, 0, ...; the diagonal ones first
-    int it = it0;
-    if (nmask > 0) tile(it++, MaskOn{}, B0{});
-    if (nmask > 1) tile(it++, MaskOn{}, B1{});
-    for (; it + 1 < nqt; it += 2) {
-      tile(it, MaskOff{}, B0{});
-      tile(it + 1, MaskOff{}, B1{});
-    }
-    if (it < nqt) tile(it, MaskOff{}, B0{});
-
-    // every wave has passed the last tile's barrier: start the next unit,
-    // then store this one's dK = scale * acc, dV = acc (lane holds key
-    // kw0 + c, d = 16db + 4g .. +3)
-    const size_t out = head + (size_t)kw0 * D + 4 * g;
-    const bool valid = kw0 + c < N;
-    unit = xcd_snake_unit((int)blockIdx.x, (int)gridDim.x, BH * nkb, ++round);
-    if (unit >= 0) {
-      set_unit(unit);
-      copy_tile(it0, B0{});
-      load_kv();
-    }
-    if (valid) {
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        v4 kv, vv;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          kv[j] = (T)(dk_acc[db][j] * scale);
-          vv[j] = (T)dv_acc[db][j];
-        }
-        *(v4*)(dK + out + (size_t)c * D + 16 * db) = kv;
-        *(v4*)(dV + out + (size_t)c * D + 16 * db) = vv;
-      }
-    }
-    if (unit < 0) break;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      dk_acc[db] = f32x4{};
-      dv_acc[db] = f32x4{};
-    }
-  }
-}
-
 // ---------------------------------------------------------------- dQ
 // Shaped like the forward: each wave keeps 32 queries' Q and dO rows as B
 // operands and dQ^T in accumulators, computes
@@ -1350,7 +1023,6 @@ __global__ __launch_bounds__(NW * 64, ATTN_DQ_MINW) void bwd_dq(
 template <typename E, int D, bool CAUSAL, bool TAIL, bool STRIDED, bool ALIBI, bool DROP>
 hipError_t launch_bwd_cfg(const BwdArgs& a) {
   constexpr int NWK = 4;            // dK/dV: waves per workgroup (32 keys each)
-  constexpr bool K16 = ATTN_DKDV16 && !STRIDED && !ALIBI && !DROP;
   constexpr int NWQ = ATTN_DQ_NW;
   constexpr int BNQ = ATTN_DQ_BN;
   const int BH = (int)(a.B * a.H);
@@ -1399,19 +1071,11 @@ hipError_t launch_bwd_cfg(const BwdArgs& a) {
                     (void*)&dotail, (void*)&ktail, (void*)&vtail, (void*)&N, (void*)&Np, (void*)&inv_scale,
                     (void*)&lq, (void*)&lk, (void*)&lv, (void*)&lo, (void*)&ldo, (void*)&H, (void*)&qc, (void*)&kc,
                     (void*)&vc, (void*)&doc};
-    hipError_t e = launch_kernel((const void*)bwd_prep<E, D, TAIL, STRIDED, K16>, dim3((unsigned)(BH * (Np / 64))),
-                                 dim3(256), args, a.stream, 1);
+    hipError_t e = launch_kernel((const void*)bwd_prep<E, D, TAIL, STRIDED>, dim3((unsigned)(BH * (Np / 64))), dim3(256), args,
+                                 a.stream, 1);
     if (e != hipSuccess) return e;
   }
-  if constexpr (K16) {
-    const int nkb = (N + 127) / 128;
-    void* args[] = {(void*)&q2,    (void*)&k2,     (void*)&v2,   (void*)&dO2,   (void*)&qt, (void*)&dot,
-                    (void*)&qtail, (void*)&dotail, (void*)&nlse, (void*)&delta, (void*)&dk, (void*)&dv,
-                    (void*)&BH,    (void*)&N,      (void*)&Np,   (void*)&nkb,   (void*)&scale, (void*)&scale_log2};
-    const void* fn = (const void*)bwd_dkdv16<E, D, CAUSAL, TAIL>;
-    hipError_t e = launch_kernel(fn, dim3((unsigned)persistent_grid(fn, 512, nkb * BH)), dim3(512), args, a.stream, 2);
-    if (e != hipSuccess) return e;
-  } else {
+  {
     const int nkb = (N + NWK * 32 - 1) / (NWK * 32);
     void* args[] = {(void*)&q2,    (void*)&k2, (void*)&v2, (void*)&dO2, (void*)&qt,  (void*)&dot,
                     (void*)&qtail, (void*)&dotail, (void*)&nlse, (void*)&delta, (void*)&dk, (void*)&dv,

@@ -8,10 +8,6 @@
 //     A: lane holds A[r][8h + i],  i = 0..7
 //     B: lane holds B[8h + i][r],  i = 0..7
 //     D: lane holds D[8*(j/4) + 4h + j%4][r],  j = 0..15
-//   v_mfma_f32_16x16x32_{bf16,f16}:  D[16x16] += A[16x32] * B[32x16]
-//   (c = lane % 16, g = lane / 16)
-//     A: lane holds A[c][8g + i],  B: lane holds B[8g + i][c],  i = 0..7
-//     D: lane holds D[4g + j][c],  j = 0..3
 // Because the reduction index enters A and B the same way, any fixed
 // relabelling of the 16 reduction slots is harmless as long as both operands
 // use it; the kernels relabel keys so that a score accumulator can be fed
@@ -45,9 +41,6 @@ struct bf16_t {
   static __device__ __forceinline__ f32x16 mfma32(v8 a, v8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   }
-  static __device__ __forceinline__ f32x4 mfma16(v8 a, v8 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-  }
   static __device__ __forceinline__ v4 tr_read(const T* lds_ptr) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((ATTN_LDS v4*)(lds_ptr));
   }
@@ -63,9 +56,6 @@ struct f16_t {
   typedef _Float16 v2 __attribute__((ext_vector_type(2)));
   static __device__ __forceinline__ f32x16 mfma32(v8 a, v8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ f32x4 mfma16(v8 a, v8 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
   }
   typedef __fp16 raw4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
   static __device__ __forceinline__ v4 tr_read(const T* lds_ptr) {
