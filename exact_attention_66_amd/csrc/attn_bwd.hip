@@ -732,6 +732,7 @@ __global__ __launch_bounds__(NW * 64, ATTN_DQ_MINW) void bwd_dq(
   if (unit < 0) return;
   const int nfull = N / BN;   // key tiles wholly inside the sequence
   int bh, q0, qw0, kv_end, ntiles, q_last;
+  bool desc = false;    // this unit walks its key tiles last to first
   float nslope2 = 0.f;   // ALIBI: -slope * log2(e) of this unit's head
   bool wave_valid;
   size_t head;
@@ -751,6 +752,13 @@ __global__ __launch_bounds__(NW * 64, ATTN_DQ_MINW) void bwd_dq(
     Vtl = VTail + (size_t)bh * BN * D;
     kv_end = CAUSAL ? min(N, q0 + BM) : N;
     ntiles = (kv_end + BN - 1) / BN;
+    // Units of odd rounds walk their key tiles last to first.  With the
+    // heaviest-first snake order, the workgroups of an XCD start the units
+    // of an even round together and end those of an odd round together, so
+    // in either direction they sweep the same key tile at about the same
+    // time and its K, V, K^T come from HBM about once per round instead of
+    // once per unit.
+    desc = (round & 1) != 0;
     q_last = qw0 + 31;
   };
   set_unit(unit);
@@ -935,26 +943,30 @@ __global__ __launch_bounds__(NW * 64, ATTN_DQ_MINW) void bwd_dq(
     ndd = ND[(size_t)bh * Np + qrow];
   };
 
-  auto k_tile = [&](const int t, auto bufc) {
+  // key tile of the unit's sq-th step
+  auto tile_of = [&](const int sq) { return desc ? ntiles - 1 - sq : sq; };
+  auto k_tile = [&](const int sq, auto bufc) {
     constexpr int buf = decltype(bufc)::value;
-    // buffer (t + 2) % 3 held tile t - 1, which every wave has finished; the
-    // copy of tile t + 2 into it goes out in three parts: K before the first
-    // key block, V before the second, K^T after the last
+    const int t = tile_of(sq);
+    // buffer (sq + 2) % 3 held the tile of step sq - 1, which every wave has
+    // finished; the copy of step sq + 2's tile into it goes out in three
+    // parts: K before the first key block, V before the second, K^T after
+    // the last
     constexpr int NB = (buf + 2) % NBUF;
-    const bool more = t + 2 < ntiles;
-    if (more) copy_part(t + 2, NB, 0);
+    const bool more = sq + 2 < ntiles;
+    if (more) copy_part(tile_of(sq + 2), NB, 0);
     const int k0 = t * BN;
     const bool run = wave_valid && (!CAUSAL || k0 <= q_last);
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      if (kb == KB / 2 && more) copy_part(t + 2, NB, 1);
+      if (kb == KB / 2 && more) copy_part(tile_of(sq + 2), NB, 1);
       const int kbk0 = k0 + kb * 32;
       if (run && (!CAUSAL || kbk0 <= q_last) && (!TAIL || kbk0 < N)) key_block(buf, kb, kbk0);
     }
-    if (more) copy_part(t + 2, NB, 2);
+    if (more) copy_part(tile_of(sq + 2), NB, 2);
     mfma_drain();
-    // tile t + 1 must be in LDS: its copies are the ones before the most recent
-    if (t + 2 < ntiles) wait_copies_but_last();
+    // step sq + 1's tile must be in LDS: its copies are the ones before the most recent
+    if (more) wait_copies_but_last();
     else wait_all_vmem_loads();
     __syncthreads();
   };
@@ -962,8 +974,8 @@ __global__ __launch_bounds__(NW * 64, ATTN_DQ_MINW) void bwd_dq(
   using B1 = std::integral_constant<int, 1>;
   using B2 = std::integral_constant<int, 2>;
 
-  copy_tile(0, 0);
-  if (ntiles > 1) copy_tile(1, 1);
+  copy_tile(tile_of(0), 0);
+  if (ntiles > 1) copy_tile(tile_of(1), 1);
   load_q();
   for (;;) {
     wait_all_vmem_loads();
@@ -979,14 +991,14 @@ __global__ __launch_bounds__(NW * 64, ATTN_DQ_MINW) void bwd_dq(
     }
     __syncthreads();
 
-    int t = 0;
-    for (; t + 2 < ntiles; t += 3) {
-      k_tile(t, B0{});
-      k_tile(t + 1, B1{});
-      k_tile(t + 2, B2{});
+    int sq = 0;
+    for (; sq + 2 < ntiles; sq += 3) {
+      k_tile(sq, B0{});
+      k_tile(sq + 1, B1{});
+      k_tile(sq + 2, B2{});
     }
-    if (t < ntiles) k_tile(t, B0{});
-    if (t + 1 < ntiles) k_tile(t + 1, B1{});
+    if (sq < ntiles) k_tile(sq, B0{});
+    if (sq + 1 < ntiles) k_tile(sq + 1, B1{});
 
     // every wave has passed the last tile's barrier: start the next unit,
     // then store this one's dQ = scale * dQ^T (lane holds query qw0 + r,
@@ -997,8 +1009,8 @@ __global__ __launch_bounds__(NW * 64, ATTN_DQ_MINW) void bwd_dq(
     unit = xcd_snake_unit((int)blockIdx.x, (int)gridDim.x, BH * nqb, ++round);
     if (unit >= 0) {
       set_unit(unit);
-      copy_tile(0, 0);
-      if (ntiles > 1) copy_tile(1, 1);
+      copy_tile(tile_of(0), 0);
+      if (ntiles > 1) copy_tile(tile_of(1), 1);
       load_q();
     }
     if (valid) {
