@@ -400,7 +400,8 @@ __global__ __launch_bounds__(NW * 64, ATTN_FWD_MINW) void fwd_kernel(const typen
       for (int kk = 0; kk < 2; ++kk)
         pf[kk][qb] = pack8<E>(p[8 * kk + 0], p[8 * kk + 1], p[8 * kk + 2], p[8 * kk + 3], p[8 * kk + 4],
                               p[8 * kk + 5], p[8 * kk + 6], p[8 * kk + 7]);
-      lr_run[qb] += sum8<E>(pf[0][qb], 0.f) + sum8<E>(pf[1][qb], 0.f);
+      // one chain of dot products straight into the running sum (no zeroed partials)
+      lr_run[qb] = sum8<E>(pf[1][qb], sum8<E>(pf[0][qb], lr_run[qb]));
       if constexpr (DROP) {
         const u32x4 tw = dtw[qb];
         const uint32_t add = (256u - drop.t) * 0x00010001u;
