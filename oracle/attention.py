@@ -69,6 +69,7 @@ __all__ = [
     "forward_head",
     "forward_head_rows",
     "backward_head",
+    "backward_head_rows",
     "forward",
     "backward",
     "online_softmax_forward_head",
@@ -171,13 +172,48 @@ def forward_head(q, k, v, scale: float, causal: bool, row_block: Optional[int] =
     return o, lse
 
 
-def backward_head(q, k, v, do, scale: float, causal: bool, row_block: Optional[int] = None, alibi_slope=None,
-                  dropout=None):
-    """dQ, dK, dV [N,d] of one head for upstream gradient dO (exact chain rule).
+def backward_head_rows(q, k, v, do, scale: float, causal: bool, rows, alibi_slope=None, dropout=None):
+    """The listed query rows' share of the backward pass of one head (exact chain rule).
+
+    Returns ``(dq, dk, dv)``: the rows' dQ (``[len(rows), d]``; complete, since
+    a row's dQ depends on that row alone) and their contributions to dK and dV
+    (``[kv, d]``, keys past ``kv`` get nothing from these rows).  dK and dV are
+    sums over the query rows, so the contributions of all rows add up to
+    them; with the causal mask only rows ``i >= j`` reach key ``j``, so the
+    rows ``j0 .. N-1`` alone give the complete dK and dV of the keys
+    ``j >= j0``.
 
     With dropout (keep factor F = Z * 256 / (256 - t), O = (P o F) V):
     ``dV = (P o F)^T dO``, ``dP = F o (dO V^T)``, and the rest as without;
     ``D_i = sum_j P_ij dP_ij`` still equals ``dO_i . O_i``.
+    """
+    q = _f64(q)
+    k = _f64(k)
+    v = _f64(v)
+    do = _f64(do)
+    n, nk = q.shape[0], k.shape[0]
+    rows = np.asarray(rows, dtype=np.int64)
+    kv = visible_keys(rows, n, nk, causal)   # keys past kv have P = 0 in these rows
+    s = masked_scores(q, k[:kv], scale, causal, rows, alibi_slope, nk_total=nk)
+    p, _, _ = row_softmax(s)
+    zf = dropout_factor(rows, n, nk, dropout)
+    if zf is not None:
+        zf = zf[:, :kv]
+    dv = (p if zf is None else p * zf).T @ do[rows]
+    dp = do[rows] @ v[:kv].T
+    if zf is not None:
+        dp = dp * zf
+    dsum = (p * dp).sum(axis=1)          # D_i = sum_j P_ij dP_ij
+    ds = p * (dp - dsum[:, None])
+    dq = float(scale) * (ds @ k[:kv])
+    dk = float(scale) * (ds.T @ q[rows])
+    return dq, dk, dv
+
+
+def backward_head(q, k, v, do, scale: float, causal: bool, row_block: Optional[int] = None, alibi_slope=None,
+                  dropout=None):
+    """dQ, dK, dV [N,d] of one head for upstream gradient dO (exact chain rule):
+    the shares of all query rows (``backward_head_rows``) put together.
 
     ``row_block`` evaluates the same sums ``dV = sum_i P_i^T dO_i`` and
     ``dK = scale * sum_i dS_i^T Q_i`` over groups of query rows, to bound
@@ -185,30 +221,18 @@ def backward_head(q, k, v, do, scale: float, causal: bool, row_block: Optional[i
     """
     q = _f64(q)
     k = _f64(k)
-    v = _f64(v)
-    do = _f64(do)
     n = q.shape[0]
     rb = n if row_block is None else min(row_block, n)
     dq = np.empty_like(q)
     dk = np.zeros_like(k)
-    dv = np.zeros_like(v)
-    nk = k.shape[0]
+    dv = np.zeros((k.shape[0], np.shape(v)[1]))
     for r0 in range(0, n, rb):
         rows = np.arange(r0, min(n, r0 + rb))
-        kv = visible_keys(rows, n, nk, causal)   # keys past kv have P = 0 in these rows
-        s = masked_scores(q, k[:kv], scale, causal, rows, alibi_slope, nk_total=nk)
-        p, _, _ = row_softmax(s)
-        zf = dropout_factor(rows, n, nk, dropout)
-        if zf is not None:
-            zf = zf[:, :kv]
-        dv[:kv] += (p if zf is None else p * zf).T @ do[rows]
-        dp = do[rows] @ v[:kv].T
-        if zf is not None:
-            dp = dp * zf
-        dsum = (p * dp).sum(axis=1)          # D_i = sum_j P_ij dP_ij
-        ds = p * (dp - dsum[:, None])
-        dq[rows] = float(scale) * (ds @ k[:kv])
-        dk[:kv] += float(scale) * (ds.T @ q[rows])
+        dq_r, dk_r, dv_r = backward_head_rows(q, k, v, do, scale, causal, rows, alibi_slope, dropout)
+        kv = dk_r.shape[0]
+        dq[rows] = dq_r
+        dk[:kv] += dk_r
+        dv[:kv] += dv_r
     return dq, dk, dv
 
 

@@ -1,9 +1,11 @@
 """Very long sequences (GPU): offsets and grid sizes far past the training workloads.
 
-A 262144-token causal head (forward rows sampled against the fp64 oracle;
-backward checked by invariants that hold at any size, since the oracle's
-gradients would need the whole N x N product) and a decoding step against a
-cache of 2^20 positions (every output row against the oracle).
+A 262144-token causal head and a decoding step against a cache of 2^20
+positions (every output row against the oracle).  For the long head the
+oracle evaluates what it can without the whole N x N product: O, lse and dQ
+of sampled query rows (a row's values depend on that row alone), and dK, dV
+of the last 64 keys (under the causal mask only the last 64 query rows reach
+them); the backward is also checked by invariants over every key.
 """
 import numpy as np
 import pytest
@@ -11,12 +13,12 @@ import torch
 
 import oracle
 import workloads
-from parity import check_lse, check_o, f64, log, require_gpu, sample_rows
+from parity import check_grad, check_lse, check_o, f64, log, require_gpu, sample_rows
 
 pytestmark = pytest.mark.gpu
 
 
-def test_long_sequence_forward_rows_and_backward_invariants():
+def test_long_sequence_sampled_rows_key_tail_and_invariants():
     ea = require_gpu()
     w = workloads.Workload("long", 1, 1, 1 << 18, 128, "bf16", True, True, seed=71001)
     x = workloads.make_inputs(w)
@@ -43,6 +45,15 @@ def test_long_sequence_forward_rows_and_backward_invariants():
     nv = dv[0, 0].double().norm().item()
     log(f"  |sum dK| / |dK| = {sk / nk:.2e}, |sum dV - sum dO| / |dV| = {sv / nv:.2e}")
     assert sk <= 2e-2 * nk and sv <= 2e-2 * nv
+    doh = workloads.to_f64_numpy(x["do"][0, 0])
+    dq_ref, _, _ = oracle.attention.backward_head_rows(qh, kh, vh, doh, w.scale, True, rows)
+    e = check_grad(f64(dq[0, 0][rows]), dq_ref, "dQ (sampled rows)")
+    log(f"  dQ of {len(rows)} rows: relative Frobenius error {e:.2e}")
+    j0 = w.N - 64
+    _, dk_ref, dv_ref = oracle.attention.backward_head_rows(qh, kh, vh, doh, w.scale, True, np.arange(j0, w.N))
+    ek = check_grad(f64(dk[0, 0][j0:]), dk_ref[j0:], "dK (last 64 keys)")
+    ev = check_grad(f64(dv[0, 0][j0:]), dv_ref[j0:], "dV (last 64 keys)")
+    log(f"  dK, dV of the last 64 keys: relative Frobenius errors {ek:.2e}, {ev:.2e}")
 
 
 def test_decode_against_a_million_positions():

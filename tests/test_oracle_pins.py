@@ -237,6 +237,33 @@ def test_row_blocks_equal_unblocked(causal):
         np.testing.assert_allclose(a, b, rtol=0, atol=1e-12)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_row_shares_give_row_gradients_and_the_causal_key_tail(causal):
+    """backward_head_rows on a subset of rows: their dQ rows are those of the
+    whole head (a row's dQ depends on that row alone), and under the causal
+    mask the rows j0 .. N-1 give the complete dK, dV of the keys j0 .. N-1.
+    Checked against the whole-head backward, which the autograd and finite
+    difference pins above fix; leaving out row j0 must change key j0's
+    gradients (so the tail check can fail)."""
+    rng = np.random.default_rng(3301)
+    n, d = 80, 32
+    q, k, v, do = (rng.standard_normal((n, d)) for _ in range(4))
+    scale = 1.0 / math.sqrt(d)
+    dq, dk, dv = A.backward_head(q, k, v, do, scale, causal)
+    rows = np.array([0, 7, 41, 79])
+    dq_r, _, _ = A.backward_head_rows(q, k, v, do, scale, causal, rows)
+    np.testing.assert_allclose(dq_r, dq[rows], rtol=1e-12, atol=1e-13)
+    if not causal:
+        return
+    j0 = 60
+    _, dk_t, dv_t = A.backward_head_rows(q, k, v, do, scale, True, np.arange(j0, n))
+    np.testing.assert_allclose(dk_t[j0:], dk[j0:], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(dv_t[j0:], dv[j0:], rtol=1e-12, atol=1e-13)
+    _, dk_m, dv_m = A.backward_head_rows(q, k, v, do, scale, True, np.arange(j0 + 1, n))
+    assert not np.allclose(dk_m[j0], dk[j0], rtol=1e-6, atol=1e-9)
+    assert not np.allclose(dv_m[j0], dv[j0], rtol=1e-6, atol=1e-9)
+
+
 def test_multihead_wrappers_match_heads():
     rng = np.random.default_rng(11)
     q, k, v, do = (rng.standard_normal((2, 3, 10, 4)) for _ in range(4))
