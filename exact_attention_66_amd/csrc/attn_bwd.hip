@@ -677,8 +677,9 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv(
 // scalars), and adds dQ^T += K^T dS^T (A operands from the K^T tile).  A
 // persistent grid, like the dK/dV kernel's: workgroups walk their units
 // (xcd_snake_unit) and start the next unit's loads before the dQ stores;
-// keeping a head's units on one XCD lets them share its K, V, K^T tiles in
-// that XCD's L2.  K, V [BN][D + 8] and
+// keeping a head's units on one XCD, and sweeping the key tiles in
+// alternate directions on alternate rounds, lets them share its K, V, K^T
+// tiles in that XCD's L2.  K, V [BN][D + 8] and
 // K^T [D][BN + 8] tiles (padded rows: conflict-free ds_read_b128, affine
 // addresses) reach LDS by direct global->LDS copies into three rotating
 // buffers, two tiles ahead of their use; a copy instruction fills 64
