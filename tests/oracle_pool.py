@@ -55,11 +55,12 @@ def _head_task(task):
     """Oracle of one head and its comparison with the GPU result (in a worker)."""
     from oracle import attention as A
 
-    (b, h, scale, causal, dtype, row_block, q, k, v, do, o_gpu, lse_gpu, grads, dropout, gain) = task
+    (b, h, scale, causal, dtype, row_block, q, k, v, do, o_gpu, lse_gpu, grads, dropout, gain, slope) = task
     q, k, v = (np.asarray(a, dtype=np.float64) for a in (q, k, v))
     out = {"b": b, "h": h}
     if o_gpu is not None:
-        o_ref, lse_ref = A.forward_head(q, k, v, scale, causal, row_block=row_block, dropout=dropout)
+        o_ref, lse_ref = A.forward_head(q, k, v, scale, causal, row_block=row_block, alibi_slope=slope,
+                                        dropout=dropout)
         err = np.abs(o_gpu.astype(np.float64) - o_ref)
         big = np.abs(o_ref) >= 4.0
         bound = np.where(big, half_ulp(o_ref, dtype) + 1e-3 * gain, 1e-2 * gain)
@@ -80,7 +81,7 @@ def _head_task(task):
         out["finite"] = bool(np.isfinite(o_gpu).all() and np.isfinite(lse_gpu).all())
     if grads is not None:
         ref = A.backward_head(q, k, v, np.asarray(do, dtype=np.float64), scale, causal, row_block=row_block,
-                              dropout=dropout)
+                              alibi_slope=slope, dropout=dropout)
         for name, g, gr in zip(("dq", "dk", "dv"), grads, ref):
             g = g.astype(np.float64)
             out[name + "_num"] = float(np.sum((g - gr) ** 2))
@@ -95,11 +96,11 @@ def _f32(t) -> np.ndarray:
 
 
 def compare_full(w, x, o=None, lse=None, grads=None, workers: Optional[int] = None,
-                 row_block: int = 512, dropout=None) -> Dict[str, float]:
+                 row_block: int = 512, dropout=None, alibi_slopes=None) -> Dict[str, float]:
     """Compare GPU outputs of workload ``w`` (inputs ``x``: CPU tensors of the I/O dtype) with the oracle
     over every head.  ``o``, ``lse``: the forward outputs (CPU tensors) or None; ``grads``: (dq, dk, dv)
     CPU tensors or None; ``dropout``: ``(p, seed, offset)`` or None (head (b, h) draws with index
-    b * H + h).  With dropout the O bounds other than the output rounding floor grow by the keep factor
+    b * H + h); ``alibi_slopes``: the H per-head slopes of a linear position bias, or None.  With dropout the O bounds other than the output rounding floor grow by the keep factor
     k = 256 / (256 - t) (every rounding made before the final multiplication by k is multiplied by it).
     Returns the whole-tensor metrics (see the module docstring)."""
     from oracle import philox
@@ -115,7 +116,8 @@ def compare_full(w, x, o=None, lse=None, grads=None, workers: Optional[int] = No
                        None if grads is None else _f32(x["do"][b, h]),
                        None if o is None else _f32(o[b, h]), None if lse is None else lse[b, h].numpy(),
                        None if grads is None else tuple(_f32(g[b, h]) for g in grads),
-                       None if dropout is None else (dropout[0], dropout[1], dropout[2], b * w.H + h), gain)
+                       None if dropout is None else (dropout[0], dropout[1], dropout[2], b * w.H + h), gain,
+                       None if alibi_slopes is None else float(alibi_slopes[h]))
 
     saved = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")}
     for k in saved:

@@ -3,8 +3,8 @@
 The bias -m_h |p_i - j| is added to the scaled scores before the softmax
 (p_i the query's position).  Slopes follow the usual geometric choice
 m_h = 2^(-8 (h + 1) / H); the oracle takes the same fp32 values.  Every
-element is compared on small and ragged shapes; the headline-sized
-training shape is checked on sampled heads.
+element is compared on small and ragged shapes and on the headline-sized
+training shape (through the per-head oracle pool).
 """
 import numpy as np
 import pytest
@@ -12,7 +12,8 @@ import torch
 
 import oracle
 import workloads
-from parity import check_grad, check_lse, check_o, f64, log, require_gpu
+from oracle_pool import compare_full
+from parity import GRAD_REL_FRO, LSE_MAX, O_MEAN, check_grad, check_lse, check_o, f64, log, require_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -65,23 +66,27 @@ def test_alibi_kvcache(Nq, Nk, splits):
     check_lse(f64(lse), lse_ref)
 
 
-def test_alibi_headline_shape_sampled_heads():
-    """B=4, H=32, N=4096, d=128 causal bf16 with ALiBi: two whole heads against the oracle."""
+@pytest.mark.timeout(900)
+def test_alibi_headline_shape_every_element():
+    """B=4, H=32, N=4096, d=128 causal bf16 with ALiBi: every element of O, lse, dQ, dK and dV
+    against the oracle, with the bounds of the full-size parity tests."""
     ea = require_gpu()
     w = workloads.WORKLOADS["causal_b4h32n4096d128"]
     x = workloads.make_inputs(w)
     sl = _slopes(w.H)
     q, k, v, do = (x[n].cuda() for n in ("q", "k", "v", "do"))
-    log("alibi headline shape B=4 H=32 N=4096 d=128")
+    log("alibi headline shape B=4 H=32 N=4096 d=128, every element")
     o, lse = ea.forward_alibi(q, k, v, sl, scale=w.scale, causal=True)
     dq, dk, dv = ea.backward_alibi(q, k, v, o, lse, do, sl, scale=w.scale, causal=True)
     torch.cuda.synchronize()
-    for b, h in ((0, 0), (3, 31)):
-        args = [_np(x[n][b, h]) for n in ("q", "k", "v")]
-        m = float(sl[h])
-        o_ref, lse_ref = oracle.forward_head(*args, w.scale, True, alibi_slope=m)
-        check_o(f64(o[b, h]), o_ref, "bf16")
-        check_lse(f64(lse[b, h]), lse_ref)
-        grads = oracle.backward_head(*args, _np(x["do"][b, h]), w.scale, True, alibi_slope=m)
-        for name, g, gr in zip(("dQ", "dK", "dV"), (dq[b, h], dk[b, h], dv[b, h]), grads):
-            check_grad(f64(g), gr, f"{name}[{b},{h}]")
+    m = compare_full(w, x, o.cpu(), lse.cpu(), tuple(g.cpu() for g in (dq, dk, dv)),
+                     alibi_slopes=sl.double().numpy())
+    log(f"  O over {m['o_elements']} elements: max|err| {m['o_max']:.3e} mean|err| {m['o_mean']:.3e}; "
+        f"lse max|err| {m['lse_max']:.3e}; rel. Frobenius dq {m['dq_rel_fro']:.3e} dk {m['dk_rel_fro']:.3e} "
+        f"dv {m['dv_rel_fro']:.3e}")
+    assert m["finite"] and all(m[g + "_finite"] for g in ("dq", "dk", "dv"))
+    assert m["o_over"] == 0, m.get("o_worst_over")
+    assert m["o_mean"] <= O_MEAN
+    assert m["lse_max"] <= LSE_MAX
+    for g in ("dq", "dk", "dv"):
+        assert m[g + "_rel_fro"] <= GRAD_REL_FRO, (g, m[g + "_rel_fro"])

@@ -57,3 +57,24 @@ def test_compare_full_rounding_floor_and_planted_errors():
     fro_head = np.linalg.norm(g_ref[1][0, 1]) / np.linalg.norm(g_ref[1])
     assert m2["dk_rel_fro"] == pytest.approx(0.5 * fro_head, rel=2e-2)
     assert m2["dk_worst_head"] == pytest.approx(0.5, rel=2e-2)
+
+
+def test_compare_full_passes_the_alibi_slopes_to_every_head():
+    """With per-head slopes the workers must evaluate the biased oracle: the
+    oracle's own biased result matches at the rounding floor, and the same
+    result compared without the slopes does not."""
+    w = workloads.Workload("pool_alibi", 2, 3, 80, 16, "bf16", True, True, seed=4243)
+    x = workloads.make_inputs(w)
+    a = {n: workloads.to_f64_numpy(x[n]) for n in ("q", "k", "v", "do")}
+    slopes = np.array([0.5, 0.25, 0.125])
+    o_ref, lse_ref = oracle.forward(a["q"], a["k"], a["v"], w.scale, True, alibi_slopes=slopes)
+    g_ref = oracle.backward(a["q"], a["k"], a["v"], a["do"], w.scale, True, alibi_slopes=slopes)
+    o = _rounded(o_ref, torch.bfloat16)
+    lse = torch.from_numpy(lse_ref.astype(np.float32))
+    grads = tuple(_rounded(g, torch.bfloat16) for g in g_ref)
+    m = compare_full(w, x, o, lse, grads, workers=2, alibi_slopes=slopes)
+    assert m["o_over"] == 0 and m["o_max"] <= m["o_floor"] + 1e-15 and m["lse_max"] < 1e-5
+    for g in ("dq", "dk", "dv"):
+        assert m[g + "_rel_fro"] < 4e-3
+    m_plain = compare_full(w, x, o, lse, grads, workers=2)
+    assert m_plain["o_over"] > 0 and m_plain["lse_max"] > 1e-2
