@@ -165,3 +165,29 @@ def test_backward_packed_qkv_and_packed_gradient():
     ref = _grads_ref(q, k, v, do, scale, True)
     for name, gg, gr in zip(("dQ", "dK", "dV"), (dqp, dkp, dvp), ref):
         check_grad(f64(gg), gr, name)
+
+
+def test_token_major_headline_size_bitwise_equal_to_contiguous():
+    """B=4, H=32, N=4096, d=128 causal bf16 (the headline workload, compared with the oracle over every
+    element in test_gpu_fullsize.py) with all eight tensors stored [B, N, H, d]: forward and backward
+    must give bitwise the contiguous call's results, and write every gradient element."""
+    ea = require_gpu()
+    w = workloads.WORKLOADS["causal_b4h32n4096d128"]
+    x = workloads.make_inputs(w)
+    log(f"strided headline size {w.name}: [B, N, H, d] storage, bitwise against the contiguous call")
+    nhd = lambda t: t.transpose(1, 2).contiguous().cuda().transpose(1, 2)
+    qs, ks, vs, dos = (nhd(x[n]) for n in ("q", "k", "v", "do"))
+    obuf = torch.full((w.B, w.N, w.H, w.d), float("nan"), dtype=qs.dtype, device="cuda")
+    o = obuf.transpose(1, 2)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
+    ea.attn_fwd(qs, ks, vs, o, lse, w.scale, True)
+    dq, dk, dv = ea.backward(qs, ks, vs, o, lse, dos, scale=w.scale, causal=True)
+    qc, kc, vc, doc = (x[n].cuda() for n in ("q", "k", "v", "do"))
+    oc, lc = ea.forward(qc, kc, vc, scale=w.scale, causal=True)
+    gc = ea.backward(qc, kc, vc, oc, lc, doc, scale=w.scale, causal=True)
+    torch.cuda.synchronize()
+    assert not torch.isnan(obuf).any(), "an output element was not written"
+    assert torch.equal(o, oc) and torch.equal(lse, lc), "strided forward differs from the contiguous call"
+    for name, gg, gcc in zip(("dQ", "dK", "dV"), (dq, dk, dv), gc):
+        assert dq.stride() == qs.stride()
+        assert torch.equal(gg.contiguous(), gcc), f"{name}: strided result differs from the contiguous call"
