@@ -135,3 +135,30 @@ def test_ragged_very_negative_scores(N, d, causal):
     check_lse(f64(lse), lse_ref)
     for name, g, gr in zip(("dQ", "dK", "dV"), (dq, dk, dv), oracle.backward(*xs, w.scale, causal)):
         check_grad(f64(g), gr, name)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("B,H,N,d,dt,causal", [(2, 8, 4000, 128, "bf16", True), (1, 8, 3001, 64, "fp16", False)])
+def test_ragged_large_every_element(B, H, N, d, dt, causal):
+    """A length that is not a multiple of 64 at a size past the tile pipelines' start-up (N = 4000,
+    3001): every element of O, lse, dQ, dK and dV against the oracle (per-head pool), with the
+    bounds of the full-size parity tests."""
+    from oracle_pool import compare_full
+    from parity import GRAD_REL_FRO, LSE_MAX, O_MEAN
+
+    ea = require_gpu()
+    w = workloads.Workload("ragged_large", B, H, N, d, dt, causal, True, seed=63000 + N + d)
+    log(f"ragged large {w}")
+    x = workloads.make_inputs(w)
+    q, k, v, do = (x[n].cuda() for n in ("q", "k", "v", "do"))
+    o, lse = ea.forward(q, k, v, scale=w.scale, causal=causal)
+    g = ea.backward(q, k, v, o, lse, do, scale=w.scale, causal=causal)
+    torch.cuda.synchronize()
+    m = compare_full(w, x, o.cpu(), lse.cpu(), tuple(t.cpu() for t in g))
+    log(f"  O max|err| {m['o_max']:.3e} mean {m['o_mean']:.3e}; lse {m['lse_max']:.3e}; "
+        f"dq {m['dq_rel_fro']:.3e} dk {m['dk_rel_fro']:.3e} dv {m['dv_rel_fro']:.3e}")
+    assert m["finite"] and all(m[n + "_finite"] for n in ("dq", "dk", "dv"))
+    assert m["o_over"] == 0, m.get("o_worst_over")
+    assert m["o_mean"] <= O_MEAN and m["lse_max"] <= LSE_MAX
+    for n in ("dq", "dk", "dv"):
+        assert m[n + "_rel_fro"] <= GRAD_REL_FRO, (n, m[n + "_rel_fro"])
