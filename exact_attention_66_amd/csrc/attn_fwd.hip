@@ -82,6 +82,9 @@ constexpr bool exact_dominant_weight() {
   return !std::is_same<E, f16_t>::value && kLog2DominantFraction < 0.0f;
 }
 
+#ifndef ATTN_FWD_COPY_AT
+#define ATTN_FWD_COPY_AT (-1)  // key block after which the next tile's copy goes out; -1: 1 if causal, else 0
+#endif
 #ifndef ATTN_FWD_QB
 #define ATTN_FWD_QB 1    // 32-query blocks per wave
 #endif
@@ -449,16 +452,22 @@ __global__ __launch_bounds__(NW * 64, ATTN_FWD_MINW) void fwd_kernel(const typen
   auto k_tile = [&](const int t, auto bufc) {
     constexpr int buf = decltype(bufc)::value;
     // buffer (t + AHEAD) % NBUF held tile t - 1, which every wave has finished
-    if (t + AHEAD < ntiles) copy_tile(t + AHEAD, (buf + AHEAD) % NBUF);
+    // The next tile's copy goes out before the tile's first key block, or
+    // (causal) before its second: right after the barrier every wave starts
+    // the tile at once, and a copy burst there stalls all of them together;
+    // one block later the waves are out of step and the copy still has
+    // three blocks to land.
+    constexpr int copy_at = ATTN_FWD_COPY_AT >= 0 ? ATTN_FWD_COPY_AT : (CAUSAL ? 1 : 0);
+    if (copy_at == 0 && t + AHEAD < ntiles) copy_tile(t + AHEAD, (buf + AHEAD) % NBUF);
     const int k0 = t * BN;
-    if (wave_valid && (!CAUSAL || k0 <= q_last)) {
-      v8 kf[KS];
-      read_k(buf, 0, kf);
+    const bool run = wave_valid && (!CAUSAL || k0 <= q_last);
+    v8 kf[KS];
+    if (run) read_k(buf, 0, kf);
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const int kbk0 = k0 + kb * 32;
-        if ((!CAUSAL || kbk0 <= q_last) && kbk0 < N) key_block(buf, kb, kbk0, kf);
-      }
+    for (int kb = 0; kb < KB; ++kb) {
+      if (copy_at > 0 && kb == copy_at && t + AHEAD < ntiles) copy_tile(t + AHEAD, (buf + AHEAD) % NBUF);
+      const int kbk0 = k0 + kb * 32;
+      if (run && (!CAUSAL || kbk0 <= q_last) && kbk0 < N) key_block(buf, kb, kbk0, kf);
     }
     mfma_drain();
     // tile t + 1 must be in LDS: with three buffers its copies are the ones
