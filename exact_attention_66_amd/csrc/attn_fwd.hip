@@ -18,8 +18,13 @@
 //    O^T += V^T P^T (keys relabelled per slot_key), and V^T comes from LDS
 //    with ds_read_b64_tr_b16, so P never leaves registers;
 //  * K/V tiles reach LDS by direct global->LDS copies (no staging registers,
-//    no LDS write instructions): 128-key tiles in two buffers at d = 128,
-//    64-key tiles in three at d = 64;
+//    no LDS write instructions);
+//  * two launch shapes, chosen per call from the work per head (see
+//    launch_fwd_a): 8 waves (256 queries) per workgroup with 128-key tiles in
+//    two buffers at d = 128 (64-key tiles in three at d = 64), or 4 waves
+//    (128 queries) with 64-key tiles in two buffers, two workgroups per CU;
+//    both walk each query row's keys in the same 32-key blocks in the same
+//    order, so they give bitwise-identical results;
 //  * within a tile each wave pipelines its 32-key blocks: a block's V^T
 //    fragments are read before its S^T product and the next block's K
 //    fragments before its P V product, so the LDS latency hides under MFMAs;
@@ -89,10 +94,13 @@ constexpr bool exact_dominant_weight() {
 #define ATTN_FWD_QB 1    // 32-query blocks per wave
 #endif
 #ifndef ATTN_FWD_NW
-#define ATTN_FWD_NW 8    // waves per workgroup
+#define ATTN_FWD_NW 0    // waves per workgroup: 0 chooses 4 or 8 per call (launch_fwd_a)
 #endif
 #ifndef ATTN_FWD_BN
-#define ATTN_FWD_BN 0    // keys per LDS tile; 0: 128 for d = 128 (two buffers), 64 for d = 64 (three)
+#define ATTN_FWD_BN 0    // keys per LDS tile of the 8-wave shape; 0: 128 for d = 128, 64 for d = 64
+#endif
+#ifndef ATTN_FWD_NBUF
+#define ATTN_FWD_NBUF 0  // LDS tile buffers; 0: three for 64-key tiles at 8 waves, else two
 #endif
 #ifndef ATTN_FWD_MINW
 #define ATTN_FWD_MINW 2  // waves per SIMD the register budget is sized for
@@ -133,9 +141,10 @@ __global__ __launch_bounds__(NW * 64, ATTN_FWD_MINW) void fwd_kernel(const typen
   constexpr int VC = (VI + NW - 1) / NW;
   constexpr int KSZ = KI * 64 * 8;           // elements per K tile buffer
   constexpr int VSZ = VI * 64 * 8;
-  // tile t in buffer t % NBUF: 64-key tiles in three buffers, copied two
-  // tiles ahead; 128-key tiles in two, copied one tile ahead
-  constexpr int NBUF = BN == 64 ? 3 : 2;
+  // tile t in buffer t % NBUF: with 8 waves, 64-key tiles in three buffers,
+  // copied two tiles ahead, and 128-key tiles in two, copied one tile ahead;
+  // with 4 waves, 64-key tiles in two
+  constexpr int NBUF = ATTN_FWD_NBUF ? ATTN_FWD_NBUF : (BN == 64 && NW == 8 ? 3 : 2);
 
   __shared__ __attribute__((aligned(16))) T lds_k[NBUF][KSZ];
   __shared__ __attribute__((aligned(16))) T lds_v[NBUF][VSZ];
@@ -269,7 +278,7 @@ __global__ __launch_bounds__(NW * 64, ATTN_FWD_MINW) void fwd_kernel(const typen
       return n;
     };
     static_assert(NBUF == 2 || KC + VC < 16, "vmcnt immediate");
-    static_assert(NW == 8, "one case per wave");
+    static_assert(NW == 8 || NW == 4, "one case per wave");
     switch (wu) {
       case 0: __builtin_amdgcn_s_waitcnt(0x0F70 | cnt(0)); break;
       case 1: __builtin_amdgcn_s_waitcnt(0x0F70 | cnt(1)); break;
@@ -453,11 +462,10 @@ __global__ __launch_bounds__(NW * 64, ATTN_FWD_MINW) void fwd_kernel(const typen
     constexpr int buf = decltype(bufc)::value;
     // buffer (t + AHEAD) % NBUF held tile t - 1, which every wave has finished
     // The next tile's copy goes out before the tile's first key block, or
-    // (causal) before its second: right after the barrier every wave starts
-    // the tile at once, and a copy burst there stalls all of them together;
-    // one block later the waves are out of step and the copy still has
-    // three blocks to land.
-    constexpr int copy_at = ATTN_FWD_COPY_AT >= 0 ? ATTN_FWD_COPY_AT : (CAUSAL ? 1 : 0);
+    // (causal, and every 4-wave launch) before its second: right after the
+    // barrier every wave starts the tile at once, and a copy burst there
+    // stalls all of them together; one block later the waves are out of step.
+    constexpr int copy_at = ATTN_FWD_COPY_AT >= 0 ? ATTN_FWD_COPY_AT : (CAUSAL || NW == 4 ? 1 : 0);
     if (copy_at == 0 && t + AHEAD < ntiles) copy_tile(t + AHEAD, (buf + AHEAD) % NBUF);
     const int k0 = t * BN;
     const bool run = wave_valid && (!CAUSAL || k0 <= q_last);
@@ -543,16 +551,33 @@ hipError_t launch_fwd_cfg(const FwdArgs& a) {
                        a.stream, 0);
 }
 
-template <typename E, int D, bool ALIBI, bool DROP>
-hipError_t launch_fwd_a(const FwdArgs& a) {
-  constexpr int BN = ATTN_FWD_BN ? ATTN_FWD_BN : (D == 128 ? 128 : 64);
-  constexpr int QB = ATTN_FWD_QB, NW = ATTN_FWD_NW;
+template <typename E, int D, int QB, int NW, int BN, bool ALIBI, bool DROP>
+hipError_t launch_fwd_shape(const FwdArgs& a) {
   if (a.N % 64 == 0) {
     if (a.causal) return launch_fwd_cfg<E, D, true, QB, NW, BN, false, ALIBI, DROP>(a);
     return launch_fwd_cfg<E, D, false, QB, NW, BN, false, ALIBI, DROP>(a);
   }
   if (a.causal) return launch_fwd_cfg<E, D, true, QB, NW, BN, true, ALIBI, DROP>(a);
   return launch_fwd_cfg<E, D, false, QB, NW, BN, true, ALIBI, DROP>(a);
+}
+
+// Launch shape.  The 4-wave shape (128 queries, 64-key tiles in two buffers,
+// 76 KB of LDS at d = 128) puts two workgroups on a CU: the two waves that
+// share a SIMD then belong to different workgroups and never meet at the same
+// tile barrier, and one workgroup's start and end overlap the other's work.
+// It reads each K/V tile for twice as many query blocks, which costs more than
+// it saves once a head's rows are long.  Measured on MI355X (forward alone,
+// same box): at d = 128 the 4-wave shape is 5-10 % faster for causal
+// N <= 4096, 2 % at N = 8192, about even at 16384 and 3 % slower at 32768;
+// non-causal, 4-7 % faster for N <= 2048 and 2-5 % slower from 4096 on; at
+// d = 64 it is ahead for causal N <= 4096 and non-causal N <= 2048.
+template <typename E, int D, bool ALIBI, bool DROP>
+hipError_t launch_fwd_a(const FwdArgs& a) {
+  constexpr int BN = ATTN_FWD_BN ? ATTN_FWD_BN : (D == 128 ? 128 : 64);
+  const int64_t small_n = a.causal ? (D == 128 ? 8192 : 4096) : 2048;
+  const bool four = ATTN_FWD_NW ? ATTN_FWD_NW == 4 : a.N <= small_n;
+  if (four) return launch_fwd_shape<E, D, 1, 4, 64, ALIBI, DROP>(a);
+  return launch_fwd_shape<E, D, ATTN_FWD_QB, 8, BN, ALIBI, DROP>(a);
 }
 
 // Dropout and ALiBi are not combined (no entry point takes both).
