@@ -47,6 +47,8 @@
 //    the row sums are taken (the softmax and lse are those of all keys) and
 //    scales O by 256 / (256 - t) in the epilogue; each lane draws one
 //    generator call per 32-key block (attn_dropout.h).
+#include <cstdlib>
+
 #include "attn_device.h"
 #include "attn_dropout.h"
 #include "attn_launch.h"
@@ -571,11 +573,19 @@ hipError_t launch_fwd_shape(const FwdArgs& a) {
 // N <= 4096, 2 % at N = 8192, about even at 16384 and 3 % slower at 32768;
 // non-causal, 4-7 % faster for N <= 2048 and 2-5 % slower from 4096 on; at
 // d = 64 it is ahead for causal N <= 4096 and non-causal N <= 2048.
+// ATTN_FWD_WAVES=4 or 8 in the environment (read on every call) forces one
+// shape, so that tests can run each case in both.
+inline int forced_fwd_waves() {
+  const char* e = std::getenv("ATTN_FWD_WAVES");
+  return e ? std::atoi(e) : 0;
+}
+
 template <typename E, int D, bool ALIBI, bool DROP>
 hipError_t launch_fwd_a(const FwdArgs& a) {
   constexpr int BN = ATTN_FWD_BN ? ATTN_FWD_BN : (D == 128 ? 128 : 64);
   const int64_t small_n = a.causal ? (D == 128 ? 8192 : 4096) : 2048;
-  const bool four = ATTN_FWD_NW ? ATTN_FWD_NW == 4 : a.N <= small_n;
+  const int forced = forced_fwd_waves();
+  const bool four = ATTN_FWD_NW ? ATTN_FWD_NW == 4 : (forced == 4 || (forced != 8 && a.N <= small_n));
   if (four) return launch_fwd_shape<E, D, 1, 4, 64, ALIBI, DROP>(a);
   return launch_fwd_shape<E, D, ATTN_FWD_QB, 8, BN, ALIBI, DROP>(a);
 }

@@ -85,6 +85,10 @@ enum attn_status {
  *   lse      [B,H,N] fp32 output: natural-log log-sum-exp of each row of the
  *            (masked, scaled) scores; the only statistic the backward needs.
  * o and lse must not overlap q, k, v or each other.
+ * The launch shape (8 waves and 256 queries, or 4 waves and 128 queries, per
+ * workgroup) is chosen on every call from N, d and causal; both give the same
+ * results bit for bit.  The environment variable ATTN_FWD_WAVES=4 or 8, read
+ * on every call, forces one (also for the strided, ALiBi and dropout forms).
  * Returns ATTN_OK or an attn_status error code.
  */
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
